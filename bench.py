@@ -1,0 +1,225 @@
+#!/usr/bin/env python
+"""Throughput of KV-cache scoring + compaction after prefill on one MI355X.
+
+A step is one pass of the whole path over one batch of synthetic inputs already
+resident in HBM: InfoKV's top-k entropy, representation distance, window
+attention, fusion, selection and gather for every layer and KV head (or, with
+--workload set to the SelKV workload, SelKV's attention, VATP union, selection and
+gated merge).  Prints one JSON line.
+
+  python bench.py [--gpus 1] [--steps 10] [--warmup 2] [--workload NAME]
+                  [--no-cpu-baseline]
+
+Timing: W untimed steps, then K steps between two events on the launch stream,
+with torch.cuda.synchronize() on both sides.  Inside the timed region an event
+follows every step of the path, so each kernel's average duration is measured
+live on the stream it runs on; the roofline object is computed from that.
+The cpu_baseline leg times the float64 oracle on a bounded sample of the same
+workload (stated in the output) on this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0                 # MI355X HBM3E, 8 TB/s
+BF16_DENSE_TFLOPS = 2500.0             # MI355X dense bf16 MFMA
+
+
+def algorithmic_bytes(w, k_list):
+    """Bytes each step of the path must move (inputs read once, outputs written
+    once), per launch group."""
+    e = 2 if w.dtype == "bf16" else 4
+    L, Hq, Hkv, n, d = w.layers, w.heads_q, w.heads_kv, w.n, w.head_dim
+    kept = sum(k_list) * Hkv
+    out = {}
+    if w.method == "infokv":
+        out["topk_entropy"] = n * w.vocab * e + n * 4
+        out["repr_distance"] = (L + 1) * n * w.hidden * e + L * n * 4
+        out["window_attn"] = L * Hkv * n * d * e + L * Hq * w.window * d * e + L * Hkv * n * 4
+        out["fuse_scores"] = 2 * L * Hkv * n * 4 + L * n * 4 + n * 4
+        out["select_topk"] = L * Hkv * n * 4 + kept * 4
+        out["compact"] = 2 * 2 * kept * d * e + kept * 4
+    else:
+        out["window_attn"] = L * Hkv * n * d * e + L * Hq * w.window * d * e + L * Hq * n * 4
+        out["vatp_union"] = L * Hkv * n * d * e + L * Hq * n * 4 + 2 * L * Hkv * n * 4
+        out["select_topk"] = L * Hkv * n * 4 + kept * 4
+        # V read, kept K read, K_c and V'_c written, A read, ln R written
+        out["merge_gated"] = L * Hkv * n * d * e + 3 * kept * d * e + L * Hkv * n * 4 + kept * 8
+    return out
+
+
+def window_flops(w):
+    """MFMA flops of one window-attention call (two passes of Q K^T)."""
+    return 2 * 2 * w.layers * w.heads_q * w.window * w.n * w.head_dim
+
+
+def cpu_baseline(w, inp, budget_s=20.0):
+    """The oracle, as it stands, on a bounded sample of the same workload; the
+    per-component times are scaled to the whole step."""
+    import numpy as np
+    import torch
+    from oracle import infokv, precision, selkv
+
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:
+        cores = 1
+
+    def f64(t):
+        t = t.detach().cpu().contiguous()
+        if t.dtype == torch.bfloat16:
+            return precision.bf16_bits_to_f64(t.view(torch.int16).numpy().view(np.uint16))
+        return t.numpy().astype(np.float64)
+
+    L, n = w.layers, w.n
+    if w.method == "infokv":
+        rows = min(n, 256)
+        lg = f64(inp["logits"][:rows])
+        t0 = time.perf_counter()
+        H = infokv.topk_entropy(lg, w.topk_entropy)
+        t_h = (time.perf_counter() - t0) * n / rows
+        hf = f64(inp["h_final"][:rows])
+        hl = [f64(inp["h"][l][:rows]) for l in range(L)]
+        t0 = time.perf_counter()
+        Ds = [infokv.repr_distance(hl[l], hf, w.tau) for l in range(L)]
+        t_d = (time.perf_counter() - t0) * n / rows
+        lay = L // 2
+        q, k = f64(inp["q_win"][lay]), f64(inp["k"][lay])
+        t0 = time.perf_counter()
+        A = infokv.window_attention(q, k)
+        t_a = (time.perf_counter() - t0) * L
+        Dn = np.resize(Ds[lay], n)
+        Hn = np.resize(H, n)
+        kk = infokv.uniform_budget(w.keep_fraction, n) if not w.adaptive_fraction else \
+            w.adaptive_total() // L
+        t0 = time.perf_counter()
+        S, _, _, _ = infokv.fuse_scores(A, Dn, Hn, w.alpha_fuse)
+        idx = infokv.select_topk(S.astype(np.float32), kk, w.window)
+        t_s = (time.perf_counter() - t0) * L
+        kb = inp["k"][lay].cpu().view(torch.int16).numpy()
+        vb = inp["v"][lay].cpu().view(torch.int16).numpy()
+        t0 = time.perf_counter()
+        infokv.compact(kb, vb, idx)
+        t_c = (time.perf_counter() - t0) * L
+        total = t_h + t_d + t_a + t_s + t_c
+        sample = (f"oracle on {rows} of {n} logits rows and hidden-state rows (all {L} layers), "
+                  f"window attention + fuse + select + gather of layer {lay} of {L}; each part "
+                  f"scaled by rows or layers to the whole step")
+    else:
+        lay = L // 2
+        nn = min(n, 16384)
+        q = f64(inp["q_win"][lay])
+        k = f64(inp["k"][lay][:, n - nn:])
+        v = f64(inp["v"][lay][:, n - nn:])
+        t0 = time.perf_counter()
+        selkv.selkv_layer(q, k, v, int(w.keep_fraction * nn), w.window, w.bucket)
+        total = (time.perf_counter() - t0) * L * (n / nn) ** 1.0
+        sample = (f"oracle SelKV layer (attention, union, select, route, gate, merge) on the "
+                  f"last {nn} of {n} tokens of layer {lay}, scaled linearly to {n} tokens and "
+                  f"{L} layers")
+    return {"value": n / total, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": sample, "est_step_s": total}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="llama3.1-8b-n32768-keep20-bf16")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this path does no cross-GPU work, so --gpus "
+              f"{args.gpus} has nothing to measure (a multi-GPU run would shard layers or KV "
+              f"heads with no collective on the hot path).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from kv_cache_compression_softmax_amd import configs, pipeline, synth
+
+    w = configs.BY_NAME[args.workload]
+    dev = torch.device("cuda:0")
+    print(f"[bench] generating {w.name} inputs ({w.input_bytes() / 1e9:.1f} GB)", file=sys.stderr, flush=True)
+    inp = synth.make_inputs(w, dev)
+    plan = pipeline.InfoKVPlan(w, dev) if w.method == "infokv" else pipeline.SelKVPlan(w, dev)
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        plan.run(inp)
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done; timing {args.steps} steps", file=sys.stderr, flush=True)
+
+    marks = []
+
+    def mark(name):
+        ev = torch.cuda.Event(enable_timing=True)
+        ev.record(stream)
+        marks.append((name, ev))
+
+    torch.cuda.synchronize()
+    for _ in range(args.steps):
+        plan.run(inp, mark=mark)
+    torch.cuda.synchronize()
+    total_ms = marks[0][1].elapsed_time(marks[-1][1])
+    ms = total_ms / args.steps
+    per = {}
+    for (n0, e0), (n1, e1) in zip(marks[:-1], marks[1:]):
+        if n1 == "start":
+            continue
+        per.setdefault(n1, []).append(e0.elapsed_time(e1))
+    per_ms = {k: sum(v) / len(v) for k, v in per.items()}
+
+    k_list = plan.k if w.method == "infokv" else plan.m
+    abytes = algorithmic_bytes(w, k_list)
+    dom = max(per_ms, key=per_ms.get)
+    achieved = abytes[dom] / (per_ms[dom] * 1e-3) / 1e9
+    path_bytes = sum(abytes.values())
+    kernels = {k: {"ms": round(per_ms[k], 4), "alg_bytes": abytes[k],
+                   "GBps": round(abytes[k] / (per_ms[k] * 1e-3) / 1e9, 1),
+                   "frac_hbm": round(abytes[k] / (per_ms[k] * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+               for k in per_ms}
+    kernels["window_attn"]["mfma_TFLOPs"] = round(window_flops(w) / (per_ms["window_attn"] * 1e-3) / 1e12, 1)
+
+    value = w.n / (ms * 1e-3)
+    out = {
+        "metric": "tokens scored+compacted/sec (all layers, 1 GPU) at 8B/32K; % of HBM roofline",
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded Llama-shaped tensors, inputs resident in HBM)",
+        "config": {"workload": w.name, "layers": w.layers, "heads_q": w.heads_q,
+                   "heads_kv": w.heads_kv, "head_dim": w.head_dim, "n": w.n, "window": w.window,
+                   "hidden": w.hidden, "vocab": w.vocab, "kept_per_layer": k_list[0]
+                   if len(set(k_list)) == 1 else "adaptive", "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": None},
+        "path_roofline": {"alg_bytes": path_bytes,
+                          "achieved_GBps": round(path_bytes / (ms * 1e-3) / 1e9, 1),
+                          "frac": round(path_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)},
+        "kernels": kernels,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(w, inp)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,237 @@
+/*
+ * kvc.h -- C ABI of the MI355X (gfx950) KV-cache scoring and compaction library.
+ *
+ * Pages cited:
+ *   [InfoKV] "긴 추론을 위한 정보 인지형 KV 캐시 압축(InfoKV)" (information-aware
+ *            KV-cache compression for long reasoning), aitrends.kr article 68510;
+ *            sections Contributions, Method, Technical detail, Glossary.
+ *   [SelKV]  "SelKV: Selective KV Cache Merging with Per-Token Merge-or-Drop and
+ *            Attention Compensation", gist.science paper 2607.16213; section 2
+ *            (soft cosine gate, attention compensation, pipeline overview).
+ *   [RECAS]  gist.science technical summary rs-10952127 (reasoning-aware,
+ *            error-bounded KV-cache compression); section 2.B, formal bound.
+ *
+ * Conventions shared by every entry point
+ *   - Batch 1.  Tensors are dense and row-major; shapes are given innermost last.
+ *   - "device" pointers are HIP device memory owned by the caller; the library
+ *     never allocates, frees or keeps them.  "host" arrays are read during the
+ *     call only.  A per-layer tensor is passed as a host array of L device
+ *     pointers (one tensor per layer, as a model holds its cache).
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *     the call returns without waiting, except kvc_adaptive_budget and
+ *     kvc_uniform_budget, which are host-only.
+ *   - dtype: KVC_F32 (binary32) or KVC_BF16 (bfloat16 bits).  Scores are float32
+ *     and indices int32 regardless of dtype; arithmetic accumulates in float32.
+ *   - Arguments are checked before anything is launched.  On error nothing is
+ *     enqueued and a negative status is returned; kvc_last_error() then holds a
+ *     message for the calling thread.  NaN or Inf inputs are not supported and
+ *     not checked.
+ *   - Workspace: an entry point that needs scratch device memory takes `ws`,
+ *     `ws_bytes`; kvc_*_workspace_size() with the same shape arguments gives the
+ *     minimum size.  Workspace contents need not be initialised and are not
+ *     preserved.  Two calls that share a workspace must be ordered (same stream).
+ */
+#ifndef KVC_H_
+#define KVC_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum kvc_status {
+  KVC_OK = 0,
+  KVC_ERR_ARG = -1,        /* null pointer, bad shape or out-of-range parameter */
+  KVC_ERR_DTYPE = -2,      /* unsupported dtype for this entry point           */
+  KVC_ERR_WORKSPACE = -3,  /* ws missing or smaller than *_workspace_size()     */
+  KVC_ERR_HIP = -4         /* a HIP launch or device query failed              */
+};
+
+enum kvc_dtype { KVC_F32 = 0, KVC_BF16 = 1 };
+
+/* Largest per-launch limits (checked; exceeding them is KVC_ERR_ARG). */
+#define KVC_MAX_LAYERS 1024
+#define KVC_MAX_TOPK_ENTROPY 1024
+
+/* Library version (major * 10000 + minor * 100 + patch). */
+int kvc_version(void);
+/* Static text for a status code. */
+const char* kvc_status_string(int status);
+/* Message of the calling thread's last failed call ("" if none). */
+const char* kvc_last_error(void);
+
+/*
+ * Top-k restricted entropy of each logits row ([InfoKV] Method; Glossary).
+ * For row i: T = the k largest logits (as a multiset), p_t = softmax over T
+ * only, H[i] = -sum_t p_t ln p_t (natural log).  0 <= H <= ln k.
+ *   logits     device, [rows, row_stride] of dtype; the first `vocab` columns
+ *              of each row are used.
+ *   rows >= 0; 1 <= topk <= min(vocab, KVC_MAX_TOPK_ENTROPY); row_stride >= vocab.
+ *   H_out      device float32 [rows].
+ */
+int kvc_topk_entropy(const void* logits, int dtype, int64_t rows, int64_t vocab,
+                     int64_t row_stride, int topk, float* H_out, void* stream);
+
+/*
+ * Layer-wise representation distance ([InfoKV] Method, Technical detail):
+ * D[l, i] = 1 - cos(h_l[i, :], h_final[i, :]) + tau, with cos := 0 when either
+ * vector has zero norm.
+ *   h_layers   host array of L device pointers, each [n, hidden] of dtype.
+ *   h_final    device [n, hidden] of dtype (the last layer's hidden state).
+ *   D_out      device float32 [L, n].
+ *   1 <= L <= KVC_MAX_LAYERS, n >= 0, hidden >= 1.
+ */
+int kvc_repr_distance(const void* const* h_layers, const void* h_final, int dtype,
+                      int L, int64_t n, int64_t hidden, float tau, float* D_out,
+                      void* stream);
+
+/*
+ * Observation-window attention ([InfoKV] Method, Technical detail; the
+ * attention factor of VATP in [SelKV] section 2, pipeline step 1).
+ * For layer l, query head h of KV group g = h / (Hq/Hkv), window row r at
+ * position p_r = n - w + r:
+ *   P[h, r, j] = softmax over j <= p_r of scale * <q[l][h, r, :], k[l][g, j, :]>
+ *   per_query_head = 1:  A[l, h, j] = (1/w) sum_r P[h, r, j]          [L, Hq, n]
+ *   per_query_head = 0:  A[l, g, j] = mean over the group's heads      [L, Hkv, n]
+ *   q_win      host array of L device pointers, each [Hq, w, d] of dtype.
+ *   k          host array of L device pointers, each [Hkv, n, d] of dtype.
+ *   A_out      device float32, shape above.  Every row of A sums to 1.
+ *   1 <= w <= n; Hq % Hkv == 0; bf16 needs d in {64, 128} and
+ *   (Hq/Hkv) * ceil(w/32) <= 8; float32 needs d <= 256.
+ *   ws         device workspace, kvc_score_window_attn_workspace_size() bytes.
+ */
+size_t kvc_score_window_attn_workspace_size(int L, int Hq, int Hkv, int64_t n,
+                                            int w, int d, int dtype);
+int kvc_score_window_attn(const void* const* q_win, const void* const* k, int dtype,
+                          int L, int Hq, int Hkv, int64_t n, int w, int d,
+                          float scale, int per_query_head, float* A_out,
+                          void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Importance fusion ([InfoKV] Contributions, Method, Technical detail):
+ *   E[l, i] = D[l, i] * H[i];  sigma[l, :] = softmax over the n tokens of E[l, :]
+ *   S[l, g, i] = alpha_fuse * A[l, g, i] + (1 - alpha_fuse) * sigma[l, i]
+ *   Ebar[l] = (1/n) sum_i E[l, i]      (the adaptive budget's layer share)
+ *   A          device float32 [L, Hkv, n];  D device float32 [L, n];
+ *   H          device float32 [n].
+ *   S_out      device float32 [L, Hkv, n].
+ *   Ebar_out   device float32 [L], or NULL.
+ *   n >= 1; 0 <= alpha_fuse <= 1.
+ */
+size_t kvc_fuse_scores_workspace_size(int L, int64_t n);
+int kvc_fuse_scores(const float* A, const float* D, const float* H, int L, int Hkv,
+                    int64_t n, float alpha_fuse, float* S_out, float* Ebar_out,
+                    void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Uniform layer budget ([InfoKV] Contributions, Technical detail; host only):
+ * k = floor(keep_fraction * n), clamped to [w, n].  Writes *k_out.
+ */
+int kvc_uniform_budget(double keep_fraction, int64_t n, int w, int64_t* k_out);
+
+/*
+ * Adaptive layer budget ([InfoKV] Method; Glossary, adaptive budget allocation;
+ * host only, synchronous):  x_l = Ebar[l] / sum_m Ebar[m] * B (in double),
+ * k_l = floor(x_l); the B - sum k_l leftover tokens go one each to the lowest
+ * layer indices; each k_l is then clamped to [w, n].
+ *   Ebar       host float32 [L], all > 0 (copy kvc_fuse_scores' Ebar_out back).
+ *   k_out      host int64 [L].
+ */
+int kvc_adaptive_budget(const float* Ebar, int L, int64_t B, int w, int64_t n,
+                        int64_t* k_out);
+
+/*
+ * Per-(layer, KV head) retention ([InfoKV] Method, Technical detail; [SelKV]
+ * section 2, pipeline step 2 when S is the VATP union):
+ * keep the last w tokens plus the k_l - w tokens of [0, n - w) with the largest
+ * S (float32 compare, ties to the lower index); if k_l <= w keep the last k_l.
+ * Indices are written in ascending order.  Exact and deterministic.
+ *   S          device float32 [L, Hkv, n].
+ *   k_keep     host int64 [L], each in [1, n].
+ *   idx_out    host array of L device pointers, each int32 [Hkv, k_keep[l]].
+ *   0 <= w <= n.
+ */
+int kvc_select_topk(const float* S, int L, int Hkv, int64_t n, const int64_t* k_keep,
+                    int w, int32_t* const* idx_out, void* stream);
+
+/*
+ * Order-preserving gather of the kept rows ([InfoKV] Method: the top tokens are
+ * retained): K_out[l][g, j, :] = K[l][g, idx[l][g, j], :], same for V.
+ * Bit-exact copy.
+ *   K, V       host arrays of L device pointers, each [Hkv, n, d] of dtype.
+ *   idx        host array of L device pointers, each int32 [Hkv, k_keep[l]],
+ *              every entry in [0, n) (not checked on the device).
+ *   k_keep     host int64 [L].
+ *   K_out, V_out  host arrays of L device pointers, each [Hkv, k_keep[l], d].
+ *   V and V_out may both be NULL (keys only).
+ */
+int kvc_compact(const void* const* K, const void* const* V, int dtype, int L, int Hkv,
+                int64_t n, int d, const int32_t* const* idx, const int64_t* k_keep,
+                void* const* K_out, void* const* V_out, void* stream);
+
+/*
+ * VATP importance and its GQA union ([SelKV] section 2, pipeline steps 1-2):
+ *   VATP[l, h, j] = A_hq[l, h, j] * ||v[l][g(h), j, :]||_2
+ *   U_out[l, g, j]  = max over the group's heads of VATP
+ *   Ag_out[l, g, j] = mean over the group's heads of A_hq (the group's prefill
+ *                     attention used for routing and merge weights)
+ *   A_hq       device float32 [L, Hq, n] (kvc_score_window_attn, per_query_head=1).
+ *   V          host array of L device pointers, each [Hkv, n, d] of dtype.
+ *   U_out, Ag_out  device float32 [L, Hkv, n].
+ */
+int kvc_vatp_union(const float* A_hq, const void* const* V, int dtype, int L, int Hq,
+                   int Hkv, int64_t n, int d, float* U_out, float* Ag_out, void* stream);
+
+/*
+ * Selective gated merge with attention compensation ([SelKV] section 2: soft
+ * cosine gate, attention compensation, pipeline steps 3-5), fused with the
+ * order-preserving gather.  For each layer l and KV head g, with kept indices
+ * idx (ascending, from kvc_select_topk on U) and A = Ag[l, g, :]:
+ *   - an evicted token e goes to t(e) = the kept token of its bucket
+ *     [floor(e/bucket)*bucket, +bucket) with the largest A (ties: lower index);
+ *     it is dropped if the bucket holds no kept token;
+ *   - gate g_e = max(cos(v_e, v_t), 0)  (cos := 0 for a zero vector);
+ *   - v'_t = (A_t v_t + sum_e g_e A_e v_e) / (A_t + sum_e g_e A_e);
+ *     R_t = (A_t + sum_e g_e A_e) / A_t;  logR_out = ln R_t (0 if nothing merged);
+ *   - K_out = K at the kept rows (keys are not merged), V_out = v' rounded to
+ *     dtype (round to nearest even for bf16).
+ *   K, V       host arrays of L device pointers, each [Hkv, n, d] of dtype.
+ *   Ag         device float32 [L, Hkv, n].
+ *   idx        host array of L device pointers, each int32 [Hkv, m_keep[l]],
+ *              ascending, every entry in [0, n).
+ *   m_keep     host int64 [L];  bucket >= 1;  d in {64, 128}.
+ *   K_out, V_out  host arrays of L device pointers, each [Hkv, m_keep[l], d].
+ *   logR_out   host array of L device pointers, each float32 [Hkv, m_keep[l]].
+ */
+int kvc_merge_gated(const void* const* K, const void* const* V, int dtype,
+                    const float* Ag, int L, int Hkv, int64_t n, int d,
+                    const int32_t* const* idx, const int64_t* m_keep, int bucket,
+                    void* const* K_out, void* const* V_out, float* const* logR_out,
+                    void* stream);
+
+/*
+ * Decode attention of one query per head over a (compacted) cache, with the
+ * optional compensation bias ([SelKV] section 2, attention compensation; used
+ * with [RECAS] section 2.B's bound as a check):
+ *   logit[h, t] = scale * <q[l][h, :], K[l][g(h), t, :]> + alpha_bias * logR[l][g(h), t]
+ *   o_out[l, h, :] = sum_t softmax(logit[h, :])_t * V[l][g(h), t, :]
+ *   lse_out[l, h]  = ln sum_t exp(logit[h, t])   (may be NULL)
+ *   q          host array of L device pointers, each [Hq, d] of dtype.
+ *   K, V       host arrays of L device pointers, each [Hkv, len, d] of dtype.
+ *   logR       host array of L device pointers, each float32 [Hkv, len], or NULL.
+ *   o_out      device float32 [L, Hq, d];  lse_out device float32 [L, Hq].
+ *   len >= 1; d <= 256.
+ */
+size_t kvc_decode_attn_workspace_size(int L, int Hq, int64_t len, int d);
+int kvc_decode_attn(const void* const* q, const void* const* K, const void* const* V,
+                    int dtype, const float* const* logR, float alpha_bias, int L,
+                    int Hq, int Hkv, int64_t len, int d, float scale, float* o_out,
+                    float* lse_out, void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif  /* KVC_H_ */

@@ -1,0 +1,112 @@
+// Order-preserving gather of the kept K/V rows into the compacted cache.
+//
+// [InfoKV] Method: each layer retains its selected tokens; the compacted cache
+// holds them in their original order, so positions stay monotone.
+//
+// Pure bandwidth: each kept row (d elements, 256 B for bf16 d = 128) is read once
+// and written once.  A workgroup copies ROWS consecutive kept rows of one
+// (layer, KV head): 16-byte lanes, rowbytes/16 lanes per row, so one wave moves
+// several whole rows per instruction and both the reads and the writes of a row
+// are single contiguous segments.  Layers of different k_l (adaptive budget)
+// share one launch through a per-layer table of block offsets.
+#include "common.h"
+
+namespace kvc {
+namespace {
+
+constexpr int NT = 256;
+constexpr int ROWS = 64;        // kept rows per workgroup
+
+struct Tables {
+  ConstPtrs K, V, idx;
+  MutPtrs Ko, Vo;
+  I64s k;
+  I64s blk0;                    // first block of each layer
+};
+
+template <bool VEC>
+__global__ void __launch_bounds__(NT)
+compact_kernel(Tables t, int lc, int Hkv, int64_t n, int rowbytes) {
+  const int64_t b = blockIdx.x;
+  int l = 0;
+  while (l + 1 < lc && t.blk0.v[l + 1] <= b) ++l;
+  const int64_t k = t.k.v[l];
+  const int64_t nbk = (k + ROWS - 1) / ROWS;
+  const int64_t local = b - t.blk0.v[l];
+  const int g = (int)(local / nbk);
+  const int64_t j0 = (local % nbk) * ROWS;
+  const int32_t* idx = (const int32_t*)t.idx.p[l] + (int64_t)g * k;
+  const char* K = (const char*)t.K.p[l] + (int64_t)g * n * rowbytes;
+  const char* V = t.V.p[l] ? (const char*)t.V.p[l] + (int64_t)g * n * rowbytes : nullptr;
+  char* Ko = (char*)t.Ko.p[l] + (int64_t)g * k * rowbytes;
+  char* Vo = V ? (char*)t.Vo.p[l] + (int64_t)g * k * rowbytes : nullptr;
+  if (VEC) {
+    const int lpr = rowbytes / 16;                 // lanes per row
+    const int rpi = NT / lpr;                      // rows per iteration
+    const int r = threadIdx.x / lpr, c = threadIdx.x % lpr;
+    if (r >= rpi) return;
+    for (int64_t j = j0 + r; j < min(k, j0 + ROWS); j += rpi) {
+      const int64_t src = idx[j];
+      const uint4 kv = *reinterpret_cast<const uint4*>(K + src * rowbytes + c * 16);
+      uint4 vv;
+      if (V) vv = *reinterpret_cast<const uint4*>(V + src * rowbytes + c * 16);
+      *reinterpret_cast<uint4*>(Ko + j * rowbytes + c * 16) = kv;
+      if (V) *reinterpret_cast<uint4*>(Vo + j * rowbytes + c * 16) = vv;
+    }
+  } else {
+    const int half = rowbytes / 2;                 // 2-byte words per row
+    for (int64_t j = j0; j < min(k, j0 + ROWS); ++j) {
+      const int64_t src = idx[j];
+      for (int c = threadIdx.x; c < half; c += NT) {
+        ((uint16_t*)(Ko + j * rowbytes))[c] = ((const uint16_t*)(K + src * rowbytes))[c];
+        if (V) ((uint16_t*)(Vo + j * rowbytes))[c] = ((const uint16_t*)(V + src * rowbytes))[c];
+      }
+    }
+  }
+}
+
+}  // namespace
+}  // namespace kvc
+
+using namespace kvc;
+
+extern "C" int kvc_compact(const void* const* K, const void* const* V, int dtype, int L, int Hkv,
+                           int64_t n, int d, const int32_t* const* idx, const int64_t* k_keep,
+                           void* const* K_out, void* const* V_out, void* stream) {
+  clear_error();
+  if (!dtype_ok(dtype)) return KVC_FAIL(KVC_ERR_DTYPE, "kvc_compact: dtype %d", dtype);
+  KVC_REQUIRE(L >= 1 && L <= KVC_MAX_LAYERS, "kvc_compact: need 1 <= L <= %d", KVC_MAX_LAYERS);
+  KVC_REQUIRE(Hkv >= 1 && n >= 1 && d >= 1 && d <= 4096, "kvc_compact: need Hkv, n >= 1 and 1 <= d <= 4096");
+  KVC_REQUIRE(K && idx && k_keep && K_out, "kvc_compact: null pointer");
+  KVC_REQUIRE((V == nullptr) == (V_out == nullptr), "kvc_compact: V and V_out must both be set or both NULL");
+  KVC_REQUIRE((int64_t)kLayersPerLaunch * Hkv * ((n + ROWS - 1) / ROWS) <= 0x7fffffffLL,
+              "kvc_compact: too many rows for one launch");
+  const int rowbytes = d * dtype_size(dtype);
+  bool vec = rowbytes % 16 == 0 && rowbytes / 16 <= NT;
+  for (int l = 0; l < L; ++l) {
+    KVC_REQUIRE(K[l] && idx[l] && K_out[l], "kvc_compact: null pointer in layer %d", l);
+    KVC_REQUIRE(!V || (V[l] && V_out[l]), "kvc_compact: null V pointer in layer %d", l);
+    KVC_REQUIRE(k_keep[l] >= 1 && k_keep[l] <= n, "kvc_compact: k_keep[%d] outside [1, n]", l);
+    vec = vec && (uintptr_t)K[l] % 16 == 0 && (uintptr_t)K_out[l] % 16 == 0;
+    if (V) vec = vec && (uintptr_t)V[l] % 16 == 0 && (uintptr_t)V_out[l] % 16 == 0;
+  }
+  hipStream_t s = as_stream(stream);
+  for (int l0 = 0; l0 < L; l0 += kLayersPerLaunch) {
+    const int lc = min(kLayersPerLaunch, L - l0);
+    Tables t{};
+    int64_t blocks = 0;
+    for (int i = 0; i < lc; ++i) {
+      t.K.p[i] = K[l0 + i];
+      t.V.p[i] = V ? V[l0 + i] : nullptr;
+      t.idx.p[i] = idx[l0 + i];
+      t.Ko.p[i] = K_out[l0 + i];
+      t.Vo.p[i] = V ? V_out[l0 + i] : nullptr;
+      t.k.v[i] = k_keep[l0 + i];
+      t.blk0.v[i] = blocks;
+      blocks += (int64_t)Hkv * ((k_keep[l0 + i] + ROWS - 1) / ROWS);
+    }
+    if (vec) hipLaunchKernelGGL(compact_kernel<true>, dim3((unsigned)blocks), dim3(NT), 0, s, t, lc, Hkv, n, rowbytes);
+    else hipLaunchKernelGGL(compact_kernel<false>, dim3((unsigned)blocks), dim3(NT), 0, s, t, lc, Hkv, n, rowbytes);
+  }
+  return launch_status("kvc_compact");
+}

@@ -1,0 +1,115 @@
+// Importance fusion S = alpha * A + (1 - alpha) * softmax_tokens(D * H), and the
+// layer's mean entropy score Ebar.
+//
+// [InfoKV] Contributions, Method and Technical detail: the layer entropy score
+// E_i = D_i * H_i is normalised by a softmax over the tokens of the layer and
+// mixed with the window attention; [InfoKV] Method / Glossary (adaptive budget):
+// the layer's share of the total entropy score drives the adaptive budget.
+//
+// Two small kernels, both deterministic:
+//   stats  one block per (layer, chunk of tokens) computes max E, sum exp(E - max)
+//          and sum E over its chunk; the chunk partials are merged in index order
+//          by a second tiny launch into (max, sum, Ebar) per layer;
+//   apply  elementwise over [L, Hkv, n], recomputing E from D and H (cheaper than
+//          storing it).
+#include "common.h"
+
+namespace kvc {
+namespace {
+
+constexpr int NT = 256;
+constexpr int CHUNK = 8192;     // tokens per stats block
+
+struct Part { float m, s, e; };
+
+__global__ void __launch_bounds__(NT)
+fuse_stats(const float* __restrict__ D, const float* __restrict__ H, int64_t n, int nchunk,
+           Part* __restrict__ part) {
+  __shared__ float red[NT / 64];
+  const int l = blockIdx.y, c = blockIdx.x;
+  const int64_t i0 = (int64_t)c * CHUNK, i1 = min(n, i0 + CHUNK);
+  const float* Dl = D + (int64_t)l * n;
+  float m = -INFINITY, esum = 0.f;
+  for (int64_t i = i0 + threadIdx.x; i < i1; i += NT) {
+    const float E = Dl[i] * H[i];
+    m = fmaxf(m, E);
+    esum += E;
+  }
+  const float M = block_max<NT>(m, red);
+  float s = 0.f;
+  for (int64_t i = i0 + threadIdx.x; i < i1; i += NT) s += expf(Dl[i] * H[i] - M);
+  const float S = block_sum<NT>(s, red);
+  const float ES = block_sum<NT>(esum, red);
+  if (threadIdx.x == 0) part[(int64_t)l * nchunk + c] = Part{M, S, ES};
+}
+
+__global__ void fuse_stats_merge(const Part* __restrict__ part, int nchunk, int L, int64_t n,
+                                 float2* __restrict__ stats, float* __restrict__ Ebar) {
+  const int l = blockIdx.x * blockDim.x + threadIdx.x;
+  if (l >= L) return;
+  const Part* p = part + (int64_t)l * nchunk;
+  float M = -INFINITY;
+  for (int c = 0; c < nchunk; ++c) M = fmaxf(M, p[c].m);
+  float S = 0.f, ES = 0.f;
+  for (int c = 0; c < nchunk; ++c) { S += p[c].s * expf(p[c].m - M); ES += p[c].e; }
+  stats[l] = make_float2(M, 1.0f / S);
+  if (Ebar) Ebar[l] = ES / (float)n;
+}
+
+__global__ void __launch_bounds__(NT)
+fuse_apply(const float* __restrict__ A, const float* __restrict__ D, const float* __restrict__ H,
+           const float2* __restrict__ stats, int Hkv, int64_t n, float alpha,
+           float* __restrict__ S) {
+  const int64_t row = blockIdx.y;               // (layer, KV head)
+  const int l = (int)(row / Hkv);
+  const float2 st = stats[l];
+  const float* Dl = D + (int64_t)l * n;
+  const float* Ar = A + row * n;
+  float* Sr = S + row * n;
+  const float beta = 1.0f - alpha;
+  for (int64_t i = (int64_t)blockIdx.x * NT + threadIdx.x; i < n; i += (int64_t)gridDim.x * NT) {
+    const float sigma = expf(Dl[i] * H[i] - st.x) * st.y;
+    Sr[i] = alpha * Ar[i] + beta * sigma;
+  }
+}
+
+}  // namespace
+}  // namespace kvc
+
+using namespace kvc;
+
+extern "C" size_t kvc_fuse_scores_workspace_size(int L, int64_t n) {
+  if (L < 1 || n < 1) return 0;
+  const int64_t nchunk = (n + CHUNK - 1) / CHUNK;
+  return (size_t)L * nchunk * sizeof(Part) + (size_t)L * sizeof(float2) + 256;
+}
+
+extern "C" int kvc_fuse_scores(const float* A, const float* D, const float* H, int L, int Hkv,
+                               int64_t n, float alpha_fuse, float* S_out, float* Ebar_out,
+                               void* ws, size_t ws_bytes, void* stream) {
+  clear_error();
+  KVC_REQUIRE(L >= 1 && L <= KVC_MAX_LAYERS, "kvc_fuse_scores: need 1 <= L <= %d", KVC_MAX_LAYERS);
+  KVC_REQUIRE(Hkv >= 1 && n >= 1, "kvc_fuse_scores: need Hkv >= 1 and n >= 1");
+  KVC_REQUIRE(alpha_fuse >= 0.f && alpha_fuse <= 1.f, "kvc_fuse_scores: alpha_fuse outside [0, 1]");
+  KVC_REQUIRE(A && D && H && S_out, "kvc_fuse_scores: null pointer");
+  const int64_t nchunk = (n + CHUNK - 1) / CHUNK;
+  KVC_REQUIRE(nchunk <= 0x7fffffff, "kvc_fuse_scores: n too large");
+  const int64_t rows = (int64_t)L * Hkv;
+  KVC_REQUIRE(rows <= 65535, "kvc_fuse_scores: L * Hkv > 65535");
+  const size_t need = kvc_fuse_scores_workspace_size(L, n);
+  if (!ws || ws_bytes < need)
+    return KVC_FAIL(KVC_ERR_WORKSPACE, "kvc_fuse_scores: workspace needs %zu bytes", need);
+  char* base = (char*)(((uintptr_t)ws + 255) & ~(uintptr_t)255);
+  Part* part = (Part*)base;
+  float2* stats = (float2*)(base + (size_t)L * nchunk * sizeof(Part));
+  hipStream_t s = as_stream(stream);
+  hipLaunchKernelGGL(fuse_stats, dim3((unsigned)nchunk, (unsigned)L), dim3(NT), 0, s, D, H, n,
+                     (int)nchunk, part);
+  hipLaunchKernelGGL(fuse_stats_merge, dim3((L + 63) / 64), dim3(64), 0, s, (const Part*)part,
+                     (int)nchunk, L, n, stats, Ebar_out);
+  const int64_t gx64 = (n + NT * 4 - 1) / (NT * 4);
+  const unsigned gx = (unsigned)(gx64 < 1024 ? gx64 : 1024);
+  hipLaunchKernelGGL(fuse_apply, dim3(gx, (unsigned)rows), dim3(NT), 0, s, A, D, H,
+                     (const float2*)stats, Hkv, n, alpha_fuse, S_out);
+  return launch_status("kvc_fuse_scores");
+}

@@ -1,0 +1,130 @@
+// Per-(layer, KV head) retention: the last w tokens plus the k - w highest scores
+// of the rest, ties to the lower index, indices written in ascending order.
+//
+// [InfoKV] Method and Technical detail: each layer keeps its top-k_l tokens by the
+// fused score.  [SelKV] section 2, pipeline step 2: the same selection on the
+// VATP union keeps the top tokens plus the recent window.
+//
+// One workgroup per (layer, KV head):
+//   1. radix select on order-preserving 32-bit keys of the float32 scores (four
+//      8-bit digits, LDS histograms) finds T, the (k - w)-th largest key of
+//      [0, n - w), and cgt = the number of keys above it;
+//   2. one ordered pass over [0, n - w) keeps every key > T and the first
+//      k - w - cgt keys == T in index order.  Output positions come from a block
+//      scan of (count > T, count == T) per thread, so the indices come out
+//      ascending and the result is exact and deterministic.
+// The score row (at most a few hundred KB) is re-read from L2 by each pass.
+#include "common.h"
+
+namespace kvc {
+namespace {
+
+constexpr int NT = 1024;
+constexpr int EPT = 4;          // consecutive elements per thread in the output pass
+
+__global__ void __launch_bounds__(NT)
+select_kernel(const float* __restrict__ S, int Hkv, int64_t n, I64s kk, int w, MutPtrs idx) {
+  __shared__ int hist[256];
+  __shared__ int scan[NT / 64];
+  __shared__ int pick[2];
+  const int tid = threadIdx.x;
+  const int l = blockIdx.x / Hkv, g = blockIdx.x % Hkv;
+  const int64_t k = kk.v[l];
+  const float* row = S + ((int64_t)l * Hkv + g) * n;
+  int32_t* out = (int32_t*)idx.p[l] + (int64_t)g * k;
+  if (k <= w) {                                   // the window alone overflows the budget
+    for (int64_t j = tid; j < k; j += NT) out[j] = (int32_t)(n - k + j);
+    return;
+  }
+  const int64_t nb = n - w, need = k - w;
+  for (int64_t j = tid; j < w; j += NT) out[need + j] = (int32_t)(nb + j);
+  if (need >= nb) {                               // everything is kept
+    for (int64_t j = tid; j < nb; j += NT) out[j] = (int32_t)j;
+    return;
+  }
+  // ---- 1. radix select of the need-th largest key
+  uint32_t prefix = 0;
+  int64_t above = 0, rem = need;
+#pragma unroll 1
+  for (int p = 3; p >= 0; --p) {
+    const int shift = 8 * p;
+    const uint32_t hi_mask = (p == 3) ? 0u : (uint32_t)(~0ull << (shift + 8));
+    if (tid < 256) hist[tid] = 0;
+    __syncthreads();
+    for (int64_t i = tid; i < nb; i += NT) {
+      const uint32_t key = f32_key(row[i]);
+      if ((key & hi_mask) == (prefix & hi_mask)) atomicAdd(&hist[(key >> shift) & 255], 1);
+    }
+    __syncthreads();
+    const int c = tid < 256 ? hist[255 - tid] : 0;
+    int tot;
+    const int incl = block_exclusive_scan<NT>(c, scan, &tot) + c;
+    if (tid < 256 && incl >= rem && incl - c < rem) { pick[0] = 255 - tid; pick[1] = incl - c; }
+    __syncthreads();
+    prefix |= (uint32_t)pick[0] << shift;
+    above += pick[1];
+    rem -= pick[1];
+    __syncthreads();
+  }
+  const uint32_t T = prefix;
+  const int64_t take_eq = need - above;           // >= 1 copies of T are kept
+  // ---- 2. ordered output of [0, nb)
+  int64_t run_gt = 0, run_eq = 0;
+#pragma unroll 1
+  for (int64_t c0 = 0; c0 < nb; c0 += (int64_t)NT * EPT) {
+    const int64_t i0 = c0 + (int64_t)tid * EPT;
+    uint32_t gt = 0, eq = 0;
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+      if (i0 + e < nb) {
+        const uint32_t key = f32_key(row[i0 + e]);
+        gt |= (uint32_t)(key > T) << e;
+        eq |= (uint32_t)(key == T) << e;
+      }
+    }
+    const int packed = __builtin_popcount(gt) | (__builtin_popcount(eq) << 16);
+    int tot;
+    const int ex = block_exclusive_scan<NT>(packed, scan, &tot);
+    int64_t gtb = run_gt + (ex & 0xffff), eqb = run_eq + (ex >> 16);
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+      if (gt & (1u << e)) {
+        out[gtb + min(eqb, take_eq)] = (int32_t)(i0 + e);
+        ++gtb;
+      } else if (eq & (1u << e)) {
+        if (eqb < take_eq) out[gtb + eqb] = (int32_t)(i0 + e);
+        ++eqb;
+      }
+    }
+    run_gt += tot & 0xffff;
+    run_eq += tot >> 16;
+  }
+}
+
+}  // namespace
+}  // namespace kvc
+
+using namespace kvc;
+
+extern "C" int kvc_select_topk(const float* S, int L, int Hkv, int64_t n, const int64_t* k_keep,
+                               int w, int32_t* const* idx_out, void* stream) {
+  clear_error();
+  KVC_REQUIRE(L >= 1 && L <= KVC_MAX_LAYERS, "kvc_select_topk: need 1 <= L <= %d", KVC_MAX_LAYERS);
+  KVC_REQUIRE(Hkv >= 1 && n >= 1 && n <= 0x7fffffffLL, "kvc_select_topk: need Hkv >= 1, 1 <= n < 2^31");
+  KVC_REQUIRE(w >= 0 && w <= n, "kvc_select_topk: need 0 <= w <= n");
+  KVC_REQUIRE(S && k_keep && idx_out, "kvc_select_topk: null pointer");
+  for (int l = 0; l < L; ++l) {
+    KVC_REQUIRE(k_keep[l] >= 1 && k_keep[l] <= n, "kvc_select_topk: k_keep[%d] outside [1, n]", l);
+    KVC_REQUIRE(idx_out[l], "kvc_select_topk: idx_out[%d] is null", l);
+  }
+  hipStream_t s = as_stream(stream);
+  for (int l0 = 0; l0 < L; l0 += kLayersPerLaunch) {
+    const int lc = min(kLayersPerLaunch, L - l0);
+    I64s kk{};
+    MutPtrs ip{};
+    for (int i = 0; i < lc; ++i) { kk.v[i] = k_keep[l0 + i]; ip.p[i] = idx_out[l0 + i]; }
+    hipLaunchKernelGGL(select_kernel, dim3((unsigned)(lc * Hkv)), dim3(NT), 0, s,
+                       S + (int64_t)l0 * Hkv * n, Hkv, n, kk, w, ip);
+  }
+  return launch_status("kvc_select_topk");
+}

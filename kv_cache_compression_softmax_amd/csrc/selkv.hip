@@ -1,0 +1,323 @@
+// SelKV's selective merge path: VATP score with its GQA union, then per-bucket
+// routing, soft cosine gate, gated merge and the log-ratio compensation.
+//
+// [SelKV] section 2.  Pipeline step 1 scores each token by its window attention
+// times the norm of its value vector (VATP); step 2 keeps the top tokens (for
+// GQA, over the union of the group's heads) plus the recent window; step 3 sends
+// every evicted token to a kept token of its positional bucket chosen by prefill
+// attention; step 4 weights each evicted value by the soft cosine gate
+// g = max(cos, 0) before the attention-weighted merge; step 5 records the ratio R
+// of the attention mass the merged entry stands for to the mass of the kept
+// token, applied at decode time as a logit bias alpha * ln R.
+//
+// Both kernels are bound by the V stream.  Rows are read as 16-byte lanes, LG
+// lanes per row (LG = row bytes / 16), so a wave covers 64/LG rows per load.
+#include "common.h"
+
+namespace kvc {
+namespace {
+
+template <typename T> struct El;
+template <> struct El<uint16_t> {
+  static constexpr int N = 8;
+  __device__ static void unpack(const uint4& u, float (&x)[8]) {
+    x[0] = bf16_lo(u.x); x[1] = bf16_hi(u.x); x[2] = bf16_lo(u.y); x[3] = bf16_hi(u.y);
+    x[4] = bf16_lo(u.z); x[5] = bf16_hi(u.z); x[6] = bf16_lo(u.w); x[7] = bf16_hi(u.w);
+  }
+  __device__ static uint4 pack(const float (&x)[8]) {
+    uint4 u;
+    u.x = f32_to_bf16_rne(x[0]) | ((uint32_t)f32_to_bf16_rne(x[1]) << 16);
+    u.y = f32_to_bf16_rne(x[2]) | ((uint32_t)f32_to_bf16_rne(x[3]) << 16);
+    u.z = f32_to_bf16_rne(x[4]) | ((uint32_t)f32_to_bf16_rne(x[5]) << 16);
+    u.w = f32_to_bf16_rne(x[6]) | ((uint32_t)f32_to_bf16_rne(x[7]) << 16);
+    return u;
+  }
+};
+template <> struct El<float> {
+  static constexpr int N = 4;
+  __device__ static void unpack(const uint4& u, float (&x)[4]) {
+    x[0] = __uint_as_float(u.x); x[1] = __uint_as_float(u.y);
+    x[2] = __uint_as_float(u.z); x[3] = __uint_as_float(u.w);
+  }
+  __device__ static uint4 pack(const float (&x)[4]) {
+    return make_uint4(__float_as_uint(x[0]), __float_as_uint(x[1]), __float_as_uint(x[2]),
+                      __float_as_uint(x[3]));
+  }
+};
+
+// ------------------------------------------------------------- VATP + union
+constexpr int NT = 256;
+
+template <typename T, int LG>
+__global__ void __launch_bounds__(NT)
+vatp_union_kernel(const float* __restrict__ A_hq, ConstPtrs V, int Hq, int Hkv, int64_t n, int d,
+                  int64_t nblk, float* __restrict__ U, float* __restrict__ Ag) {
+  constexpr int W = El<T>::N;
+  constexpr int RPI = NT / LG;                  // rows per block iteration
+  const int64_t bid = blockIdx.x;
+  const int64_t jblk = bid % nblk;
+  const int g = (int)((bid / nblk) % Hkv);
+  const int l = (int)(bid / (nblk * Hkv));
+  const int G = Hq / Hkv;
+  const int r = threadIdx.x / LG, c = threadIdx.x % LG;
+  const T* Vg = (const T*)V.p[l] + (int64_t)g * n * d;
+  const float* Ah = A_hq + ((int64_t)l * Hq + (int64_t)g * G) * n;
+  const int64_t j = jblk * RPI + r;
+  float ss = 0.f;
+  if (j < n) {
+    float x[W];
+    El<T>::unpack(*reinterpret_cast<const uint4*>(Vg + j * d + c * W), x);
+#pragma unroll
+    for (int e = 0; e < W; ++e) ss += x[e] * x[e];
+  }
+  ss = group_sum<LG>(ss);
+  if (c == 0 && j < n) {
+    const float vn = sqrtf(ss);
+    float mx = -INFINITY, sum = 0.f;
+    for (int h = 0; h < G; ++h) {
+      const float a = Ah[(int64_t)h * n + j];
+      mx = fmaxf(mx, a * vn);
+      sum += a;
+    }
+    const int64_t o = ((int64_t)l * Hkv + g) * n + j;
+    U[o] = mx;
+    Ag[o] = sum / (float)G;
+  }
+}
+
+// ------------------------------------------------------------- merge
+constexpr int NTM = 256;        // 4 waves, one bucket each
+
+__device__ __forceinline__ int64_t lower_bound(const int32_t* a, int64_t m, int64_t x) {
+  int64_t lo = 0, hi = m;
+  while (lo < hi) {
+    const int64_t mid = (lo + hi) >> 1;
+    if (a[mid] < x) lo = mid + 1; else hi = mid;
+  }
+  return lo;
+}
+
+struct MergeTables {
+  ConstPtrs K, V, idx;
+  MutPtrs Ko, Vo, logR;
+  I64s m;
+  I64s task0;     // first bucket task of each layer (tasks of a layer = Hkv * nbuckets)
+};
+
+template <typename T, int LG>
+__global__ void __launch_bounds__(NTM)
+merge_kernel(MergeTables t, int lc, const float* __restrict__ Ag, int Hkv, int64_t n, int d,
+             int bucket, int64_t nbuckets, int64_t ntask) {
+  constexpr int W = El<T>::N;
+  constexpr int RPP = 64 / LG;                   // rows per wave pass
+  const int lane = threadIdx.x & 63;
+  const int64_t task = (int64_t)blockIdx.x * (NTM / 64) + threadIdx.x / 64;
+  if (task >= ntask) return;                     // waves are independent (no barriers)
+  int l = 0;
+  while (l + 1 < lc && t.task0.v[l + 1] <= task) ++l;
+  const int64_t local = task - t.task0.v[l];
+  const int g = (int)(local / nbuckets);
+  const int64_t b0 = (local % nbuckets) * bucket;
+  const int64_t b1 = min(n, b0 + bucket);
+  const int64_t m = t.m.v[l];
+  const int32_t* ip = (const int32_t*)t.idx.p[l] + (int64_t)g * m;
+  const int64_t lo = lower_bound(ip, m, b0), hi = lower_bound(ip, m, b1);
+  if (lo == hi) return;                          // no kept token: evicted tokens dropped
+  const float* A = Ag + ((int64_t)l * Hkv + g) * n;
+  const T* Vg = (const T*)t.V.p[l] + (int64_t)g * n * d;
+  const T* Kg = (const T*)t.K.p[l] + (int64_t)g * n * d;
+  T* Vo = (T*)t.Vo.p[l] + (int64_t)g * m * d;
+  T* Ko = (T*)t.Ko.p[l] + (int64_t)g * m * d;
+  float* lR = (float*)t.logR.p[l] + (int64_t)g * m;
+
+  // merge target: the kept token with the largest A, ties to the lower index
+  float bv = -INFINITY;
+  int64_t bs = INT64_MAX;
+  for (int64_t s = lo + lane; s < hi; s += 64) {
+    const float a = A[ip[s]];
+    if (bs == INT64_MAX || a > bv) { bv = a; bs = s; }   // s ascends per lane: first max kept
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const float ov = __shfl_xor(bv, o, 64);
+    const int64_t os = __shfl_xor(bs, o, 64);
+    if (ov > bv || (ov == bv && os < bs)) { bv = ov; bs = os; }
+  }
+  // every lane holds the same winner; the clamp only guards against NaN scores
+  const int64_t ts = (bs >= lo && bs < hi) ? bs : lo, tt = ip[ts];
+  const float At = A[tt];
+
+  const int rg = lane / LG, c = lane % LG;
+  float vt[W];
+  El<T>::unpack(*reinterpret_cast<const uint4*>(Vg + tt * d + c * W), vt);
+  float nt2 = 0.f;
+#pragma unroll
+  for (int e = 0; e < W; ++e) nt2 += vt[e] * vt[e];
+  nt2 = group_sum<LG>(nt2);
+  const float nt = sqrtf(nt2);
+
+  float num[W];
+#pragma unroll
+  for (int e = 0; e < W; ++e) num[e] = 0.f;
+  float den = 0.f;
+  int64_t ptr = lo;                              // walk of the kept list, per row group
+  for (int64_t e = b0 + rg; e < b1; e += RPP) {
+    while (ptr < hi && ip[ptr] < e) ++ptr;
+    const bool kept = ptr < hi && ip[ptr] == e;
+    const uint4 raw = *reinterpret_cast<const uint4*>(Vg + e * d + c * W);
+    if (kept) {
+      *reinterpret_cast<uint4*>(Ko + ptr * d + c * W) = *reinterpret_cast<const uint4*>(Kg + e * d + c * W);
+      if (e != tt) {
+        *reinterpret_cast<uint4*>(Vo + ptr * d + c * W) = raw;
+        if (c == 0) lR[ptr] = 0.f;
+      }
+      continue;
+    }
+    float ve[W];
+    El<T>::unpack(raw, ve);
+    float dot = 0.f, ne2 = 0.f;
+#pragma unroll
+    for (int i = 0; i < W; ++i) { dot += ve[i] * vt[i]; ne2 += ve[i] * ve[i]; }
+    dot = group_sum<LG>(dot);
+    ne2 = group_sum<LG>(ne2);
+    const float nd = sqrtf(ne2) * nt;
+    const float gate = nd > 0.f ? fmaxf(dot / nd, 0.f) : 0.f;
+    const float wgt = gate * A[e];
+#pragma unroll
+    for (int i = 0; i < W; ++i) num[i] += wgt * ve[i];
+    den += wgt;
+  }
+  // sum the row groups (lanes with the same chunk c)
+#pragma unroll
+  for (int o = LG; o < 64; o <<= 1) {
+#pragma unroll
+    for (int i = 0; i < W; ++i) num[i] += __shfl_xor(num[i], o, 64);
+    den += __shfl_xor(den, o, 64);
+  }
+  if (rg == 0) {
+    float out[W];
+    float lr = 0.f;
+    if (den > 0.f) {
+      const float inv = 1.0f / (At + den);
+#pragma unroll
+      for (int i = 0; i < W; ++i) out[i] = (At * vt[i] + num[i]) * inv;
+      lr = log1pf(den / At);
+      *reinterpret_cast<uint4*>(Vo + ts * d + c * W) = El<T>::pack(out);
+    } else {
+      *reinterpret_cast<uint4*>(Vo + ts * d + c * W) =
+          *reinterpret_cast<const uint4*>(Vg + tt * d + c * W);
+    }
+    if (c == 0) lR[ts] = lr;
+  }
+}
+
+template <typename T>
+bool launch_vatp(int LG, dim3 grid, hipStream_t s, const float* A_hq, const ConstPtrs& V, int Hq,
+                 int Hkv, int64_t n, int d, int64_t nblk, float* U, float* Ag) {
+#define KVC_V(LGV) hipLaunchKernelGGL((vatp_union_kernel<T, LGV>), grid, dim3(NT), 0, s, A_hq, V, Hq, Hkv, n, d, nblk, U, Ag)
+  switch (LG) {
+    case 4: KVC_V(4); return true;
+    case 8: KVC_V(8); return true;
+    case 16: KVC_V(16); return true;
+    case 32: KVC_V(32); return true;
+    default: return false;
+  }
+#undef KVC_V
+}
+
+template <typename T>
+bool launch_merge(int LG, dim3 grid, hipStream_t s, const MergeTables& t, int lc, const float* Ag,
+                  int Hkv, int64_t n, int d, int bucket, int64_t nbuckets, int64_t ntask) {
+#define KVC_M(LGV) hipLaunchKernelGGL((merge_kernel<T, LGV>), grid, dim3(NTM), 0, s, t, lc, Ag, Hkv, n, d, bucket, nbuckets, ntask)
+  switch (LG) {
+    case 4: KVC_M(4); return true;
+    case 8: KVC_M(8); return true;
+    case 16: KVC_M(16); return true;
+    case 32: KVC_M(32); return true;
+    default: return false;
+  }
+#undef KVC_M
+}
+
+bool lg_ok(int d, int dtype, int* LG) {
+  const int rb = d * dtype_size(dtype);
+  if (rb % 16) return false;
+  *LG = rb / 16;
+  return *LG == 4 || *LG == 8 || *LG == 16 || *LG == 32;
+}
+
+}  // namespace
+}  // namespace kvc
+
+using namespace kvc;
+
+extern "C" int kvc_vatp_union(const float* A_hq, const void* const* V, int dtype, int L, int Hq,
+                              int Hkv, int64_t n, int d, float* U_out, float* Ag_out, void* stream) {
+  clear_error();
+  if (!dtype_ok(dtype)) return KVC_FAIL(KVC_ERR_DTYPE, "kvc_vatp_union: dtype %d", dtype);
+  KVC_REQUIRE(L >= 1 && L <= KVC_MAX_LAYERS, "kvc_vatp_union: need 1 <= L <= %d", KVC_MAX_LAYERS);
+  KVC_REQUIRE(Hkv >= 1 && Hq >= Hkv && Hq % Hkv == 0, "kvc_vatp_union: need Hq %% Hkv == 0");
+  KVC_REQUIRE(n >= 1 && n <= 0x7fffffffLL, "kvc_vatp_union: need 1 <= n < 2^31");
+  KVC_REQUIRE(A_hq && V && U_out && Ag_out, "kvc_vatp_union: null pointer");
+  int LG = 0;
+  KVC_REQUIRE(lg_ok(d, dtype, &LG), "kvc_vatp_union: need d * elsize in {64, 128, 256, 512} bytes");
+  for (int l = 0; l < L; ++l)
+    KVC_REQUIRE(V[l] && (uintptr_t)V[l] % 16 == 0, "kvc_vatp_union: V[%d] null or not 16-byte aligned", l);
+  hipStream_t s = as_stream(stream);
+  const int64_t nblk = (n + NT / LG - 1) / (NT / LG);
+  for (int l0 = 0; l0 < L; l0 += kLayersPerLaunch) {
+    const int lc = min(kLayersPerLaunch, L - l0);
+    ConstPtrs vt{};
+    for (int i = 0; i < lc; ++i) vt.p[i] = V[l0 + i];
+    const dim3 grid((unsigned)((int64_t)lc * Hkv * nblk));
+    const int64_t off = (int64_t)l0 * Hkv * n;
+    if (dtype == KVC_BF16)
+      launch_vatp<uint16_t>(LG, grid, s, A_hq + (int64_t)l0 * Hq * n, vt, Hq, Hkv, n, d, nblk, U_out + off, Ag_out + off);
+    else
+      launch_vatp<float>(LG, grid, s, A_hq + (int64_t)l0 * Hq * n, vt, Hq, Hkv, n, d, nblk, U_out + off, Ag_out + off);
+  }
+  return launch_status("kvc_vatp_union");
+}
+
+extern "C" int kvc_merge_gated(const void* const* K, const void* const* V, int dtype, const float* Ag,
+                               int L, int Hkv, int64_t n, int d, const int32_t* const* idx,
+                               const int64_t* m_keep, int bucket, void* const* K_out,
+                               void* const* V_out, float* const* logR_out, void* stream) {
+  clear_error();
+  if (!dtype_ok(dtype)) return KVC_FAIL(KVC_ERR_DTYPE, "kvc_merge_gated: dtype %d", dtype);
+  KVC_REQUIRE(L >= 1 && L <= KVC_MAX_LAYERS, "kvc_merge_gated: need 1 <= L <= %d", KVC_MAX_LAYERS);
+  KVC_REQUIRE(Hkv >= 1 && n >= 1 && n <= 0x7fffffffLL, "kvc_merge_gated: need Hkv >= 1, 1 <= n < 2^31");
+  KVC_REQUIRE(bucket >= 1, "kvc_merge_gated: bucket < 1");
+  KVC_REQUIRE(K && V && Ag && idx && m_keep && K_out && V_out && logR_out, "kvc_merge_gated: null pointer");
+  int LG = 0;
+  KVC_REQUIRE(lg_ok(d, dtype, &LG), "kvc_merge_gated: need d * elsize in {64, 128, 256, 512} bytes");
+  for (int l = 0; l < L; ++l) {
+    KVC_REQUIRE(K[l] && V[l] && idx[l] && K_out[l] && V_out[l] && logR_out[l],
+                "kvc_merge_gated: null pointer in layer %d", l);
+    KVC_REQUIRE((uintptr_t)K[l] % 16 == 0 && (uintptr_t)V[l] % 16 == 0 && (uintptr_t)K_out[l] % 16 == 0 &&
+                (uintptr_t)V_out[l] % 16 == 0, "kvc_merge_gated: tensors of layer %d not 16-byte aligned", l);
+    KVC_REQUIRE(m_keep[l] >= 1 && m_keep[l] <= n, "kvc_merge_gated: m_keep[%d] outside [1, n]", l);
+  }
+  const int64_t nbuckets = (n + bucket - 1) / bucket;
+  KVC_REQUIRE((int64_t)kLayersPerLaunch * Hkv * nbuckets / 4 <= 0x7fffffffLL, "kvc_merge_gated: too many buckets");
+  hipStream_t s = as_stream(stream);
+  for (int l0 = 0; l0 < L; l0 += kLayersPerLaunch) {
+    const int lc = min(kLayersPerLaunch, L - l0);
+    MergeTables t{};
+    int64_t ntask = 0;
+    for (int i = 0; i < lc; ++i) {
+      t.K.p[i] = K[l0 + i]; t.V.p[i] = V[l0 + i]; t.idx.p[i] = idx[l0 + i];
+      t.Ko.p[i] = K_out[l0 + i]; t.Vo.p[i] = V_out[l0 + i]; t.logR.p[i] = logR_out[l0 + i];
+      t.m.v[i] = m_keep[l0 + i];
+      t.task0.v[i] = ntask;
+      ntask += (int64_t)Hkv * nbuckets;
+    }
+    const dim3 grid((unsigned)((ntask + 3) / 4));
+    const float* Agl = Ag + (int64_t)l0 * Hkv * n;
+    if (dtype == KVC_BF16)
+      launch_merge<uint16_t>(LG, grid, s, t, lc, Agl, Hkv, n, d, bucket, nbuckets, ntask);
+    else
+      launch_merge<float>(LG, grid, s, t, lc, Agl, Hkv, n, d, bucket, nbuckets, ntask);
+  }
+  return launch_status("kvc_merge_gated");
+}

@@ -1,0 +1,158 @@
+"""Host orchestration of the two compression paths over the C ABI.
+
+InfoKV ([InfoKV] Method / Technical detail): H (top-k entropy of the final
+logits), D (layer-wise distance), A (window attention), fuse -> S, budget,
+select -> kept indices, compact -> K_c, V_c.
+
+SelKV ([SelKV] section 2, pipeline steps 1-5): per-head window attention, VATP
+union, select, then the fused route / gate / merge / ln R / gather.
+
+A plan allocates every output and workspace once; ``run`` only enqueues HIP
+work (plus, for the adaptive budget, one device-to-host copy of L floats and
+the host budget call).  Nothing here computes on the CPU.
+"""
+from __future__ import annotations
+
+import math
+
+import torch
+
+from . import binding as B
+from .configs import Workload
+
+
+def _carve(pool: torch.Tensor, sizes, shape_of):
+    """Per-layer views into one flat buffer (no allocation)."""
+    out, off = [], 0
+    for s in sizes:
+        shp = shape_of(s)
+        num = math.prod(shp)
+        out.append(pool[off:off + num].view(shp))
+        off += num
+    return out
+
+
+class InfoKVPlan:
+    def __init__(self, w: Workload, device="cuda"):
+        assert w.method == "infokv"
+        self.w = w
+        self.device = device
+        L, Hkv, n, d = w.layers, w.heads_kv, w.n, w.head_dim
+        f32 = torch.float32
+        dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+        self.scale = 1.0 / math.sqrt(d)
+        self.H = torch.empty(n, dtype=f32, device=device)
+        self.D = torch.empty(L, n, dtype=f32, device=device)
+        self.A = torch.empty(L, Hkv, n, dtype=f32, device=device)
+        self.S = torch.empty(L, Hkv, n, dtype=f32, device=device)
+        self.Ebar = torch.empty(L, dtype=f32, device=device)
+        dtc = B.KVC_BF16 if w.dtype == "bf16" else B.KVC_F32
+        self.ws_attn = torch.empty(max(1, B.kvc_score_window_attn_workspace_size(
+            L, w.heads_q, Hkv, n, w.window, d, dtc)), dtype=torch.uint8, device=device)
+        self.ws_fuse = torch.empty(max(1, B.kvc_fuse_scores_workspace_size(L, n)),
+                                   dtype=torch.uint8, device=device)
+        budgets = w.budgets()
+        if budgets is not None:
+            self.k = [B.kvc_uniform_budget(w.keep_fraction, n, w.window)] * L
+            total = sum(self.k)
+        else:
+            self.k = None
+            total = w.adaptive_total()
+        self.total = total
+        self.idx_pool = torch.empty(Hkv * total, dtype=torch.int32, device=device)
+        self.kc_pool = torch.empty(Hkv * total * d, dtype=dt, device=device)
+        self.vc_pool = torch.empty(Hkv * total * d, dtype=dt, device=device)
+        if self.k is not None:
+            self._views(self.k)
+
+    def _views(self, k):
+        Hkv, d = self.w.heads_kv, self.w.head_dim
+        self.idx = _carve(self.idx_pool, k, lambda s: (Hkv, s))
+        self.Kc = _carve(self.kc_pool, k, lambda s: (Hkv, s, d))
+        self.Vc = _carve(self.vc_pool, k, lambda s: (Hkv, s, d))
+
+    def run(self, inp: dict, stream=None, mark=None):
+        """Enqueue the whole path.  ``mark(name)``, if given, is called before
+        the first step ("start") and after each step (for event timing)."""
+        w = self.w
+        mark = mark or (lambda name: None)
+        mark("start")
+        chunk = w.logits_chunk_rows or w.n
+        logits = inp["logits"]
+        for r0 in range(0, w.n, chunk):
+            r1 = min(w.n, r0 + chunk)
+            B.kvc_topk_entropy(logits[r0:r1], w.topk_entropy, self.H[r0:r1], stream=stream)
+        mark("topk_entropy")
+        B.kvc_repr_distance(inp["h"], inp["h_final"], w.tau, self.D, stream=stream)
+        mark("repr_distance")
+        B.kvc_score_window_attn(inp["q_win"], inp["k"], self.scale, False, self.A,
+                                ws=self.ws_attn, stream=stream)
+        mark("window_attn")
+        B.kvc_fuse_scores(self.A, self.D, self.H, w.alpha_fuse, self.S, self.Ebar,
+                          ws=self.ws_fuse, stream=stream)
+        mark("fuse_scores")
+        if w.adaptive_fraction:
+            ebar = self.Ebar.cpu()                       # the one host sync of the path
+            k = B.kvc_adaptive_budget(ebar.numpy(), self.total, w.window, w.n)
+            if sum(k) != self.total:
+                raise RuntimeError("adaptive budget clamp changed the total")
+            self.k = k
+            self._views(k)
+        B.kvc_select_topk(self.S, self.k, w.window, self.idx, stream=stream)
+        mark("select_topk")
+        B.kvc_compact(inp["k"], inp["v"], self.idx, self.k, self.Kc, self.Vc, stream=stream)
+        mark("compact")
+        return self
+
+
+class SelKVPlan:
+    def __init__(self, w: Workload, device="cuda"):
+        assert w.method == "selkv"
+        self.w = w
+        L, Hq, Hkv, n, d = w.layers, w.heads_q, w.heads_kv, w.n, w.head_dim
+        f32 = torch.float32
+        dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+        dtc = B.KVC_BF16 if w.dtype == "bf16" else B.KVC_F32
+        self.scale = 1.0 / math.sqrt(d)
+        self.A_hq = torch.empty(L, Hq, n, dtype=f32, device=device)
+        self.U = torch.empty(L, Hkv, n, dtype=f32, device=device)
+        self.Ag = torch.empty(L, Hkv, n, dtype=f32, device=device)
+        self.ws_attn = torch.empty(max(1, B.kvc_score_window_attn_workspace_size(
+            L, Hq, Hkv, n, w.window, d, dtc)), dtype=torch.uint8, device=device)
+        m = B.kvc_uniform_budget(w.keep_fraction, n, w.window)
+        self.m = [m] * L
+        self.idx = [torch.empty(Hkv, m, dtype=torch.int32, device=device) for _ in range(L)]
+        self.Kc = [torch.empty(Hkv, m, d, dtype=dt, device=device) for _ in range(L)]
+        self.Vc = [torch.empty(Hkv, m, d, dtype=dt, device=device) for _ in range(L)]
+        self.logR = [torch.empty(Hkv, m, dtype=f32, device=device) for _ in range(L)]
+
+    def run(self, inp: dict, stream=None, mark=None):
+        w = self.w
+        mark = mark or (lambda name: None)
+        mark("start")
+        B.kvc_score_window_attn(inp["q_win"], inp["k"], self.scale, True, self.A_hq,
+                                ws=self.ws_attn, stream=stream)
+        mark("window_attn")
+        B.kvc_vatp_union(self.A_hq, inp["v"], self.U, self.Ag, stream=stream)
+        mark("vatp_union")
+        B.kvc_select_topk(self.U, self.m, w.window, self.idx, stream=stream)
+        mark("select_topk")
+        B.kvc_merge_gated(inp["k"], inp["v"], self.Ag, self.idx, self.m, w.bucket,
+                          self.Kc, self.Vc, self.logR, stream=stream)
+        mark("merge_gated")
+        return self
+
+    def decode_check(self, inp: dict, stream=None):
+        """Compensated decode over the compacted cache and plain decode over the
+        full cache, one query per head and layer: (o', lse', o, lse)."""
+        w = self.w
+        L, Hq, d = w.layers, w.heads_q, w.head_dim
+        q = [inp["q_dec"][l] for l in range(L)]
+        o_c = torch.empty(L, Hq, d, dtype=torch.float32, device=self.U.device)
+        l_c = torch.empty(L, Hq, dtype=torch.float32, device=self.U.device)
+        o_f = torch.empty_like(o_c)
+        l_f = torch.empty_like(l_c)
+        B.kvc_decode_attn(q, self.Kc, self.Vc, self.logR, w.alpha_bias, self.scale, o_c, l_c,
+                          stream=stream)
+        B.kvc_decode_attn(q, inp["k"], inp["v"], None, 0.0, self.scale, o_f, l_f, stream=stream)
+        return o_c, l_c, o_f, l_f

@@ -1,0 +1,331 @@
+"""Per-kernel GPU parity against the float64 oracle, through the C ABI.
+
+Sizes are small enough for the oracle to finish in seconds while still spanning
+several tiles / chunks and a ragged tail.  Tolerances: float32-accumulated
+scores 1e-3 relative; selection and gather bit-exact given identical scores.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from kv_cache_compression_softmax_amd import synth
+from oracle import infokv, selkv
+from tests.gpu_util import announce, assert_rel, host_bits, host_f64, need_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    d = need_gpu()
+    from kv_cache_compression_softmax_amd import binding
+    binding.lib()                        # fail loudly if the HIP library is missing
+    return d
+
+
+def B():
+    from kv_cache_compression_softmax_amd import binding
+    return binding
+
+
+def gen(shape, seed, dev, dtype=torch.bfloat16, scale=1.0):
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed)
+    x = torch.randn(shape, generator=g, device=dev, dtype=torch.float32) * scale
+    return x.to(dtype)
+
+
+# ----------------------------------------------------------------- top-k entropy
+ENTROPY_CASES = [
+    # rows, vocab, stride, k, dtype, kind
+    (512, 2048, 2048, 64, torch.float32, "normal3"),       # tiny-workload shape
+    (70, 128256, 128256, 256, torch.bfloat16, "spiked"),   # Llama vocabulary
+    (33, 152064, 152064, 256, torch.bfloat16, "spiked"),   # Qwen-size vocabulary
+    (17, 128257, 128257, 256, torch.bfloat16, "normal4"),  # odd width: unaligned rows
+    (9, 5000, 5003, 1024, torch.bfloat16, "normal4"),      # stride > vocab, max k
+    (9, 4096, 4096, 1, torch.bfloat16, "normal4"),         # k = 1 -> H = 0
+    (5, 300, 300, 300, torch.float32, "normal4"),          # k = vocab
+    (6, 9000, 9000, 256, torch.bfloat16, "ascending"),     # worst case for the filter
+    (6, 9000, 9000, 256, torch.bfloat16, "ties"),          # many equal values at the threshold
+    (4, 20000, 20000, 64, torch.float32, "flat"),          # all equal -> ln k
+]
+
+
+def entropy_input(rows, stride, kind, dtype, dev, seed):
+    if kind == "ascending":
+        base = torch.linspace(-8, 8, stride, device=dev)[None, :].repeat(rows, 1)
+        return base.to(dtype)
+    if kind == "ties":
+        g = torch.Generator(device=dev)
+        g.manual_seed(seed)
+        return torch.randint(0, 12, (rows, stride), generator=g, device=dev).to(torch.float32).div(2).to(dtype)
+    if kind == "flat":
+        return torch.full((rows, stride), 0.5, device=dev, dtype=dtype)
+    scale = 3.0 if kind == "normal3" else 4.0
+    x = gen((rows, stride), seed, dev, torch.float32, scale)
+    if kind == "spiked":
+        g = torch.Generator(device=dev)
+        g.manual_seed(seed + 1)
+        cols = torch.randint(0, stride, (rows, 8), generator=g, device=dev)
+        cnt = torch.randint(1, 9, (rows, 1), generator=g, device=dev)
+        x.scatter_add_(1, cols, (torch.arange(8, device=dev)[None, :] < cnt).float() * 12.0)
+    return x.to(dtype)
+
+
+@pytest.mark.parametrize("case", ENTROPY_CASES, ids=lambda c: f"{c[0]}x{c[1]}s{c[2]}k{c[3]}{c[5]}")
+def test_topk_entropy(dev, case):
+    rows, vocab, stride, k, dtype, kind = case
+    announce("topk_entropy", case)
+    z = entropy_input(rows, stride, kind, dtype, dev, seed=rows * 7 + k)
+    H = torch.full((rows,), -1.0, device=dev)
+    B().kvc_topk_entropy(z, k, H, vocab=vocab)
+    torch.cuda.synchronize()
+    ref = infokv.topk_entropy(host_f64(z)[:, :vocab], k)
+    got = H.cpu().numpy()
+    if k == 1:
+        assert np.all(got == 0)
+    else:
+        assert_rel(got, ref, 1e-3, what="H")
+    if kind == "flat":
+        np.testing.assert_allclose(got, math.log(k), rtol=1e-6)
+
+
+def test_topk_entropy_deterministic(dev):
+    z = entropy_input(64, 128256, "spiked", torch.bfloat16, dev, 5)
+    H1 = torch.empty(64, device=dev)
+    H2 = torch.empty(64, device=dev)
+    B().kvc_topk_entropy(z, 256, H1)
+    B().kvc_topk_entropy(z, 256, H2)
+    assert torch.equal(H1, H2)
+
+
+# ----------------------------------------------------------------- distance
+DIST_CASES = [
+    # L, n, hidden, dtype
+    (1, 512, 256, torch.float32),
+    (3, 2051, 3072, torch.bfloat16),
+    (2, 1029, 4096, torch.bfloat16),
+    (2, 77, 1000, torch.bfloat16),       # width not a multiple of 8: element path
+    (2, 65, 8192, torch.bfloat16),       # 16 vectors per lane
+    (35, 130, 512, torch.bfloat16),      # more layers than one launch holds
+]
+
+
+@pytest.mark.parametrize("case", DIST_CASES, ids=str)
+def test_repr_distance(dev, case):
+    L, n, hidden, dtype = case
+    announce("repr_distance", case)
+    hf32 = gen((n, hidden), 11, dev, torch.float32)
+    layers = []
+    for l in range(L):
+        c = 0.2 + 0.8 * l / max(1, L - 1)
+        layers.append((c * hf32 + math.sqrt(max(0.0, 1 - c * c)) * gen((n, hidden), 100 + l, dev, torch.float32)).to(dtype))
+    hf = hf32.to(dtype)
+    D = torch.empty(L, n, device=dev)
+    B().kvc_repr_distance(layers, hf, 1.0, D)
+    torch.cuda.synchronize()
+    ref = np.stack([infokv.repr_distance(host_f64(layers[l]), host_f64(hf), 1.0) for l in range(L)])
+    assert_rel(D.cpu().numpy(), ref, 1e-3, what="D")
+    if L > 1:   # last layer equals the final state bit for bit -> D = tau
+        np.testing.assert_allclose(D[L - 1].cpu().numpy(), 1.0, atol=1e-6)
+
+
+# ----------------------------------------------------------------- window attention
+WIN_CASES = [
+    # L, Hq, Hkv, n, w, d, dtype
+    (1, 4, 2, 512, 16, 64, torch.float32),          # tiny workload
+    (2, 24, 8, 2085, 32, 128, torch.bfloat16),      # Llama-3.2-3B heads, ragged n
+    (2, 32, 8, 1600, 32, 128, torch.bfloat16),      # Llama-3.1-8B heads
+    (1, 8, 2, 1000, 16, 128, torch.bfloat16),       # padding rows in every tile
+    (1, 4, 2, 700, 48, 128, torch.bfloat16),        # two tiles per head
+    (1, 16, 2, 600, 32, 128, torch.bfloat16),       # 8 tiles: two register groups
+    (1, 8, 4, 333, 32, 64, torch.bfloat16),         # head dim 64
+    (1, 4, 2, 40, 33, 128, torch.bfloat16),         # window nearly the whole sequence
+    (1, 2, 1, 31, 31, 64, torch.bfloat16),          # w = n < 32
+    (1, 6, 2, 150, 20, 32, torch.float32),          # float32 path, G = 3
+]
+
+
+@pytest.mark.parametrize("per_head", [False, True])
+@pytest.mark.parametrize("case", WIN_CASES, ids=str)
+def test_window_attention(dev, case, per_head):
+    L, Hq, Hkv, n, w, d, dtype = case
+    announce("window_attn", case, per_head)
+    q = [gen((Hq, w, d), 20 + l, dev, dtype) for l in range(L)]
+    k = [gen((Hkv, n, d), 40 + l, dev, dtype) for l in range(L)]
+    A = torch.empty(L, Hq if per_head else Hkv, n, device=dev)
+    B().kvc_score_window_attn(q, k, 1 / math.sqrt(d), per_head, A)
+    torch.cuda.synchronize()
+    for l in range(L):
+        ref = infokv.window_attention(host_f64(q[l]), host_f64(k[l]), per_query_head=per_head)
+        assert_rel(A[l].cpu().numpy(), ref, 1e-3, what=f"A layer {l}")
+    np.testing.assert_allclose(A.sum(dim=2).cpu().numpy(), 1.0, atol=1e-4)
+
+
+# ----------------------------------------------------------------- fuse
+@pytest.mark.parametrize("L,Hkv,n", [(1, 2, 512), (3, 8, 20001), (2, 4, 70000)])
+def test_fuse_scores(dev, L, Hkv, n):
+    announce("fuse", L, Hkv, n)
+    g = torch.Generator(device=dev)
+    g.manual_seed(n)
+    A = torch.rand(L, Hkv, n, generator=g, device=dev)
+    A /= A.sum(dim=2, keepdim=True)
+    D = 1.0 + 2.0 * torch.rand(L, n, generator=g, device=dev)
+    H = 5.5 * torch.rand(n, generator=g, device=dev)
+    S = torch.empty_like(A)
+    Eb = torch.empty(L, device=dev)
+    B().kvc_fuse_scores(A, D, H, 0.9, S, Eb)
+    torch.cuda.synchronize()
+    An, Dn, Hn = host_f64(A), host_f64(D), host_f64(H)
+    for l in range(L):
+        Sr, Ebr, _, _ = infokv.fuse_scores(An[l], Dn[l], Hn, 0.9)
+        assert_rel(S[l].cpu().numpy(), Sr, 1e-3, what="S")
+        assert_rel([Eb[l].item()], [Ebr], 1e-3, what="Ebar")
+
+
+# ----------------------------------------------------------------- select + compact
+SELECT_CASES = [
+    # L, Hkv, n, k, w, tie_levels
+    (1, 2, 512, 128, 16, 0),
+    (3, 8, 2085, 834, 32, 0),
+    (2, 8, 2085, 834, 32, 5),        # heavy ties at the threshold
+    (1, 4, 4000, 4000, 32, 0),       # keep everything
+    (1, 4, 4000, 32, 32, 0),         # window only
+    (1, 4, 4000, 10, 32, 0),         # budget smaller than the window
+    (1, 4, 999, 300, 0, 3),          # no window
+    (1, 2, 102400, 25600, 32, 0),    # SelKV length
+    (2, 1, 50, 1, 0, 1),             # one token, all tied
+]
+
+
+@pytest.mark.parametrize("case", SELECT_CASES, ids=str)
+def test_select_and_compact(dev, case):
+    L, Hkv, n, k, w, levels = case
+    announce("select", case)
+    S = synth.random_scores((L, Hkv, n), dev, seed=n + k, tie_levels=levels)
+    idx = [torch.full((Hkv, k), -1, dtype=torch.int32, device=dev) for _ in range(L)]
+    B().kvc_select_topk(S, [k] * L, w, idx)
+    d = 128
+    K = [gen((Hkv, n, d), 60 + l, dev) for l in range(L)]
+    V = [gen((Hkv, n, d), 80 + l, dev) for l in range(L)]
+    Kc = [torch.empty(Hkv, k, d, dtype=torch.bfloat16, device=dev) for _ in range(L)]
+    Vc = [torch.empty_like(x) for x in Kc]
+    B().kvc_compact(K, V, idx, [k] * L, Kc, Vc)
+    torch.cuda.synchronize()
+    Sn = S.cpu().numpy()
+    for l in range(L):
+        ref = infokv.select_topk(Sn[l], k, w)
+        np.testing.assert_array_equal(idx[l].cpu().numpy(), ref)
+        kr, vr = infokv.compact(host_bits(K[l]), host_bits(V[l]), ref)
+        np.testing.assert_array_equal(host_bits(Kc[l]), kr)
+        np.testing.assert_array_equal(host_bits(Vc[l]), vr)
+
+
+def test_select_ragged_budgets_and_compact_f32(dev):
+    L, Hkv, n, w, d = 5, 3, 777, 8, 64
+    ks = [8, 100, 777, 9, 400]
+    announce("select ragged", ks)
+    S = synth.random_scores((L, Hkv, n), dev, seed=3, tie_levels=7)
+    idx = [torch.empty(Hkv, k, dtype=torch.int32, device=dev) for k in ks]
+    B().kvc_select_topk(S, ks, w, idx)
+    K = [gen((Hkv, n, d), 5 + l, dev, torch.float32) for l in range(L)]
+    Kc = [torch.empty(Hkv, k, d, device=dev) for k in ks]
+    B().kvc_compact(K, None, idx, ks, Kc, None)
+    torch.cuda.synchronize()
+    Sn = S.cpu().numpy()
+    for l in range(L):
+        ref = infokv.select_topk(Sn[l], ks[l], w)
+        np.testing.assert_array_equal(idx[l].cpu().numpy(), ref)
+        kr, _ = infokv.compact(host_bits(K[l]), host_bits(K[l]), ref)
+        np.testing.assert_array_equal(host_bits(Kc[l]), kr)
+
+
+def test_select_deterministic(dev):
+    S = synth.random_scores((4, 8, 5000), dev, seed=9, tie_levels=4)
+    a = [torch.empty(8, 1000, dtype=torch.int32, device=dev) for _ in range(4)]
+    b = [torch.empty_like(x) for x in a]
+    B().kvc_select_topk(S, [1000] * 4, 32, a)
+    B().kvc_select_topk(S, [1000] * 4, 32, b)
+    assert all(torch.equal(x, y) for x, y in zip(a, b))
+
+
+# ----------------------------------------------------------------- SelKV pieces
+SELKV_CASES = [
+    # L, Hq, Hkv, n, w, d, m, bucket
+    (2, 32, 8, 2048, 32, 128, 512, 64),
+    (1, 8, 2, 1000, 32, 128, 250, 64),       # last bucket partial
+    (1, 4, 2, 700, 16, 64, 300, 50),         # head dim 64, odd bucket
+    (1, 4, 4, 520, 32, 128, 40, 128),        # MHA, some buckets with no kept token
+]
+
+
+@pytest.mark.parametrize("case", SELKV_CASES, ids=str)
+def test_selkv_pieces(dev, case):
+    L, Hq, Hkv, n, w, d, m, bucket = case
+    announce("selkv", case)
+    q = [gen((Hq, w, d), 200 + l, dev) for l in range(L)]
+    K = [gen((Hkv, n, d), 220 + l, dev) for l in range(L)]
+    V = [gen((Hkv, n, d), 240 + l, dev) for l in range(L)]
+    A_hq = torch.empty(L, Hq, n, device=dev)
+    B().kvc_score_window_attn(q, K, 1 / math.sqrt(d), True, A_hq)
+    U = torch.empty(L, Hkv, n, device=dev)
+    Ag = torch.empty(L, Hkv, n, device=dev)
+    B().kvc_vatp_union(A_hq, V, U, Ag)
+    torch.cuda.synchronize()
+    G = Hq // Hkv
+    for l in range(L):
+        Vn = host_f64(V[l])
+        Ah = host_f64(A_hq[l])
+        ref_o = selkv.selkv_layer(host_f64(q[l]), host_f64(K[l]), Vn, m, w, bucket)
+        assert_rel(Ah, ref_o["A_hq"], 1e-3, what="A_hq")
+        _, U_ref = selkv.vatp_union(ref_o["A_hq"], Vn)
+        assert_rel(U[l].cpu().numpy(), U_ref, 1e-3, what="U")
+        assert_rel(Ag[l].cpu().numpy(), ref_o["A_g"], 1e-3, what="Ag")
+        # selection given identical scores (the oracle's float32 U): bit-exact
+        U32 = torch.from_numpy(ref_o["U32"]).to(dev)[None].contiguous()
+        idx = [torch.empty(Hkv, m, dtype=torch.int32, device=dev)]
+        B().kvc_select_topk(U32, [m], w, idx)
+        np.testing.assert_array_equal(idx[0].cpu().numpy(), ref_o["idx"])
+        # merge given identical inputs: the oracle's idx and float32-rounded A_g
+        Ag32 = ref_o["A_g"].astype(np.float32)
+        Kc = [torch.empty(Hkv, m, d, dtype=torch.bfloat16, device=dev)]
+        Vc = [torch.empty_like(Kc[0])]
+        lr = [torch.empty(Hkv, m, device=dev)]
+        B().kvc_merge_gated([K[l]], [V[l]], torch.from_numpy(Ag32).to(dev)[None].contiguous(), idx, [m],
+                            bucket, Kc, Vc, lr)
+        torch.cuda.synchronize()
+        kr, _ = infokv.compact(host_bits(K[l]), host_bits(K[l]), ref_o["idx"])
+        np.testing.assert_array_equal(host_bits(Kc[0]), kr)
+        Vp_ref = np.empty((Hkv, m, d))
+        lnR_ref = np.empty((Hkv, m))
+        for gi in range(Hkv):
+            Agd = Ag32[gi].astype(np.float64)
+            tgt = selkv.route(ref_o["idx"][gi], Agd, n, bucket)
+            Vp_ref[gi], lnR_ref[gi], _ = selkv.merge_group(Vn[gi], Agd, ref_o["idx"][gi], tgt)
+        got_v = host_f64(Vc[0])
+        assert np.max(np.abs(got_v - Vp_ref)) <= 2e-2, "merged V"
+        assert_rel(lr[0].cpu().numpy(), lnR_ref, 1e-3, floor=1e-4, what="ln R")
+        assert np.all(lr[0].cpu().numpy() >= 0)
+
+
+# ----------------------------------------------------------------- decode
+@pytest.mark.parametrize("Hq,Hkv,length,d,bias", [(32, 8, 3000, 128, True), (4, 2, 100, 64, False),
+                                                  (8, 8, 1025, 128, True), (6, 2, 2049, 64, True)])
+def test_decode_attention(dev, Hq, Hkv, length, d, bias):
+    L = 2
+    announce("decode", Hq, Hkv, length, d, bias)
+    q = [gen((Hq, d), 300 + l, dev) for l in range(L)]
+    K = [gen((Hkv, length, d), 320 + l, dev) for l in range(L)]
+    V = [gen((Hkv, length, d), 340 + l, dev) for l in range(L)]
+    lr = [torch.rand(Hkv, length, device=dev) * 2 for _ in range(L)] if bias else None
+    o = torch.empty(L, Hq, d, device=dev)
+    lse = torch.empty(L, Hq, device=dev)
+    B().kvc_decode_attn(q, K, V, lr, 0.7, 1 / math.sqrt(d), o, lse)
+    torch.cuda.synchronize()
+    for l in range(L):
+        ro, rl = infokv.decode_attention(host_f64(q[l]), host_f64(K[l]), host_f64(V[l]),
+                                         host_f64(lr[l]) if bias else None, 0.7 if bias else 0.0)
+        assert np.max(np.abs(o[l].cpu().numpy() - ro)) <= 1e-3
+        assert_rel(lse[l].cpu().numpy(), rl, 1e-4, what="lse")
