@@ -24,6 +24,8 @@ ARCH = "gfx950"
 
 FLAGS = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         # MFMA results straight into VGPRs (gfx950 allows it): no accvgpr moves
+         "-mllvm", "-amdgpu-mfma-vgpr-form",
          "-I", os.path.join(ROOT, "include"), "-Wall", "-Wno-unused-function"]
 
 

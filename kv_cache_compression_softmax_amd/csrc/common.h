@@ -6,7 +6,7 @@
 
 #include <string>
 
-#include "../../include/kvc.h"
+#include "kvc.h"
 
 namespace kvc {
 
@@ -145,15 +145,6 @@ __device__ __forceinline__ uint32_t bf16_key(uint32_t b) {   // b: 16-bit patter
 __device__ __forceinline__ float key_bf16(uint32_t k) {
   uint32_t b = (k & 0x8000u) ? (k & 0x7fffu) : (~k & 0xffffu);
   return __uint_as_float(b << 16);
-}
-
-// Agent-scope (whole GPU, all XCDs) ticket counter used by "last block finishes"
-// combines: release before, acquire after.
-__device__ __forceinline__ unsigned ticket_add(unsigned* ctr) {
-  __threadfence();
-  unsigned t = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-  __threadfence();
-  return t;
 }
 
 }  // namespace kvc

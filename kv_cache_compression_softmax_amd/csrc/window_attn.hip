@@ -10,20 +10,24 @@
 // padded to a multiple of 32 so that every 32-row "tile" belongs to one head.
 //
 // A needs each row's softmax normaliser before any column can be summed, so the
-// bf16 path runs two passes over K (the second usually hits the 256 MB MALL when
-// the layer chunk is small):
+// bf16 path makes two passes over K:
 //   pass 1  per 32-key block, S^T = K * Q^T on MFMA (keys on M, queries on N);
-//           each lane keeps an online (max, sum) of exp2 for one query row;
-//           one partial per (wave task, row) goes to the workspace;
-//   combine fixed-order merge of the partials into c_r = log2 of the row's
-//           normaliser (max + log2 sum);
+//           each lane keeps an online (max, sum of exp2) for one query row.  The
+//           four waves of a workgroup merge in LDS and write one partial;
+//           Each pass-2 workgroup merges its (layer, KV head)'s partials in index
+//           order into c_r = max + log2(sum), +inf for padding rows;
 //   pass 2  S = Q * K^T on MFMA (queries on M, keys on N): each lane owns one key
 //           column, so exp2(s - c_r) summed over the lane's 16 rows plus its
-//           partner lane gives the column sum with no atomics.
-// Both passes read every key row as 16-byte vectors straight into MFMA operand
-// registers: lane (row i, half hf) holds d/2 contiguous elements, and the
-// contraction index k of step s maps to element hf*d/2 + 8s + e, the same map
-// for Q and K (the contraction does not depend on the order of k).
+//           partner lane is the column sum, with no atomics.
+// Launch i runs pass 2 of layer chunk i-1 next to pass 1 of chunk i, so a chunk's
+// keys are read again one chunk later, while they are still in the 256 MB MALL.
+// Key rows go straight from HBM into MFMA operand registers (16 bytes per lane:
+// lane (row i, half hf) holds d/2 contiguous elements and step s of the
+// contraction uses elements hf*d/2 + 8s .. +8, the same map for Q and K, which
+// the contraction does not depend on).  Q is staged once per workgroup in LDS in
+// fragment order, one conflict-free ds_read_b128 per fragment.
+#include <type_traits>
+
 #include "common.h"
 
 namespace kvc {
@@ -32,39 +36,42 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int NTW = 256;        // threads per workgroup (4 waves, one task each)
+constexpr int NTW = 256;        // threads per workgroup (4 waves)
 constexpr int MAX_TILES = 8;    // G * ceil(w/32)
-constexpr int MAX_TG = 4;       // tiles held in registers per launch
-constexpr int KPW = 512;        // keys per wave task (multiple of 32)
+constexpr int MAX_TG = 4;       // tiles per launch
+constexpr int KPW = 256;        // keys per wave
+#ifndef KVC_WIN_CHAINS
+#define KVC_WIN_CHAINS 1
+#endif
+constexpr int CH = KVC_WIN_CHAINS;  // tiles whose MFMA chains are issued interleaved
+#ifndef KVC_WIN_PF
+#define KVC_WIN_PF 1
+#endif
+constexpr int PF = KVC_WIN_PF;      // key blocks loaded ahead of the one being computed
+constexpr int MIN_WAVES = 4096; // waves per launch that fill 256 CUs
 constexpr float LOG2E = 1.4426950408889634f;
 
 struct Geo {
-  int Hq, Hkv, G, w, d, tph, ntiles;   // tiles per head, tiles per group
+  int Hq, Hkv, G, w, d, tph, ntiles;   // tiles per head, tiles per KV group
   int64_t n;
-  int nb;                              // wave tasks per (layer, KV head)
+  int nwg;                             // workgroups per (layer, KV head)
 };
 
-__device__ __forceinline__ int tile_row_pos(const Geo& g, int tile, int i) {
-  // window position of row i of a tile, or -1 for a padding row
-  const int rr = (tile % g.tph) * 32 + i;
-  return rr < g.w ? (int)(g.n - g.w) + rr : -1;
-}
+struct Span { int l0, nl, pass; };     // layers [l0, l0 + nl) of the table, pass 1 or 2
 
-template <int D>
-__device__ __forceinline__ void load_q(const uint16_t* q, const Geo& g, int kvh, int tile, int lane,
-                                       bf16x8 (&qf)[D / 16]) {
-  const int i = lane & 31, hf = lane >> 5;
-  const int head = kvh * g.G + tile / g.tph;
-  const int rr = (tile % g.tph) * 32 + i;
-  if (rr < g.w) {
-    const uint16_t* p = q + ((int64_t)head * g.w + rr) * D + hf * (D / 2);
-#pragma unroll
-    for (int s = 0; s < D / 16; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(p + 8 * s);
-  } else {
-#pragma unroll
-    for (int s = 0; s < D / 16; ++s) qf[s] = bf16x8{};
-  }
-}
+struct WinArgs {
+  ConstPtrs q, k;                      // per-layer pointers of the current layer group
+  Geo g;
+  int tile0;                           // first query tile of this launch
+  float sl2;                           // scale * log2(e)
+  int per_head;
+  float2* part;                        // [32, Hkv, nwg, rows] pass-1 partials
+  float* A;                            // output of the layer group
+  int nspan;
+  Span span[2];
+  int64_t blocks0;                     // tasks of span 0
+  int64_t ntask;                       // tasks of all spans
+};
 
 template <int D>
 __device__ __forceinline__ void load_k(const uint16_t* k, const Geo& g, int kvh, int64_t j0, int lane,
@@ -84,161 +91,287 @@ __device__ __forceinline__ void load_k(const uint16_t* k, const Geo& g, int kvh,
 // row (M index) of accumulator element v held by a lane of half hf
 __device__ __forceinline__ int acc_row(int v, int hf) { return 8 * (v >> 2) + 4 * hf + (v & 3); }
 
-// ---------------------------------------------------------------- pass 1
-template <int D, int TG>
-__global__ void __launch_bounds__(NTW)
-win_pass1(ConstPtrs qs, ConstPtrs ks, Geo g, int tile0, int lc, float scale_log2,
-          float2* __restrict__ part) {
-  const int lane = threadIdx.x & 63, hf = lane >> 5, qi = lane & 31;
-  const int64_t task = (int64_t)blockIdx.x * (NTW / 64) + threadIdx.x / 64;
-  const int64_t ntask = (int64_t)lc * g.Hkv * g.nb;
-  if (task >= ntask) return;
-  const int b = (int)(task % g.nb);
-  const int kvh = (int)((task / g.nb) % g.Hkv);
-  const int l = (int)(task / ((int64_t)g.nb * g.Hkv));
-  const uint16_t* q = (const uint16_t*)qs.p[l];
-  const uint16_t* k = (const uint16_t*)ks.p[l];
+__device__ __forceinline__ bf16x8 as_bf16x8(const uint4& u) {
+  bf16x8 r;
+  __builtin_memcpy(&r, &u, 16);
+  return r;
+}
 
-  bf16x8 qf[TG][D / 16];
-  int pos[TG];
+// Streams the 32-key blocks of [jb, je) through PF + 1 rotating register sets:
+// block j's keys are requested PF blocks before `block` runs on them.
+template <int D, typename F>
+__device__ __forceinline__ void stream_blocks(const uint16_t* k, const Geo& g, int kvh, int64_t jb,
+                                              int64_t je, int lane, F&& block) {
+  constexpr int S = D / 16, NB = PF + 1;
+  bf16x8 kb[NB][S];
 #pragma unroll
-  for (int t = 0; t < TG; ++t) {
-    load_q<D>(q, g, kvh, tile0 + t, lane, qf[t]);
-    pos[t] = tile_row_pos(g, tile0 + t, qi);
-  }
-  float m[TG], s[TG];
-#pragma unroll
-  for (int t = 0; t < TG; ++t) { m[t] = -INFINITY; s[t] = 0.f; }
-
-  const int64_t jb = (int64_t)b * KPW;
-  const int64_t je = min(g.n, jb + KPW);
-  bf16x8 kf[D / 16], kn[D / 16];
-  load_k<D>(k, g, kvh, jb, lane, kf);
+  for (int p = 0; p < PF; ++p)
+    if (jb + 32 * p < je) load_k<D>(k, g, kvh, jb + 32 * p, lane, kb[p]);
 #pragma unroll 1
-  for (int64_t j0 = jb; j0 < je; j0 += 32) {
-    if (j0 + 32 < je) load_k<D>(k, g, kvh, j0 + 32, lane, kn);
+  for (int64_t j0 = jb; j0 < je; j0 += 32 * NB) {
 #pragma unroll
-    for (int t = 0; t < TG; ++t) {
-      f32x16 acc = {};
-#pragma unroll
-      for (int st = 0; st < D / 16; ++st)
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[st], qf[t][st], acc, 0, 0, 0);
-      float x[16];
-      float bm = -INFINITY;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int64_t key = j0 + acc_row(v, hf);
-        x[v] = (key <= pos[t] && key < g.n) ? acc[v] * scale_log2 : -INFINITY;
-        bm = fmaxf(bm, x[v]);
-      }
-      if (bm > -INFINITY) {
-        const float mn = fmaxf(m[t], bm);
-        float sum = 0.f;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) sum += exp2f(x[v] - mn);
-        s[t] = s[t] * exp2f(m[t] - mn) + sum;
-        m[t] = mn;
-      }
-    }
-#pragma unroll
-    for (int st = 0; st < D / 16; ++st) kf[st] = kn[st];
-  }
-  // merge the two halves (lanes i and i+32 hold the same query row)
-#pragma unroll
-  for (int t = 0; t < TG; ++t) {
-    const float mo = __shfl_xor(m[t], 32, 64), so = __shfl_xor(s[t], 32, 64);
-    const float M = fmaxf(m[t], mo);
-    float S = 0.f;
-    if (M > -INFINITY) S = s[t] * exp2f(m[t] - M) + so * exp2f(mo - M);
-    if (hf == 0) {
-      const int64_t row = (int64_t)(tile0 + t) * 32 + qi;
-      part[(((int64_t)l * g.Hkv + kvh) * g.nb + b) * (g.ntiles * 32) + row] = make_float2(M, S);
+    for (int r = 0; r < NB; ++r) {
+      const int64_t jj = j0 + 32 * r;
+      if (jj >= je) break;
+      if (jj + 32 * PF < je) load_k<D>(k, g, kvh, jj + 32 * PF, lane, kb[(r + PF) % NB]);
+      block(kb[r], jj);
     }
   }
 }
 
-// ---------------------------------------------------------------- combine
-// c[l, g, row] = log2 of the row's softmax normaliser in exp2 units (+inf for a
-// row with no visible key, i.e. a padding row).  Fixed order over the tasks.
-__global__ void __launch_bounds__(256)
-win_combine(const float2* __restrict__ part, int nb, int rows, int64_t ngroups, float* __restrict__ c) {
-  const int64_t gi = blockIdx.x;              // (layer, KV head)
-  if (gi >= ngroups) return;
-  for (int r = threadIdx.x; r < rows; r += blockDim.x) {
-    const float2* p = part + gi * nb * rows + r;
-    float M = -INFINITY;
-    for (int b = 0; b < nb; ++b) M = fmaxf(M, p[(int64_t)b * rows].x);
-    float out = INFINITY;
-    if (M > -INFINITY) {
-      float S = 0.f;
-      for (int b = 0; b < nb; ++b) {
-        const float2 v = p[(int64_t)b * rows];
-        if (v.x > -INFINITY) S += v.y * exp2f(v.x - M);
+// Q rows of TG tiles into LDS in fragment order: entry (t, s, lane) holds the 16
+// bytes lane `lane` feeds to step s of tile t.  Global reads are row-contiguous.
+template <int D, int TG>
+__device__ __forceinline__ void stage_q(const uint16_t* q, const Geo& g, int kvh, int tile0, uint4* qlds) {
+  constexpr int S = D / 16, C = D / 8;          // steps, 16-byte chunks per row
+  for (int f = threadIdx.x; f < TG * 32 * C; f += NTW) {
+    const int c16 = f % C, i = (f / C) % 32, t = f / (32 * C);
+    const int hf = c16 / S, st = c16 % S;
+    const int tile = tile0 + t;
+    const int head = kvh * g.G + tile / g.tph;
+    const int rr = (tile % g.tph) * 32 + i;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (rr < g.w) v = *reinterpret_cast<const uint4*>(q + ((int64_t)head * g.w + rr) * D + c16 * 8);
+    qlds[(t * S + st) * 64 + hf * 32 + i] = v;
+  }
+}
+
+template <int D, int TG>
+struct WinSmem {
+  uint4 q[TG * (D / 16) * 64];
+  union {
+    float2 wst[NTW / 64][TG * 32];                 // pass 1: per-wave row stats
+    struct {
+      __attribute__((aligned(16))) float c[TG * 32]; // pass 2: row normalisers
+      float2 red[NTW];                             // pass 2: partial merges
+    };
+  };
+};
+
+// ---------------------------------------------------------------- pass 1
+template <int D, int TG>
+__device__ __forceinline__ void pass1(const WinArgs& a, WinSmem<D, TG>& sm, int l, int kvh, int wgi) {
+  constexpr int S = D / 16;
+  const Geo& g = a.g;
+  const int lane = threadIdx.x & 63, hf = lane >> 5, qi = lane & 31, wv = threadIdx.x / 64;
+  const int64_t lg = (int64_t)l * g.Hkv + kvh;
+  const uint16_t* k = (const uint16_t*)a.k.p[l];
+  stage_q<D, TG>((const uint16_t*)a.q.p[l], g, kvh, a.tile0, sm.q);
+  __syncthreads();
+
+  int pos[TG];                                   // window position of this lane's row
+#pragma unroll
+  for (int t = 0; t < TG; ++t) {
+    const int rr = ((a.tile0 + t) % g.tph) * 32 + qi;
+    pos[t] = rr < g.w ? (int)(g.n - g.w) + rr : -1;
+  }
+  float m[TG], sm_[TG];
+#pragma unroll
+  for (int t = 0; t < TG; ++t) { m[t] = -INFINITY; sm_[t] = 0.f; }
+
+  const int64_t jb = ((int64_t)wgi * (NTW / 64) + wv) * KPW;
+  const int64_t je = min(g.n, jb + KPW);
+  const int64_t safe_end = g.n - g.w;            // keys <= this are seen by every row
+  // one 32-key block; kc holds its key fragments
+  // FULL: every key of the block is visible to every row (no mask code at all)
+  auto block_t = [&](const bf16x8 (&kc)[S], int64_t j0, auto full_t) {
+    constexpr bool full = decltype(full_t)::value;
+    int qo = lane;
+    asm volatile("" : "+v"(qo));                 // keep the Q reads in the loop (LDS, not VGPRs)
+#pragma unroll
+    for (int t0 = 0; t0 < TG; t0 += CH) {
+      // CH independent MFMA chains issued interleaved, then their epilogues
+      f32x16 accs[CH];
+#pragma unroll
+      for (int c = 0; c < CH; ++c) accs[c] = f32x16{};
+      // all fragment reads first, then the MFMAs: each MFMA waits only for its own
+      // read (staggered lgkmcnt) instead of a full LDS round trip per step
+      bf16x8 qf[CH][S];
+#pragma unroll
+      for (int c = 0; c < CH; ++c)
+#pragma unroll
+        for (int st = 0; st < S; ++st)
+          if (t0 + c < TG) qf[c][st] = as_bf16x8(sm.q[((t0 + c) * S + st) * 64 + qo]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int st = 0; st < S; ++st)
+#pragma unroll
+        for (int c = 0; c < CH; ++c)
+          if (t0 + c < TG)
+            accs[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kc[st], qf[c][st], accs[c], 0, 0, 0);
+#pragma unroll
+      for (int c = 0; c < CH; ++c) {
+      const int t = t0 + c;
+      if (t >= TG) break;
+      f32x16& acc = accs[c];
+      // scores in log2 units are acc * sl2 (sl2 > 0): take the block max on the raw
+      // accumulator, then one FMA and one v_exp_f32 per element (results below
+      // 2^-126 flush to zero, which changes no sum at float32 precision)
+      float bm = -INFINITY;
+      if constexpr (full) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) bm = fmaxf(bm, acc[v]);
+      } else {
+        const int64_t lim = min((int64_t)pos[t], g.n - 1) - j0 - 4 * hf;   // key offset limit
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int off = 8 * (v >> 2) + (v & 3);
+          acc[v] = (off <= lim) ? acc[v] : -INFINITY;
+          bm = fmaxf(bm, acc[v]);
+        }
       }
-      out = M + log2f(S);
+      if (full || bm > -INFINITY) {
+        const float mn = fmaxf(m[t], bm * a.sl2);
+        float sum = 0.f;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) sum += __builtin_amdgcn_exp2f(fmaf(acc[v], a.sl2, -mn));
+        sm_[t] = sm_[t] * __builtin_amdgcn_exp2f(m[t] - mn) + sum;
+        m[t] = mn;
+      }
+      }
     }
-    c[gi * rows + r] = out;
+  };
+  auto block = [&](const bf16x8 (&kc)[S], int64_t j0) {
+    if (j0 + 31 <= safe_end) block_t(kc, j0, std::true_type{});   // wave-uniform branch
+    else block_t(kc, j0, std::false_type{});
+  };
+  stream_blocks<D>(k, g, kvh, jb, je, lane, block);
+  // halves (lanes i, i+32 share a query row), then the 4 waves, in fixed order
+#pragma unroll
+  for (int t = 0; t < TG; ++t) {
+    const float mo = __shfl_xor(m[t], 32, 64), so = __shfl_xor(sm_[t], 32, 64);
+    const float M = fmaxf(m[t], mo);
+    float Sx = 0.f;
+    if (M > -INFINITY) Sx = sm_[t] * exp2f(m[t] - M) + so * exp2f(mo - M);
+    if (hf == 0) sm.wst[wv][t * 32 + qi] = make_float2(M, Sx);
+  }
+  __syncthreads();
+  const int rows = g.ntiles * 32;
+  float2* pl = a.part + lg * (int64_t)g.nwg * rows;
+  for (int r = threadIdx.x; r < TG * 32; r += NTW) {
+    float M = -INFINITY;
+#pragma unroll
+    for (int w2 = 0; w2 < NTW / 64; ++w2) M = fmaxf(M, sm.wst[w2][r].x);
+    float Sx = 0.f;
+    if (M > -INFINITY) {
+#pragma unroll
+      for (int w2 = 0; w2 < NTW / 64; ++w2)
+        if (sm.wst[w2][r].x > -INFINITY) Sx += sm.wst[w2][r].y * exp2f(sm.wst[w2][r].x - M);
+    }
+    pl[(int64_t)wgi * rows + a.tile0 * 32 + r] = make_float2(M, Sx);
   }
 }
 
 // ---------------------------------------------------------------- pass 2
 template <int D, int TG>
-__global__ void __launch_bounds__(NTW)
-win_pass2(ConstPtrs qs, ConstPtrs ks, Geo g, int tile0, int lc, float scale_log2,
-          const float* __restrict__ cfin, int per_head, float* __restrict__ A) {
-  __shared__ float csh[NTW / 64][MAX_TG * 32];
+__device__ __forceinline__ void pass2(const WinArgs& a, WinSmem<D, TG>& sm, int l, int kvh, int wgi) {
+  constexpr int S = D / 16;
+  const Geo& g = a.g;
   const int lane = threadIdx.x & 63, hf = lane >> 5, qi = lane & 31, wv = threadIdx.x / 64;
-  const int64_t ntask = (int64_t)lc * g.Hkv * g.nb;
-  const int64_t task0 = (int64_t)blockIdx.x * (NTW / 64) + wv;
-  const bool active = task0 < ntask;
-  const int64_t task = active ? task0 : 0;
-  const int b = (int)(task % g.nb);
-  const int kvh = (int)((task / g.nb) % g.Hkv);
-  const int l = (int)(task / ((int64_t)g.nb * g.Hkv));
-  const uint16_t* q = (const uint16_t*)qs.p[l];
-  const uint16_t* k = (const uint16_t*)ks.p[l];
+  const int64_t lg = (int64_t)l * g.Hkv + kvh;
+  const uint16_t* k = (const uint16_t*)a.k.p[l];
   const int rows = g.ntiles * 32;
-
-  // each wave stages the row normalisers of its (layer, KV head) tiles in LDS
-  const float* cg = cfin + ((int64_t)l * g.Hkv + kvh) * rows + tile0 * 32;
-  for (int r = lane; r < TG * 32; r += 64) csh[wv][r] = cg[r];
-  __syncthreads();                 // the only barrier; idle waves leave after it
-  if (!active) return;
-  bf16x8 qf[TG][D / 16];
+  stage_q<D, TG>((const uint16_t*)a.q.p[l], g, kvh, a.tile0, sm.q);
+  // row normalisers from pass 1's workgroup partials: P threads per row each merge
+  // every P-th partial (loads issued 8 at a time), then the P results are merged
+  // in a fixed order; +inf for padding rows and rows that see no key
+  {
+    constexpr int R = TG * 32, P = NTW / R;
+    const float2* pl = a.part + lg * (int64_t)g.nwg * rows + a.tile0 * 32;
+    const int r = threadIdx.x % R, j = threadIdx.x / R;
+    float M = -INFINITY, Sx = 0.f;
+    if (j < P) {
+      for (int bb = j; bb < g.nwg; bb += 8 * P) {
+        float2 v[8];
 #pragma unroll
-  for (int t = 0; t < TG; ++t) load_q<D>(q, g, kvh, tile0 + t, lane, qf[t]);
+        for (int u = 0; u < 8; ++u)
+          v[u] = (bb + u * P < g.nwg) ? pl[(int64_t)(bb + u * P) * rows + r] : make_float2(-INFINITY, 0.f);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          if (v[u].x > -INFINITY) {
+            const float mn = fmaxf(M, v[u].x);
+            Sx = Sx * exp2f(M - mn) + v[u].y * exp2f(v[u].x - mn);
+            M = mn;
+          }
+        }
+      }
+      sm.red[j * R + r] = make_float2(M, Sx);
+    }
+    __syncthreads();
+    if (threadIdx.x < R) {
+      float Mt = -INFINITY, St = 0.f;
+      for (int jj = 0; jj < P; ++jj) {
+        const float2 v = sm.red[jj * R + r];
+        if (v.x > -INFINITY) {
+          const float mn = fmaxf(Mt, v.x);
+          St = St * exp2f(Mt - mn) + v.y * exp2f(v.x - mn);
+          Mt = mn;
+        }
+      }
+      const int row = a.tile0 * 32 + r;
+      const bool pad = ((row >> 5) % g.tph) * 32 + (row & 31) >= g.w;
+      sm.c[r] = (!pad && Mt > -INFINITY) ? Mt + log2f(St) : INFINITY;
+    }
+  }
+  __syncthreads();
 
-  // head of each tile, and the window position of each of this lane's rows
-  const int64_t jb = (int64_t)b * KPW;
+  const int64_t jb = ((int64_t)wgi * (NTW / 64) + wv) * KPW;
   const int64_t je = min(g.n, jb + KPW);
+  const int64_t safe_end = g.n - g.w;
   const float inv_group = 1.0f / (float)(g.G * g.w), inv_w = 1.0f / (float)g.w;
-  bf16x8 kf[D / 16], kn[D / 16];
-  load_k<D>(k, g, kvh, jb, lane, kf);
-#pragma unroll 1
-  for (int64_t j0 = jb; j0 < je; j0 += 32) {
-    if (j0 + 32 < je) load_k<D>(k, g, kvh, j0 + 32, lane, kn);
-    const int64_t key = j0 + qi;               // this lane's key column
-    float total = 0.f;                         // group mode: over all tiles
-    float hsum = 0.f;                          // head mode: current head
+  float* A = a.A;
+  auto block_t = [&](const bf16x8 (&kc)[S], int64_t j0, auto full_t) {
+    constexpr bool full = decltype(full_t)::value;
+    const int64_t key = j0 + qi;                 // this lane's key column
+    float total = 0.f, hsum = 0.f;
+    int qo = lane, co = 4 * hf;
+    asm volatile("" : "+v"(qo), "+v"(co));       // keep Q and c reads in the loop
 #pragma unroll
-    for (int t = 0; t < TG; ++t) {
-      f32x16 acc = {};
+    for (int t0 = 0; t0 < TG; t0 += CH) {
+      f32x16 accs[CH];
 #pragma unroll
-      for (int st = 0; st < D / 16; ++st)
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[t][st], kf[st], acc, 0, 0, 0);
+      for (int c = 0; c < CH; ++c) accs[c] = f32x16{};
+      bf16x8 qf[CH][S];
+#pragma unroll
+      for (int c = 0; c < CH; ++c)
+#pragma unroll
+        for (int st = 0; st < S; ++st)
+          if (t0 + c < TG) qf[c][st] = as_bf16x8(sm.q[((t0 + c) * S + st) * 64 + qo]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int st = 0; st < S; ++st)
+#pragma unroll
+        for (int c = 0; c < CH; ++c)
+          if (t0 + c < TG)
+            accs[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[c][st], kc[st], accs[c], 0, 0, 0);
+#pragma unroll
+      for (int c = 0; c < CH; ++c) {
+      const int t = t0 + c;
+      if (t >= TG) break;
+      f32x16& acc = accs[c];
+      // window row of element v: base + (8*(v/4) + v%4); the key is seen by rows
+      // rr with key - (n - w) <= rr < w, and only if key < n
+      const int base = ((a.tile0 + t) % g.tph) * 32 + 4 * hf;
+      const int lo = (int)(key - safe_end) - base;
+      const int hi = (key < g.n) ? g.w - base : -1;
       float colsum = 0.f;
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int r = acc_row(v, hf);
-        const int p = tile_row_pos(g, tile0 + t, r);
-        const float e = exp2f(acc[v] * scale_log2 - csh[wv][t * 32 + r]);
-        colsum += (key <= p && key < g.n) ? e : 0.f;
+      for (int qd = 0; qd < 4; ++qd) {
+        const float4 c4 = *reinterpret_cast<const float4*>(&sm.c[t * 32 + 8 * qd + co]);
+        const float cc[4] = {c4.x, c4.y, c4.z, c4.w};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int v = 4 * qd + u, off = 8 * qd + u;
+          float e = __builtin_amdgcn_exp2f(fmaf(acc[v], a.sl2, -cc[u]));
+          if constexpr (!full) e = (off >= lo && off < hi) ? e : 0.f;
+          colsum += e;
+        }
       }
       colsum += __shfl_xor(colsum, 32, 64);
       total += colsum;
-      if (per_head) {
+      if (a.per_head) {
         hsum += colsum;
-        const int tile = tile0 + t;
+        const int tile = a.tile0 + t;
         const bool last_of_head = (t == TG - 1) || ((tile + 1) % g.tph == 0);
         if (last_of_head) {
           if (hf == 0 && key < g.n) {
@@ -250,15 +383,39 @@ win_pass2(ConstPtrs qs, ConstPtrs ks, Geo g, int tile0, int lc, float scale_log2
           hsum = 0.f;
         }
       }
+      }
     }
-    if (!per_head && hf == 0 && key < g.n) {
+    if (!a.per_head && hf == 0 && key < g.n) {
       float* dst = A + ((int64_t)l * g.Hkv + kvh) * g.n + key;
-      *dst = tile0 == 0 ? total * inv_group : *dst + total * inv_group;
+      *dst = a.tile0 == 0 ? total * inv_group : *dst + total * inv_group;
     }
-#pragma unroll
-    for (int st = 0; st < D / 16; ++st) kf[st] = kn[st];
+  };
+  auto block = [&](const bf16x8 (&kc)[S], int64_t j0) {
+    if (j0 + 31 <= safe_end) block_t(kc, j0, std::true_type{});   // wave-uniform branch
+    else block_t(kc, j0, std::false_type{});
+  };
+  stream_blocks<D>(k, g, kvh, jb, je, lane, block);
+}
+
+template <int D, int TG>
+__global__ void __launch_bounds__(NTW)
+win_kernel(WinArgs a) {
+  __shared__ WinSmem<D, TG> sm;
+  // persistent grid: as many workgroups as fit at once, each looping over tasks, so
+  // no launch ends with a sparsely occupied last round
+  for (int64_t b = blockIdx.x; b < a.ntask; b += gridDim.x) {
+    const int si = (a.nspan > 1 && b >= a.blocks0) ? 1 : 0;
+    const Span sp = a.span[si];
+    const int64_t local = si ? b - a.blocks0 : b;
+    const int64_t lgl = local / a.g.nwg;         // (layer in span, KV head)
+    const int wgi = (int)(local % a.g.nwg);
+    const int l = sp.l0 + (int)(lgl / a.g.Hkv), kvh = (int)(lgl % a.g.Hkv);
+    if (sp.pass == 1) pass1<D, TG>(a, sm, l, kvh, wgi);
+    else pass2<D, TG>(a, sm, l, kvh, wgi);
+    __syncthreads();                             // LDS is reused by the next task
   }
 }
+
 
 // ---------------------------------------------------------------- float32 path
 // Plain vector-ALU version for float32 inputs (small shapes).  Rows are indexed
@@ -329,51 +486,73 @@ win_f32_accum(ConstPtrs qs, ConstPtrs ks, Geo g, float scale_log2, const float* 
 struct Plan {
   Geo g;
   bool mfma;
+  int lch;                      // layers per chunk
   size_t part_bytes, c_bytes;
 };
 
-int make_plan(int L, int Hq, int Hkv, int64_t n, int w, int d, int dtype, Plan* P) {
+void make_plan(int L, int Hq, int Hkv, int64_t n, int w, int d, int dtype, Plan* P) {
   Geo g{};
   g.Hq = Hq; g.Hkv = Hkv; g.G = Hq / Hkv; g.w = w; g.d = d; g.n = n;
   g.tph = (w + 31) / 32;
   g.ntiles = g.G * g.tph;
-  g.nb = (int)((n + KPW - 1) / KPW);
-  const int lc = L < kLayersPerLaunch ? L : kLayersPerLaunch;
+  g.nwg = (int)((n + 4LL * KPW - 1) / (4LL * KPW));
   P->g = g;
   P->mfma = (dtype == KVC_BF16);
+  const int lg_max = L < kLayersPerLaunch ? L : kLayersPerLaunch;
+  // chunk: enough layers that a launch (two chunks) has MIN_WAVES waves
+  const int64_t waves_per_layer = (int64_t)Hkv * ((n + KPW - 1) / KPW);
+  int64_t lch = (MIN_WAVES + 2 * waves_per_layer - 1) / (2 * waves_per_layer);
+  lch = lch < 1 ? 1 : (lch > lg_max ? lg_max : lch);
+  P->lch = (int)lch;
   if (P->mfma) {
-    P->part_bytes = (size_t)lc * Hkv * g.nb * g.ntiles * 32 * sizeof(float2);
-    P->c_bytes = (size_t)lc * Hkv * g.ntiles * 32 * sizeof(float);
+    P->part_bytes = (size_t)lg_max * Hkv * g.nwg * g.ntiles * 32 * sizeof(float2);
+    P->c_bytes = 0;
   } else {
     P->part_bytes = 0;
-    P->c_bytes = (size_t)lc * Hkv * g.G * w * sizeof(float);
+    P->c_bytes = (size_t)lg_max * Hkv * g.G * w * sizeof(float);
   }
-  return KVC_OK;
+}
+
+// Workgroups of `kern` resident at once on the current device.
+int resident_blocks(const void* kern) {
+  int dev = 0, ncu = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, NTW, 0) != hipSuccess)
+    return 1024;
+  return (ncu > 0 ? ncu : 1) * (per_cu > 0 ? per_cu : 1);
 }
 
 template <int D, int TG>
-void launch_tiles(const ConstPtrs& qt, const ConstPtrs& kt, const Geo& g, int tile0, int lc,
-                  float sl2, float2* part, float* cfin, int per_head, float* A, hipStream_t s,
-                  bool stats) {
-  const int64_t ntask = (int64_t)lc * g.Hkv * g.nb;
-  const unsigned grid = (unsigned)((ntask + 3) / 4);
-  if (stats)
-    hipLaunchKernelGGL((win_pass1<D, TG>), dim3(grid), dim3(NTW), 0, s, qt, kt, g, tile0, lc, sl2, part);
-  else
-    hipLaunchKernelGGL((win_pass2<D, TG>), dim3(grid), dim3(NTW), 0, s, qt, kt, g, tile0, lc, sl2,
-                       (const float*)cfin, per_head, A);
+void launch_win_tg(WinArgs a, hipStream_t s) {
+  const void* kern = reinterpret_cast<const void*>(&win_kernel<D, TG>);
+  const int64_t res = resident_blocks(kern);
+  const dim3 grid((unsigned)(a.ntask < res ? a.ntask : res)), block(NTW);
+  hipLaunchKernelGGL((win_kernel<D, TG>), grid, block, 0, s, a);
 }
 
 template <int D>
-void launch_group(int tg, const ConstPtrs& qt, const ConstPtrs& kt, const Geo& g, int tile0, int lc,
-                  float sl2, float2* part, float* cfin, int per_head, float* A, hipStream_t s,
-                  bool stats) {
+void launch_win(int tg, WinArgs a, hipStream_t s) {
+  a.ntask = 0;
+  for (int i = 0; i < a.nspan; ++i) a.ntask += (int64_t)a.span[i].nl * a.g.Hkv * a.g.nwg;
   switch (tg) {
-    case 1: launch_tiles<D, 1>(qt, kt, g, tile0, lc, sl2, part, cfin, per_head, A, s, stats); break;
-    case 2: launch_tiles<D, 2>(qt, kt, g, tile0, lc, sl2, part, cfin, per_head, A, s, stats); break;
-    case 3: launch_tiles<D, 3>(qt, kt, g, tile0, lc, sl2, part, cfin, per_head, A, s, stats); break;
-    default: launch_tiles<D, 4>(qt, kt, g, tile0, lc, sl2, part, cfin, per_head, A, s, stats); break;
+    case 1: launch_win_tg<D, 1>(a, s); break;
+    case 2: launch_win_tg<D, 2>(a, s); break;
+    case 3: launch_win_tg<D, 3>(a, s); break;
+    default: launch_win_tg<D, 4>(a, s); break;
   }
+}
+
+// One launch: up to two spans (pass 2 of one chunk, pass 1 of the next).
+void launch_spans(const WinArgs& base, int tile0, int tg, int nspan, const Span* sp, hipStream_t s) {
+  WinArgs a = base;
+  a.tile0 = tile0;
+  a.nspan = nspan;
+  a.span[0] = sp[0];
+  a.span[1] = nspan > 1 ? sp[1] : sp[0];
+  a.blocks0 = (int64_t)sp[0].nl * a.g.Hkv * a.g.nwg;
+  if (a.g.d == 64) launch_win<64>(tg, a, s);
+  else launch_win<128>(tg, a, s);
 }
 
 }  // namespace
@@ -412,16 +591,16 @@ extern "C" int kvc_score_window_attn(const void* const* q_win, const void* const
     for (int l = 0; l < L; ++l)
       KVC_REQUIRE((uintptr_t)q_win[l] % 16 == 0 && (uintptr_t)k[l] % 16 == 0,
                   "kvc_score_window_attn: bf16 tensors must be 16-byte aligned");
+    KVC_REQUIRE((int64_t)2 * kLayersPerLaunch * Hkv * g.nwg <= 0x7fffffffLL,
+                "kvc_score_window_attn: grid too large");
   } else {
     KVC_REQUIRE(d >= 1 && d <= 256, "kvc_score_window_attn: float32 needs d <= 256");
     KVC_REQUIRE((int64_t)g.G * w * d * 4 <= 64 * 1024,
                 "kvc_score_window_attn: float32 path needs (Hq/Hkv)*w*d*4 <= 64 KB");
   }
   const size_t need = P.part_bytes + P.c_bytes;
-  if (!ws || ws_bytes < need)
-    return KVC_FAIL(KVC_ERR_WORKSPACE, "kvc_score_window_attn: workspace needs %zu bytes", need);
-  char* base = (char*)(((uintptr_t)ws + 255) & ~(uintptr_t)255);
-  if ((size_t)(base - (char*)ws) + need > ws_bytes)
+  char* base = ws ? (char*)(((uintptr_t)ws + 255) & ~(uintptr_t)255) : nullptr;
+  if (!ws || (size_t)(base - (char*)ws) + need > ws_bytes)
     return KVC_FAIL(KVC_ERR_WORKSPACE, "kvc_score_window_attn: workspace needs %zu bytes", need + 256);
   float2* part = (float2*)base;
   float* cfin = (float*)(base + P.part_bytes);
@@ -429,24 +608,32 @@ extern "C" int kvc_score_window_attn(const void* const* q_win, const void* const
   const float sl2 = scale * LOG2E;
   const int Aheads = per_query_head ? Hq : Hkv;
 
-  for (int l0 = 0; l0 < L; l0 += kLayersPerLaunch) {
+  for (int l0 = 0; l0 < L; l0 += kLayersPerLaunch) {        // layer groups of at most 32
     const int lc = min(kLayersPerLaunch, L - l0);
     ConstPtrs qt{}, kt{};
     for (int i = 0; i < lc; ++i) { qt.p[i] = q_win[l0 + i]; kt.p[i] = k[l0 + i]; }
     float* A = A_out + (int64_t)l0 * Aheads * n;
     if (P.mfma) {
-      const int64_t ngroups = (int64_t)lc * Hkv;
-      for (int t0 = 0; t0 < g.ntiles; t0 += MAX_TG) {
-        const int tg = min(MAX_TG, g.ntiles - t0);
-        if (d == 64) launch_group<64>(tg, qt, kt, g, t0, lc, sl2, part, cfin, per_query_head, A, s, true);
-        else launch_group<128>(tg, qt, kt, g, t0, lc, sl2, part, cfin, per_query_head, A, s, true);
-      }
-      hipLaunchKernelGGL(win_combine, dim3((unsigned)ngroups), dim3(256), 0, s, (const float2*)part,
-                         g.nb, g.ntiles * 32, ngroups, cfin);
-      for (int t0 = 0; t0 < g.ntiles; t0 += MAX_TG) {
-        const int tg = min(MAX_TG, g.ntiles - t0);
-        if (d == 64) launch_group<64>(tg, qt, kt, g, t0, lc, sl2, part, cfin, per_query_head, A, s, false);
-        else launch_group<128>(tg, qt, kt, g, t0, lc, sl2, part, cfin, per_query_head, A, s, false);
+      WinArgs a{};
+      a.q = qt; a.k = kt; a.g = g; a.sl2 = sl2; a.per_head = per_query_head;
+      a.part = part; a.A = A;
+      const int nch = (lc + P.lch - 1) / P.lch;
+      if (g.ntiles <= MAX_TG) {
+        // launch i: pass 2 of chunk i-1 beside pass 1 of chunk i
+        for (int i = 0; i <= nch; ++i) {
+          Span sp[2];
+          int ns = 0;
+          if (i >= 1) sp[ns++] = Span{(i - 1) * P.lch, min(P.lch, lc - (i - 1) * P.lch), 2};
+          if (i < nch) sp[ns++] = Span{i * P.lch, min(P.lch, lc - i * P.lch), 1};
+          launch_spans(a, 0, g.ntiles, ns, sp, s);
+        }
+      } else {
+        for (int c = 0; c < nch; ++c) {
+          const Span s1{c * P.lch, min(P.lch, lc - c * P.lch), 1};
+          const Span s2{s1.l0, s1.nl, 2};
+          for (int t0 = 0; t0 < g.ntiles; t0 += MAX_TG) launch_spans(a, t0, min(MAX_TG, g.ntiles - t0), 1, &s1, s);
+          for (int t0 = 0; t0 < g.ntiles; t0 += MAX_TG) launch_spans(a, t0, min(MAX_TG, g.ntiles - t0), 1, &s2, s);
+        }
       }
     } else {
       const int R = g.G * w;
