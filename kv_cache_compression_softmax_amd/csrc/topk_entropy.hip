@@ -4,216 +4,369 @@
 // entropy of the model's next-token distribution is taken over its k most likely
 // tokens only, renormalised over them.
 //
-// One workgroup streams one row from HBM exactly once.  Instead of holding the
-// 256 KB row on chip, it keeps a small candidate set in LDS:
-//   * after the first chunk it knows tau = the k-th largest key seen so far;
-//   * every later element is compared with tau and only strictly larger ones are
-//     appended (an element equal to tau can never add to the top-k multiset:
-//     enough copies of tau are already held);
-//   * when the candidate set grows past RESEL, an exact radix select over the
-//     candidates (8-bit digits of the order-preserving key) recomputes tau and
-//     shrinks the set back to exactly k (all keys > tau, then copies of tau).
-// Any element of the final top-k is >= every intermediate tau, so nothing it
-// needs is ever dropped.  For random rows the filter passes a few hundred
-// elements per row, so the kernel runs at the speed of the row stream.
-// Appends use an ordered block scan (no atomics decide positions), so the
-// candidate order, and with it every float sum, is deterministic.
+// One wave streams one row from HBM exactly once (16-byte lanes, the next step's
+// loads in flight while the current one is filtered) and never waits for another
+// wave.  Instead of holding the 256 KB row on chip it keeps a candidate list in its
+// own slice of LDS.  All comparisons are in the order of the order-preserving
+// integer keys (bit patterns), so they are exact and free of float rounding.
+//   * tau is the k-th largest key among the elements seen so far.
+//   * Filter: a lane appends its whole 16-byte vector (8 bf16 or 4 float32) when
+//     any element's key exceeds tau.  For tau >= +0 that test is a signed max of
+//     the raw bit patterns (packed 16-bit for bf16: half an instruction per
+//     element); for tau < 0 it is "some element is >= +0, or the unsigned min of
+//     the bit patterns is below tau's".  At k ~ 0.2% of the row about one vector
+//     in a hundred is appended, so the test, not the appending, sets the pace.
+//   * Re-select, when the list passes RESEL: an ordered compaction keeps the keys
+//     >= tau (the other elements of appended vectors are dropped here), an exact
+//     radix select (8-bit digits, LDS histogram) finds the new tau, and a second
+//     compaction rewrites the list as the keys > tau followed by copies of tau,
+//     padded to a whole vector with the smallest key.
+// The list always holds, besides real elements of the row and padding of the
+// smallest key, exactly the top-k multiset of what was seen: an element that is
+// not > the current tau never enters the final top-k beyond the copies of tau
+// already held, so the final list equals the row's top-k multiset.  Appends and
+// compactions are ordered by lane and element index (ballots and prefix sums; no
+// atomic decides a position), so the float sums below are deterministic.
+// Entropy is float32 over the k survivors, summing -p ln p term by term.
 #include "common.h"
 
 namespace kvc {
 namespace {
 
-constexpr int NT = 256;      // threads per workgroup
-constexpr int NV = 2;        // 16-byte vectors per thread per chunk
-constexpr int CAP = 8192;    // candidate capacity (keys)
-constexpr int RESEL = 2048;  // re-select once more candidates than this are held
+constexpr int NT = 256;      // 4 waves = 4 rows per workgroup
+constexpr int NV = 4;        // 16-byte vectors per lane per step
+constexpr int RESEL = 2048;  // list length that triggers a re-select (>= k rounded up)
+
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
 template <typename T> struct Tr;
 template <> struct Tr<uint16_t> {                 // bf16 bit patterns
-  using Key = uint16_t;
+  using Raw = uint16_t;
   static constexpr int VEC = 8;
   static constexpr int DIGITS = 2;
-  __device__ static Key key(uint16_t raw) { return (Key)bf16_key(raw); }
-  __device__ static float value(Key k) { return key_bf16(k); }
+  static constexpr Raw kMin = 0xffffu;            // bit pattern of the smallest key (0)
+  __device__ static uint32_t key(Raw r) { return bf16_key(r); }
+  __device__ static float value(uint32_t k) { return key_bf16(k); }
+  __device__ static Raw raw(uint32_t k) {         // canonical bit pattern of a key
+    return (k & 0x8000u) ? (Raw)(k & 0x7fffu) : (Raw)(~k & 0xffffu);
+  }
+  // some element's key > key(t), t = raw(tau): for t with a clear sign bit a
+  // signed max of the bit patterns, else "some element >= +0 or the unsigned min
+  // of the bit patterns below t"
+  __device__ static bool above_pos(const uint4& u, Raw t) {
+    const s16x2 a = __builtin_bit_cast(s16x2, u.x), b = __builtin_bit_cast(s16x2, u.y);
+    const s16x2 c = __builtin_bit_cast(s16x2, u.z), d = __builtin_bit_cast(s16x2, u.w);
+    const s16x2 m = __builtin_elementwise_max(__builtin_elementwise_max(a, b),
+                                              __builtin_elementwise_max(c, d));
+    return max((int)m.x, (int)m.y) > (int)(short)t;
+  }
+  __device__ static bool above_neg(const uint4& u, Raw t) {
+    const s16x2 a = __builtin_bit_cast(s16x2, u.x), b = __builtin_bit_cast(s16x2, u.y);
+    const s16x2 c = __builtin_bit_cast(s16x2, u.z), d = __builtin_bit_cast(s16x2, u.w);
+    const s16x2 m = __builtin_elementwise_max(__builtin_elementwise_max(a, b),
+                                              __builtin_elementwise_max(c, d));
+    const u16x2 ua = __builtin_bit_cast(u16x2, u.x), ub = __builtin_bit_cast(u16x2, u.y);
+    const u16x2 uc = __builtin_bit_cast(u16x2, u.z), ud = __builtin_bit_cast(u16x2, u.w);
+    const u16x2 n = __builtin_elementwise_min(__builtin_elementwise_min(ua, ub),
+                                              __builtin_elementwise_min(uc, ud));
+    return max((int)m.x, (int)m.y) >= 0 || min((int)n.x, (int)n.y) < (int)t;
+  }
 };
 template <> struct Tr<float> {
-  using Key = uint32_t;
+  using Raw = uint32_t;
   static constexpr int VEC = 4;
   static constexpr int DIGITS = 4;
-  __device__ static Key key(float raw) { return f32_key(raw); }
-  __device__ static float value(Key k) { return key_f32(k); }
+  static constexpr Raw kMin = 0xffffffffu;
+  __device__ static uint32_t key(Raw r) { return f32_key(__uint_as_float(r)); }
+  __device__ static float value(uint32_t k) { return key_f32(k); }
+  __device__ static Raw raw(uint32_t k) { return (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k; }
+  __device__ static bool above_pos(const uint4& u, Raw t) {
+    return max(max((int)u.x, (int)u.y), max((int)u.z, (int)u.w)) > (int)t;
+  }
+  __device__ static bool above_neg(const uint4& u, Raw t) {
+    const int mx = max(max((int)u.x, (int)u.y), max((int)u.z, (int)u.w));
+    return mx >= 0 || min(min(u.x, u.y), min(u.z, u.w)) < t;
+  }
 };
 
-template <typename T>
-struct Smem {
-  typename Tr<T>::Key cand[CAP];
-  typename Tr<T>::Key stage[KVC_MAX_TOPK_ENTROPY];
+// Per-wave LDS: CAP candidate bit patterns and a 256-bin histogram.
+template <typename Raw, int CAP>
+struct WaveSmem {
+  uint4 cand4[CAP * sizeof(Raw) / 16];
   int hist[256];
-  int wtot[2][NT / kWave];
-  int scan[NT / kWave];
-  int pick[2];
-  float red[NT / kWave];
 };
 
-// Exact k-th largest key of cand[0..count) and the number of keys above it.
-// Then rewrites cand[0..k) as (keys > tau in their current order, then k - cgt
-// copies of tau).  Called by all threads; returns the new count (= k).
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// lanes strictly below this one that have their bit set in `mask`
+__device__ __forceinline__ int lanes_below(uint64_t mask) {
+  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                        __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+// Ordered in-place compaction of cand[0..c): keeps the elements whose key passes
+// `keep`, in their order; returns how many.  Lane l of round r reads the 16-byte
+// group 64r + l; all reads of a round precede its writes, and an element only
+// moves to a lower index.
+template <typename T, typename Keep>
+__device__ __forceinline__ int compact_keep(typename Tr<T>::Raw* cand, int c, Keep keep) {
+  using Raw = typename Tr<T>::Raw;
+  constexpr int VEC = Tr<T>::VEC;
+  const int lane = threadIdx.x & 63;
+  int pos = 0;
+  for (int g0 = 0; g0 * VEC < c; g0 += 64) {
+    const int g = g0 + lane;
+    Raw e[VEC];
+    uint32_t bits = 0;
+    if (g * VEC < c) {
+      const uint4 u = reinterpret_cast<const uint4*>(cand)[g];
+      __builtin_memcpy(&e, &u, 16);
+#pragma unroll
+      for (int i = 0; i < VEC; ++i)
+        bits |= (uint32_t)(g * VEC + i < c && keep(Tr<T>::key(e[i]))) << i;
+    }
+    const int cnt = __builtin_popcount(bits);
+    const int incl = wave_inclusive_scan(cnt);
+    wave_sync();
+    int p = pos + incl - cnt;
+#pragma unroll
+    for (int i = 0; i < VEC; ++i)
+      if (bits & (1u << i)) cand[p++] = e[i];
+    pos += __builtin_amdgcn_readlane(incl, 63);   // wave-uniform
+    wave_sync();
+  }
+  return pos;
+}
+
+// Re-select over cand[0..count): returns the new tau (the k-th largest key) and
+// leaves cand[0..k) = the keys > tau in order, then copies of tau, padded with
+// the smallest key to a whole vector; count receives the padded length.
+// With have_tau, the elements below the old tau are dropped first (the list
+// holds k elements >= it, so none of them can be in the top-k).
 template <typename T>
-__device__ int reselect(Smem<T>& sm, int count, int k) {
-  using Key = typename Tr<T>::Key;
+__device__ __forceinline__ uint32_t reselect(typename Tr<T>::Raw* cand, int* hist, int& count,
+                                             int k, bool have_tau, uint32_t tau_old) {
+  using Raw = typename Tr<T>::Raw;
+  constexpr int VEC = Tr<T>::VEC;
   constexpr int DIG = Tr<T>::DIGITS;
-  const int tid = threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  wave_sync();
+  int c = count;
+  if (have_tau) c = compact_keep<T>(cand, c, [=](uint32_t key) { return key >= tau_old; });
   uint32_t prefix = 0;
-  int above = 0, need = k;
+  int need = k;                                  // rank of tau among the keys left
 #pragma unroll 1
   for (int p = DIG - 1; p >= 0; --p) {
     const int shift = 8 * p;
     const uint32_t hi_mask = (p == DIG - 1) ? 0u : (uint32_t)(~0ull << (shift + 8));
-    sm.hist[tid] = 0;
-    __syncthreads();
-    for (int i = tid; i < count; i += NT) {
-      uint32_t key = sm.cand[i];
-      if ((key & hi_mask) == (prefix & hi_mask)) atomicAdd(&sm.hist[(key >> shift) & 255], 1);
-    }
-    __syncthreads();
-    // thread t owns bin 255 - t: inclusive scan from the top bin down
-    const int c = sm.hist[255 - tid];
-    int tot;
-    const int incl = block_exclusive_scan<NT>(c, sm.scan, &tot) + c;
-    if (incl >= need && incl - c < need) { sm.pick[0] = 255 - tid; sm.pick[1] = incl - c; }
-    __syncthreads();
-    prefix |= (uint32_t)sm.pick[0] << shift;
-    above += sm.pick[1];
-    need -= sm.pick[1];
-    __syncthreads();
-  }
-  const Key tau = (Key)prefix;
-  const int cgt = above;
-  // ordered compaction of keys > tau into stage[0..cgt)
-  const int seg = (count + NT - 1) / NT;
-  const int b = min(count, tid * seg), e = min(count, b + seg);
-  int mine = 0;
-  for (int i = b; i < e; ++i) mine += sm.cand[i] > tau;
-  int tot;
-  int pos = block_exclusive_scan<NT>(mine, sm.scan, &tot);
-  for (int i = b; i < e; ++i) {
-    Key key = sm.cand[i];
-    if (key > tau) sm.stage[pos++] = key;
-  }
-  for (int i = cgt + tid; i < k; i += NT) sm.stage[i] = tau;
-  __syncthreads();
-  for (int i = tid; i < k; i += NT) sm.cand[i] = sm.stage[i];
-  __syncthreads();
-  return k;
-}
-
-template <typename T>
-__device__ __forceinline__ void load_vec(const T* row, int64_t e0, int64_t vocab, bool vec_ok,
-                                         T (&out)[Tr<T>::VEC], int& nvalid) {
-  constexpr int VEC = Tr<T>::VEC;
-  int64_t left = vocab - e0;
-  nvalid = left >= VEC ? VEC : (left > 0 ? (int)left : 0);
-  if (nvalid == VEC && vec_ok) {
-    uint4 u = *reinterpret_cast<const uint4*>(row + e0);
-    __builtin_memcpy(&out, &u, 16);
-  } else {
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) out[e] = (e < nvalid) ? row[e0 + e] : T(0);
-  }
-}
-
-template <typename T>
-__global__ void __launch_bounds__(NT)
-topk_entropy_kernel(const T* __restrict__ logits, int64_t vocab, int64_t stride, int k,
-                    float* __restrict__ H) {
-  using Key = typename Tr<T>::Key;
-  constexpr int VEC = Tr<T>::VEC;
-  constexpr int E = NV * VEC;
-  constexpr int CHUNK = NT * E;
-  __shared__ Smem<T> sm;
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
-  const int64_t rowi = blockIdx.x;
-  const T* row = logits + rowi * stride;
-  const bool vec_ok = ((reinterpret_cast<uintptr_t>(row) & 15) == 0);
-  const int64_t nchunks = (vocab + CHUNK - 1) / CHUNK;
-
-  T cur[NV][VEC], nxt[NV][VEC];
-  int ncur[NV], nnxt[NV];
+    for (int b = 0; b < 4; ++b) hist[lane * 4 + b] = 0;
+    wave_sync();
+    for (int g0 = 0; g0 * VEC < c; g0 += 64) {
+      const int g = g0 + lane;
+      if (g * VEC < c) {
+        const uint4 u = reinterpret_cast<const uint4*>(cand)[g];
+        Raw e[VEC];
+        __builtin_memcpy(&e, &u, 16);
 #pragma unroll
-  for (int v = 0; v < NV; ++v) load_vec<T>(row, (int64_t)(v * NT + tid) * VEC, vocab, vec_ok, cur[v], ncur[v]);
-
-  int count = 0, parity = 0;
-  bool have_tau = false;
-  Key tau = 0;
-#pragma unroll 1
-  for (int64_t c = 0; c < nchunks; ++c) {
-    if (c + 1 < nchunks) {
-#pragma unroll
-      for (int v = 0; v < NV; ++v)
-        load_vec<T>(row, (c + 1) * CHUNK + (int64_t)(v * NT + tid) * VEC, vocab, vec_ok, nxt[v], nnxt[v]);
-    }
-    Key keys[E];
-    uint32_t pass = 0;
-#pragma unroll
-    for (int v = 0; v < NV; ++v)
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) {
-        Key kk = Tr<T>::key(cur[v][e]);
-        keys[v * VEC + e] = kk;
-        bool p = (e < ncur[v]) && (!have_tau || kk > tau);
-        pass |= (uint32_t)p << (v * VEC + e);
+        for (int i = 0; i < VEC; ++i) {
+          const uint32_t key = Tr<T>::key(e[i]);
+          if (g * VEC + i < c && (key & hi_mask) == (prefix & hi_mask))
+            atomicAdd(&hist[(key >> shift) & 255], 1);
+        }
       }
-    const int cnt = __builtin_popcount(pass);
-    const int incl = wave_inclusive_scan(cnt);
-    if (lane == kWave - 1) sm.wtot[parity][wv] = incl;
-    __syncthreads();
-    int base = 0, tot = 0;
+    }
+    wave_sync();
+    // lane owns bins 255-4*lane ... 252-4*lane (descending); inclusive scan of the
+    // lane totals, then the crossing bin is found inside the owning lane
+    int cb[4], tot = 0;
 #pragma unroll
-    for (int i = 0; i < NT / kWave; ++i) {
-      int s = sm.wtot[parity][i];
-      base += (i < wv) ? s : 0;
-      tot += s;
-    }
-    if (pass) {
-      int pos = count + base + incl - cnt;
+    for (int b = 0; b < 4; ++b) { cb[b] = hist[255 - 4 * lane - b]; tot += cb[b]; }
+    const int incl = wave_inclusive_scan(tot);
+    int run = incl - tot, dsel = -1, asel = 0;
 #pragma unroll
-      for (int e = 0; e < E; ++e)
-        if (pass & (1u << e)) sm.cand[pos++] = keys[e];
+    for (int b = 0; b < 4; ++b) {
+      if (dsel < 0 && run + cb[b] >= need) { dsel = 255 - 4 * lane - b; asel = run; }
+      run += cb[b];
     }
-    count += tot;
-    parity ^= 1;
-    if (!have_tau || count > RESEL) {
-      __syncthreads();
-      count = reselect<T>(sm, count, k);
-      tau = sm.cand[k - 1];   // the copies of tau sit at the end
-      // the smallest key held is tau (all others are > tau)
-      have_tau = true;
+    const uint64_t who = __ballot(dsel >= 0 && incl - tot < need);
+    const int src = __builtin_ctzll(who);
+    const int digit = __builtin_amdgcn_readlane(dsel, src);
+    const int abv = __builtin_amdgcn_readlane(asel, src);
+    prefix |= (uint32_t)digit << shift;
+    need -= abv;
+    wave_sync();
+  }
+  const uint32_t tau = prefix;
+  const int cgt = compact_keep<T>(cand, c, [=](uint32_t key) { return key > tau; });
+  // the cgt keys > tau are now cand[0..cgt), with cgt < k
+  const int kr = (k + VEC - 1) / VEC * VEC;
+  const Raw traw = Tr<T>::raw(tau);
+  for (int i = cgt + lane; i < kr; i += 64) cand[i] = i < k ? traw : Tr<T>::kMin;
+  wave_sync();
+  count = kr;
+  return tau;
+}
+
+// One vector of the ragged last step: elements past the row end read as the
+// smallest key, which never enters the top-k ahead of a real element.
+template <typename T>
+__device__ __forceinline__ uint4 load_tail(const T* row, int64_t e0, int64_t vocab, bool vec_ok) {
+  using Raw = typename Tr<T>::Raw;
+  constexpr int VEC = Tr<T>::VEC;
+  const int64_t left = vocab - e0;
+  if (left >= VEC && vec_ok) return *reinterpret_cast<const uint4*>(row + e0);
+  const Raw* r = reinterpret_cast<const Raw*>(row);
+  Raw e[VEC];
+#pragma unroll
+  for (int i = 0; i < VEC; ++i) e[i] = (i < left) ? r[e0 + i] : Tr<T>::kMin;
+  uint4 u;
+  __builtin_memcpy(&u, &e, 16);
+  return u;
+}
+
+template <typename T, int CAP, bool ALIGNED>
+__global__ void __launch_bounds__(NT)
+topk_entropy_kernel(const T* __restrict__ logits, int64_t rows, int64_t vocab, int64_t stride,
+                    int k, float* __restrict__ H) {
+  using Raw = typename Tr<T>::Raw;
+  constexpr int VEC = Tr<T>::VEC;
+  constexpr int STEP = 64 * NV * VEC;            // elements per wave per step
+  static_assert(CAP == RESEL + STEP && CAP % VEC == 0, "list capacity");
+  __shared__ WaveSmem<Raw, CAP> smem[NT / 64];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x / 64;
+  const int64_t rowi = (int64_t)blockIdx.x * (NT / 64) + wv;
+  if (rowi >= rows) return;                      // no block barriers below
+  Raw* cand = reinterpret_cast<Raw*>(smem[wv].cand4);
+  int* hist = smem[wv].hist;
+  const T* row = logits + rowi * stride;
+  const int64_t nfull = vocab / STEP;            // steps with every element present
+
+  int count = 0;                                 // list length, a multiple of VEC
+  bool exact = false;                            // cand[0..k) is the top-k so far
+  uint32_t tau = 0;
+  Raw traw = 0;
+  bool tpos = true;
+
+  auto append = [&](const uint4& u, bool hit) __attribute__((always_inline)) {  // in lane order, whole vectors
+    const uint64_t m = __ballot(hit);
+    if (m) {
+      if (hit) reinterpret_cast<uint4*>(cand + count)[lanes_below(m)] = u;
+      count = __builtin_amdgcn_readfirstlane(count + __builtin_popcountll(m) * VEC);
+      exact = false;
     }
+  };
+  auto select = [&](bool have_tau) __attribute__((always_inline)) {
+    tau = __builtin_amdgcn_readfirstlane(reselect<T>(cand, hist, count, k, have_tau, tau));
+    count = __builtin_amdgcn_readfirstlane(count);
+    traw = (Raw)__builtin_amdgcn_readfirstlane((uint32_t)Tr<T>::raw(tau));
+    tpos = !(traw & (Raw)(Tr<T>::kMin ^ (Tr<T>::kMin >> 1)));
+    exact = true;
+  };
+  // the first step: every vector, then the first select (it holds >= k elements)
+  auto first = [&](const uint4 (&buf)[NV]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int v = 0; v < NV; ++v) append(buf[v], true);
+    select(false);
+  };
+  // later steps: the vectors holding a key above tau; re-select when long
+  auto filter = [&](const uint4 (&buf)[NV]) __attribute__((always_inline)) {
+    if (tpos) {
+#pragma unroll
+      for (int v = 0; v < NV; ++v) append(buf[v], Tr<T>::above_pos(buf[v], traw));
+    } else {
+#pragma unroll
+      for (int v = 0; v < NV; ++v) append(buf[v], Tr<T>::above_neg(buf[v], traw));
+    }
+    if (count > RESEL) select(true);
+  };
+  auto load = [&](int64_t c, uint4 (&buf)[NV]) __attribute__((always_inline)) {
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
-      ncur[v] = nnxt[v];
+      const T* p = row + c * STEP + (int64_t)(v * 64 + lane) * VEC;
+      if constexpr (ALIGNED) {
+        buf[v] = *reinterpret_cast<const uint4*>(p);
+      } else {
+        const Raw* r = reinterpret_cast<const Raw*>(p);
+        Raw e[VEC];
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) cur[v][e] = nxt[v][e];
+        for (int i = 0; i < VEC; ++i) e[i] = r[i];
+        __builtin_memcpy(&buf[v], &e, 16);
+      }
     }
+  };
+  auto load_last = [&](uint4 (&buf)[NV]) __attribute__((always_inline)) {       // the ragged last step
+#pragma unroll
+    for (int v = 0; v < NV; ++v)
+      buf[v] = load_tail<T>(row, nfull * STEP + (int64_t)(v * 64 + lane) * VEC, vocab, ALIGNED);
+  };
+  // Full steps.  The next step's loads are issued before the current step is
+  // filtered, and unconditionally (past the end they re-read the last full step,
+  // an L2 hit): a load issued on only some paths would make the compiler wait for
+  // every outstanding load before each step.
+  uint4 ba[NV], bb[NV];
+  if (nfull > 0) {
+    const int64_t last = nfull - 1;
+    load(0, ba);
+    load(min((int64_t)1, last), bb);
+    first(ba);
+    // whole pairs of steps, no exit in between (an exit between the two halves
+    // would also make the compiler wait for the loads in flight at the top)
+    int64_t c = 1;                               // bb holds step c
+#pragma unroll 1
+    for (; c + 1 < nfull; c += 2) {
+      load(c + 1, ba);
+      filter(bb);
+      load(min(c + 2, last), bb);
+      filter(ba);
+    }
+    if (c < nfull) filter(bb);                   // the odd step left over
+    if (nfull * STEP < vocab) {
+      load_last(ba);
+      filter(ba);
+    }
+  } else {                                       // the row is shorter than a step
+    load_last(ba);
+    first(ba);
   }
-  __syncthreads();
-  if (count > k) count = reselect<T>(sm, count, k);
+  if (!exact) select(true);
 
   // entropy over the k held keys (float32, fixed reduction order)
   float mloc = -INFINITY;
-  for (int i = tid; i < k; i += NT) mloc = fmaxf(mloc, Tr<T>::value(sm.cand[i]));
-  const float m = block_max<NT>(mloc, sm.red);
+  for (int i = lane; i < k; i += 64) mloc = fmaxf(mloc, Tr<T>::value(Tr<T>::key(cand[i])));
+  const float m = wave_max(mloc);
   float zloc = 0.f;
-  for (int i = tid; i < k; i += NT) zloc += expf(Tr<T>::value(sm.cand[i]) - m);
-  const float Z = block_sum<NT>(zloc, sm.red);
+  for (int i = lane; i < k; i += 64) zloc += expf(Tr<T>::value(Tr<T>::key(cand[i])) - m);
+  const float Z = wave_sum(zloc);
   const float lnZ = logf(Z), invZ = 1.0f / Z;
   float hloc = 0.f;
-  for (int i = tid; i < k; i += NT) {
-    float t = Tr<T>::value(sm.cand[i]);
+  for (int i = lane; i < k; i += 64) {
+    const float t = Tr<T>::value(Tr<T>::key(cand[i]));
     hloc += expf(t - m) * invZ * ((m - t) + lnZ);   // -p ln p, every term >= 0
   }
-  const float h = block_sum<NT>(hloc, sm.red);
-  if (tid == 0) H[rowi] = h;
+  const float h = wave_sum(hloc);
+  if (lane == 0) H[rowi] = h;
+}
+
+template <typename T>
+void launch(const void* logits, int64_t rows, int64_t vocab, int64_t stride, int k, float* H,
+            hipStream_t s) {
+  constexpr int CAP = RESEL + 64 * NV * Tr<T>::VEC;
+  static_assert(RESEL >= KVC_MAX_TOPK_ENTROPY + 8, "a re-selected list must fit below RESEL");
+  const unsigned grid = (unsigned)((rows + NT / 64 - 1) / (NT / 64));
+  // every row start is 16-byte aligned iff the base and the row pitch are
+  const bool aligned = ((uintptr_t)logits % 16 == 0) && ((stride * (int64_t)sizeof(T)) % 16 == 0);
+  if (aligned)
+    hipLaunchKernelGGL((topk_entropy_kernel<T, CAP, true>), dim3(grid), dim3(NT), 0, s,
+                       (const T*)logits, rows, vocab, stride, k, H);
+  else
+    hipLaunchKernelGGL((topk_entropy_kernel<T, CAP, false>), dim3(grid), dim3(NT), 0, s,
+                       (const T*)logits, rows, vocab, stride, k, H);
 }
 
 }  // namespace
@@ -226,18 +379,14 @@ extern "C" int kvc_topk_entropy(const void* logits, int dtype, int64_t rows, int
   clear_error();
   if (!dtype_ok(dtype)) return KVC_FAIL(KVC_ERR_DTYPE, "kvc_topk_entropy: dtype %d", dtype);
   KVC_REQUIRE(rows >= 0, "kvc_topk_entropy: rows < 0");
-  KVC_REQUIRE(rows <= 0x7fffffff, "kvc_topk_entropy: rows > 2^31-1");
+  KVC_REQUIRE(rows <= 0x7fffffffLL * 4, "kvc_topk_entropy: too many rows");
   KVC_REQUIRE(vocab >= 1 && row_stride >= vocab, "kvc_topk_entropy: need 1 <= vocab <= row_stride");
   KVC_REQUIRE(topk >= 1 && topk <= KVC_MAX_TOPK_ENTROPY && topk <= vocab,
               "kvc_topk_entropy: need 1 <= topk <= min(vocab, %d)", KVC_MAX_TOPK_ENTROPY);
   if (rows == 0) return KVC_OK;
   KVC_REQUIRE(logits && H_out, "kvc_topk_entropy: null pointer");
   hipStream_t s = as_stream(stream);
-  if (dtype == KVC_BF16)
-    hipLaunchKernelGGL(topk_entropy_kernel<uint16_t>, dim3((unsigned)rows), dim3(NT), 0, s,
-                       (const uint16_t*)logits, vocab, row_stride, topk, H_out);
-  else
-    hipLaunchKernelGGL(topk_entropy_kernel<float>, dim3((unsigned)rows), dim3(NT), 0, s,
-                       (const float*)logits, vocab, row_stride, topk, H_out);
+  if (dtype == KVC_BF16) launch<uint16_t>(logits, rows, vocab, row_stride, topk, H_out, s);
+  else launch<float>(logits, rows, vocab, row_stride, topk, H_out, s);
   return launch_status("kvc_topk_entropy");
 }

@@ -50,6 +50,15 @@ ENTROPY_CASES = [
     (6, 9000, 9000, 256, torch.bfloat16, "ascending"),     # worst case for the filter
     (6, 9000, 9000, 256, torch.bfloat16, "ties"),          # many equal values at the threshold
     (4, 20000, 20000, 64, torch.float32, "flat"),          # all equal -> ln k
+    (12, 128256, 128256, 256, torch.bfloat16, "logprob"),  # every value < 0: negative threshold
+    (7, 50000, 50001, 200, torch.float32, "logprob"),      # the same in float32, odd pitch
+    (8, 9000, 9000, 256, torch.bfloat16, "zeros"),         # +0 / -0 ties: threshold 0
+    (8, 5000, 5000, 1000, torch.bfloat16, "zeros"),        # -0 above a negative threshold
+    (8, 5000, 5000, 1000, torch.float32, "zeros"),
+    (8, 9000, 9000, 256, torch.bfloat16, "neginf"),        # 90% -inf (masked vocabulary)
+    (5, 1000, 1000, 256, torch.bfloat16, "normal4"),       # row shorter than one step
+    (5, 700, 701, 100, torch.float32, "normal4"),          # the same in float32, odd pitch
+    (6, 9000, 9000, 256, torch.bfloat16, "descending"),
 ]
 
 
@@ -63,6 +72,23 @@ def entropy_input(rows, stride, kind, dtype, dev, seed):
         return torch.randint(0, 12, (rows, stride), generator=g, device=dev).to(torch.float32).div(2).to(dtype)
     if kind == "flat":
         return torch.full((rows, stride), 0.5, device=dev, dtype=dtype)
+    if kind == "descending":
+        return torch.linspace(8, -8, stride, device=dev)[None, :].repeat(rows, 1).to(dtype)
+    if kind == "zeros":      # values in {-3.5, ..., -0.5, 0}, each zero +0 or -0 at random
+        g = torch.Generator(device=dev)
+        g.manual_seed(seed)
+        v = -torch.randint(0, 8, (rows, stride), generator=g, device=dev).to(torch.float32) / 2
+        neg = torch.randint(0, 2, (rows, stride), generator=g, device=dev).bool()
+        v = torch.where((v == 0) & neg, torch.full_like(v, -0.0), v)
+        return v.to(dtype)
+    if kind == "logprob":
+        return torch.log_softmax(gen((rows, stride), seed, dev, torch.float32, 4.0), dim=1).to(dtype)
+    if kind == "neginf":
+        g = torch.Generator(device=dev)
+        g.manual_seed(seed + 2)
+        x = gen((rows, stride), seed, dev, torch.float32, 4.0)
+        x[torch.rand((rows, stride), generator=g, device=dev) < 0.9] = -math.inf
+        return x.to(dtype)
     scale = 3.0 if kind == "normal3" else 4.0
     x = gen((rows, stride), seed, dev, torch.float32, scale)
     if kind == "spiked":
