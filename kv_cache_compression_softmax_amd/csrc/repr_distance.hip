@@ -8,8 +8,10 @@
 // wave owns one token: it loads the token's final-layer row once into registers
 // (hidden/64 elements per lane), then streams the same row of every layer,
 // accumulating <a, b> and |a|^2 per lane in float32 and reducing across the wave.
-// Loads are 16 bytes per lane and a wave instruction covers 1 KB of one row.  The
-// next layer's row is requested before the current one is reduced.
+// Loads are 16 bytes per lane and a wave instruction covers 1 KB of one row.  Two
+// layer rows are held in turn: the next layer's row is in flight while the current
+// one is reduced.  bf16 products go through v_dot2_f32_bf16 (two products and the
+// float32 accumulate in one instruction, no unpacking).
 #include "common.h"
 
 namespace kvc {
@@ -18,21 +20,32 @@ namespace {
 constexpr int NT = 256;          // 4 waves = 4 tokens per workgroup
 constexpr int MAXV = 16;         // most 16-byte vectors per lane kept in registers
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
 template <typename T> struct VecT;
 template <> struct VecT<uint16_t> { static constexpr int N = 8; };
 template <> struct VecT<float> { static constexpr int N = 4; };
 
+// acc[j] += <x, y> over the 16-byte vector's elements (4 independent sums)
 template <typename T>
-__device__ __forceinline__ void unpack(const uint4& u, float (&x)[VecT<T>::N]);
+__device__ __forceinline__ void dot_acc(const uint4& x, const uint4& y, float (&acc)[4]);
 template <>
-__device__ __forceinline__ void unpack<uint16_t>(const uint4& u, float (&x)[8]) {
-  x[0] = bf16_lo(u.x); x[1] = bf16_hi(u.x); x[2] = bf16_lo(u.y); x[3] = bf16_hi(u.y);
-  x[4] = bf16_lo(u.z); x[5] = bf16_hi(u.z); x[6] = bf16_lo(u.w); x[7] = bf16_hi(u.w);
+__device__ __forceinline__ void dot_acc<uint16_t>(const uint4& x, const uint4& y, float (&acc)[4]) {
+  acc[0] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x.x),
+                                           __builtin_bit_cast(bf16x2, y.x), acc[0], false);
+  acc[1] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x.y),
+                                           __builtin_bit_cast(bf16x2, y.y), acc[1], false);
+  acc[2] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x.z),
+                                           __builtin_bit_cast(bf16x2, y.z), acc[2], false);
+  acc[3] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x.w),
+                                           __builtin_bit_cast(bf16x2, y.w), acc[3], false);
 }
 template <>
-__device__ __forceinline__ void unpack<float>(const uint4& u, float (&x)[4]) {
-  x[0] = __uint_as_float(u.x); x[1] = __uint_as_float(u.y);
-  x[2] = __uint_as_float(u.z); x[3] = __uint_as_float(u.w);
+__device__ __forceinline__ void dot_acc<float>(const uint4& x, const uint4& y, float (&acc)[4]) {
+  acc[0] = fmaf(__uint_as_float(x.x), __uint_as_float(y.x), acc[0]);
+  acc[1] = fmaf(__uint_as_float(x.y), __uint_as_float(y.y), acc[1]);
+  acc[2] = fmaf(__uint_as_float(x.z), __uint_as_float(y.z), acc[2]);
+  acc[3] = fmaf(__uint_as_float(x.w), __uint_as_float(y.w), acc[3]);
 }
 
 __device__ __forceinline__ float distance(float dot, float na2, float nb2, float tau) {
@@ -42,8 +55,9 @@ __device__ __forceinline__ float distance(float dot, float na2, float nb2, float
 }
 
 // Fast path: rows 16-byte aligned, hidden a multiple of the vector width and at
-// most 64 * V vectors (V = vectors per lane held in registers).
-template <typename T, int V>
+// most 64 * V vectors (V = vectors per lane held in registers); FULL: exactly
+// 64 * V, so no lane skips a vector.
+template <typename T, int V, bool FULL>
 __global__ void __launch_bounds__(NT)
 repr_distance_vec(ConstPtrs h, const T* __restrict__ hf, int L, int64_t n, int64_t hidden,
                   float tau, float* __restrict__ D) {
@@ -53,52 +67,60 @@ repr_distance_vec(ConstPtrs h, const T* __restrict__ hf, int L, int64_t n, int64
   if (tok >= n) return;
   const int nvec = (int)(hidden / W);             // vectors per row
   const int64_t roff = tok * hidden;
-  uint4 b[V];
-  float nb2 = 0.f;
-#pragma unroll
-  for (int v = 0; v < V; ++v) {
-    const int vi = v * kWave + lane;
-    if (vi < nvec) {
-      b[v] = *reinterpret_cast<const uint4*>(hf + roff + (int64_t)vi * W);
-      float x[W];
-      unpack<T>(b[v], x);
-#pragma unroll
-      for (int e = 0; e < W; ++e) nb2 += x[e] * x[e];
-    }
-  }
-  nb2 = wave_sum(nb2);
-  uint4 a[V];
-#pragma unroll
-  for (int v = 0; v < V; ++v) {
-    const int vi = v * kWave + lane;
-    if (vi < nvec) a[v] = *reinterpret_cast<const uint4*>((const T*)h.p[0] + roff + (int64_t)vi * W);
-  }
-#pragma unroll 1
-  for (int l = 0; l < L; ++l) {
-    float dot = 0.f, na2 = 0.f;
+  // The rows are read-only, so the compiler may re-issue a prefetch where its data
+  // is used; the empty asm with a memory clobber keeps each load where it stands.
+  auto load = [&](const T* row, uint4 (&a)[V]) __attribute__((always_inline)) {
 #pragma unroll
     for (int v = 0; v < V; ++v) {
       const int vi = v * kWave + lane;
-      if (vi < nvec) {
-        float x[W], y[W];
-        unpack<T>(a[v], x);
-        unpack<T>(b[v], y);
-#pragma unroll
-        for (int e = 0; e < W; ++e) { dot += x[e] * y[e]; na2 += x[e] * x[e]; }
-      }
+      if (FULL || vi < nvec) a[v] = *reinterpret_cast<const uint4*>(row + (int64_t)vi * W);
+      else a[v] = make_uint4(0u, 0u, 0u, 0u);      // contributes 0 to every sum
     }
-    if (l + 1 < L) {                        // next layer's row while this one reduces
-      const T* nl = (const T*)h.p[l + 1] + roff;
+    asm volatile("" ::: "memory");
+  };
+  uint4 b[V];
+  load(hf + roff, b);
+  float nb2;
+  {
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int v = 0; v < V; ++v) {
-        const int vi = v * kWave + lane;
-        if (vi < nvec) a[v] = *reinterpret_cast<const uint4*>(nl + (int64_t)vi * W);
-      }
-    }
-    dot = wave_sum(dot);
-    na2 = wave_sum(na2);
-    if (lane == 0) D[(int64_t)l * n + tok] = distance(dot, na2, nb2, tau);
+    for (int v = 0; v < V; ++v) dot_acc<T>(b[v], b[v], acc);
+    nb2 = wave_sum((acc[0] + acc[1]) + (acc[2] + acc[3]));
   }
+  // lane l keeps layer l's result (L <= 64 per launch); one store per lane at the
+  // end, so the layer loop is a single basic block the scheduler keeps in order
+  float mine = 0.f;
+  auto layer = [&](int l, const uint4 (&a)[V]) __attribute__((always_inline)) {
+    float d4[4] = {0.f, 0.f, 0.f, 0.f}, n4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int v = 0; v < V; ++v) { dot_acc<T>(a[v], b[v], d4); dot_acc<T>(a[v], a[v], n4); }
+    const float dot = wave_sum((d4[0] + d4[1]) + (d4[2] + d4[3]));
+    const float na2 = wave_sum((n4[0] + n4[1]) + (n4[2] + n4[3]));
+    float dist = distance(dot, na2, nb2, tau);
+    asm volatile("" : "+v"(dist));               // computed by every lane, then selected
+    mine = lane == l ? dist : mine;
+  };
+  // Layers in pairs, two rows in turn.  Loads are unconditional (past the last
+  // layer they re-read it, an L2 hit) and no exit sits between the halves, so the
+  // compiler never has to wait for the row that is still in flight.
+  uint4 a0[V], a1[V];
+  const int last = L - 1;
+  load((const T*)h.p[0] + roff, a0);
+  load((const T*)h.p[min(1, last)] + roff, a1);
+  int l = 0;
+#pragma unroll 1
+  for (; l + 1 < L; l += 2) {
+    // the barriers keep each refill behind the last read of its buffer, so the
+    // new row lands in the same registers (no copies of rows still in flight)
+    layer(l, a0);
+    __builtin_amdgcn_sched_barrier(0);
+    load((const T*)h.p[min(l + 2, last)] + roff, a0);
+    layer(l + 1, a1);
+    __builtin_amdgcn_sched_barrier(0);
+    load((const T*)h.p[min(l + 3, last)] + roff, a1);
+  }
+  if (l < L) layer(l, a0);
+  if (lane < L) D[(int64_t)lane * n + tok] = mine;
 }
 
 template <typename T> __device__ __forceinline__ float ld(const T* p);
@@ -145,8 +167,14 @@ int launch(const void* const* h_layers, const void* h_final, int L, int64_t n, i
     float* Dl = D + (int64_t)l0 * n;
     const int64_t per_lane = (hidden / W + kWave - 1) / kWave;
 #define KVC_RD_LAUNCH(VV)                                                                     \
-    hipLaunchKernelGGL((repr_distance_vec<T, VV>), dim3(grid), dim3(NT), 0, s, tab,          \
-                       (const T*)h_final, lc, n, hidden, tau, Dl)
+    do {                                                                                      \
+      if (hidden / W == (int64_t)(VV) * kWave)                                                \
+        hipLaunchKernelGGL((repr_distance_vec<T, VV, true>), dim3(grid), dim3(NT), 0, s, tab, \
+                           (const T*)h_final, lc, n, hidden, tau, Dl);                        \
+      else                                                                                    \
+        hipLaunchKernelGGL((repr_distance_vec<T, VV, false>), dim3(grid), dim3(NT), 0, s, tab,\
+                           (const T*)h_final, lc, n, hidden, tau, Dl);                        \
+    } while (0)
     if (vec && per_lane <= 1) KVC_RD_LAUNCH(1);
     else if (vec && per_lane <= 2) KVC_RD_LAUNCH(2);
     else if (vec && per_lane <= 4) KVC_RD_LAUNCH(4);

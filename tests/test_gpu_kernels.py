@@ -133,9 +133,12 @@ DIST_CASES = [
     (1, 512, 256, torch.float32),
     (3, 2051, 3072, torch.bfloat16),
     (2, 1029, 4096, torch.bfloat16),
-    (2, 77, 1000, torch.bfloat16),       # width not a multiple of 8: element path
+    (2, 77, 1000, torch.bfloat16),       # 125 vectors: a partly filled register row
+    (2, 64, 4100, torch.bfloat16),       # width not a multiple of 8: element path
     (2, 65, 8192, torch.bfloat16),       # 16 vectors per lane
+    (4, 300, 4096, torch.float32),       # float32, 16 vectors per lane
     (35, 130, 512, torch.bfloat16),      # more layers than one launch holds
+    (64, 40, 256, torch.bfloat16),       # two full launches
 ]
 
 
@@ -156,6 +159,22 @@ def test_repr_distance(dev, case):
     assert_rel(D.cpu().numpy(), ref, 1e-3, what="D")
     if L > 1:   # last layer equals the final state bit for bit -> D = tau
         np.testing.assert_allclose(D[L - 1].cpu().numpy(), 1.0, atol=1e-6)
+
+
+def test_repr_distance_zero_rows(dev):
+    """A zero hidden state has cos := 0, so D = 1 + tau exactly."""
+    n, hidden = 40, 4096
+    hf = gen((n, hidden), 3, dev, torch.bfloat16)
+    layers = [gen((n, hidden), 4 + l, dev, torch.bfloat16) for l in range(3)]
+    layers[0][5].zero_()
+    hf[9].zero_()
+    D = torch.empty(3, n, device=dev)
+    B().kvc_repr_distance(layers, hf, 0.25, D)
+    torch.cuda.synchronize()
+    got = D.cpu().numpy()
+    assert got[0, 5] == 1.25 and np.all(got[:, 9] == 1.25)
+    ref = np.stack([infokv.repr_distance(host_f64(layers[l]), host_f64(hf), 0.25) for l in range(3)])
+    assert_rel(got, ref, 1e-3, what="D")
 
 
 # ----------------------------------------------------------------- window attention
