@@ -44,10 +44,6 @@ constexpr int KPW = 256;        // keys per wave
 #define KVC_WIN_CHAINS 1
 #endif
 constexpr int CH = KVC_WIN_CHAINS;  // tiles whose MFMA chains are issued interleaved
-#ifndef KVC_WIN_PF
-#define KVC_WIN_PF 1
-#endif
-constexpr int PF = KVC_WIN_PF;      // key blocks loaded ahead of the one being computed
 constexpr int MIN_WAVES = 4096; // waves per launch that fill 256 CUs
 constexpr float LOG2E = 1.4426950408889634f;
 
@@ -73,50 +69,45 @@ struct WinArgs {
   int64_t ntask;                       // tasks of all spans
 };
 
-template <int D>
-__device__ __forceinline__ void load_k(const uint16_t* k, const Geo& g, int kvh, int64_t j0, int lane,
-                                       bf16x8 (&kf)[D / 16]) {
-  const int i = lane & 31, hf = lane >> 5;
-  const int64_t key = j0 + i;
-  if (key < g.n) {
-    const uint16_t* p = k + ((int64_t)kvh * g.n + key) * D + hf * (D / 2);
-#pragma unroll
-    for (int s = 0; s < D / 16; ++s) kf[s] = *reinterpret_cast<const bf16x8*>(p + 8 * s);
-  } else {
-#pragma unroll
-    for (int s = 0; s < D / 16; ++s) kf[s] = bf16x8{};
-  }
-}
-
-// row (M index) of accumulator element v held by a lane of half hf
-__device__ __forceinline__ int acc_row(int v, int hf) { return 8 * (v >> 2) + 4 * hf + (v & 3); }
-
 __device__ __forceinline__ bf16x8 as_bf16x8(const uint4& u) {
   bf16x8 r;
   __builtin_memcpy(&r, &u, 16);
   return r;
 }
 
-// Streams the 32-key blocks of [jb, je) through PF + 1 rotating register sets:
-// block j's keys are requested PF blocks before `block` runs on them.
+// Streams the 32-key blocks jb, jb + 32, ... (nb of them) of one KV head through
+// two register sets used in turn: block b + 1 is in flight while `block` runs on
+// block b.  Rows past the end of K are clamped to the last key (the callers mask
+// every key >= n), so every prefetch is unconditional; loads issued on only some
+// paths, or re-issued by the compiler at their use (the data are read-only: the
+// memory clobber pins them), would make every block wait for its own keys.
 template <int D, typename F>
-__device__ __forceinline__ void stream_blocks(const uint16_t* k, const Geo& g, int kvh, int64_t jb,
-                                              int64_t je, int lane, F&& block) {
-  constexpr int S = D / 16, NB = PF + 1;
-  bf16x8 kb[NB][S];
+__device__ __forceinline__ void stream_blocks(const uint16_t* kh, int64_t n, int64_t jb, int nb,
+                                              int lane, F&& block) {
+  constexpr int S = D / 16;
+  if (nb <= 0) return;
+  const int i = lane & 31, hf = lane >> 5;
+  auto load = [&](int b, bf16x8 (&kf)[S]) __attribute__((always_inline)) {
+    const int64_t key = min(jb + 32 * b + i, n - 1);
+    const uint16_t* p = kh + key * D + hf * (D / 2);
 #pragma unroll
-  for (int p = 0; p < PF; ++p)
-    if (jb + 32 * p < je) load_k<D>(k, g, kvh, jb + 32 * p, lane, kb[p]);
+    for (int st = 0; st < S; ++st) kf[st] = *reinterpret_cast<const bf16x8*>(p + 8 * st);
+    asm volatile("" ::: "memory");
+  };
+  bf16x8 k0[S], k1[S];
+  load(0, k0);
+  load(min(1, nb - 1), k1);
+  int b = 0;
 #pragma unroll 1
-  for (int64_t j0 = jb; j0 < je; j0 += 32 * NB) {
-#pragma unroll
-    for (int r = 0; r < NB; ++r) {
-      const int64_t jj = j0 + 32 * r;
-      if (jj >= je) break;
-      if (jj + 32 * PF < je) load_k<D>(k, g, kvh, jj + 32 * PF, lane, kb[(r + PF) % NB]);
-      block(kb[r], jj);
-    }
+  for (; b + 1 < nb; b += 2) {
+    block(k0, jb + 32 * b);
+    __builtin_amdgcn_sched_barrier(0);
+    load(min(b + 2, nb - 1), k0);
+    block(k1, jb + 32 * (b + 1));
+    __builtin_amdgcn_sched_barrier(0);
+    load(min(b + 3, nb - 1), k1);
   }
+  if (b < nb) block(k0, jb + 32 * b);
 }
 
 // Q rows of TG tiles into LDS in fragment order: entry (t, s, lane) holds the 16
@@ -153,9 +144,10 @@ template <int D, int TG>
 __device__ __forceinline__ void pass1(const WinArgs& a, WinSmem<D, TG>& sm, int l, int kvh, int wgi) {
   constexpr int S = D / 16;
   const Geo& g = a.g;
-  const int lane = threadIdx.x & 63, hf = lane >> 5, qi = lane & 31, wv = threadIdx.x / 64;
+  const int lane = threadIdx.x & 63, hf = lane >> 5, qi = lane & 31;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
   const int64_t lg = (int64_t)l * g.Hkv + kvh;
-  const uint16_t* k = (const uint16_t*)a.k.p[l];
+  const uint16_t* kh = (const uint16_t*)a.k.p[l] + (int64_t)kvh * g.n * D;   // this KV head's keys
   stage_q<D, TG>((const uint16_t*)a.q.p[l], g, kvh, a.tile0, sm.q);
   __syncthreads();
 
@@ -171,6 +163,7 @@ __device__ __forceinline__ void pass1(const WinArgs& a, WinSmem<D, TG>& sm, int 
 
   const int64_t jb = ((int64_t)wgi * (NTW / 64) + wv) * KPW;
   const int64_t je = min(g.n, jb + KPW);
+  const int nb = (int)((je - jb + 31) / 32);     // <= 0 past the end of K
   const int64_t safe_end = g.n - g.w;            // keys <= this are seen by every row
   // one 32-key block; kc holds its key fragments
   // FULL: every key of the block is visible to every row (no mask code at all)
@@ -212,7 +205,8 @@ __device__ __forceinline__ void pass1(const WinArgs& a, WinSmem<D, TG>& sm, int 
 #pragma unroll
         for (int v = 0; v < 16; ++v) bm = fmaxf(bm, acc[v]);
       } else {
-        const int64_t lim = min((int64_t)pos[t], g.n - 1) - j0 - 4 * hf;   // key offset limit
+        // key offset limit within the block; blocks start below n and pos < n
+        const int lim = (int)(min((int64_t)pos[t], g.n - 1) - j0) - 4 * hf;
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int off = 8 * (v >> 2) + (v & 3);
@@ -220,14 +214,15 @@ __device__ __forceinline__ void pass1(const WinArgs& a, WinSmem<D, TG>& sm, int 
           bm = fmaxf(bm, acc[v]);
         }
       }
-      if (full || bm > -INFINITY) {
-        const float mn = fmaxf(m[t], bm * a.sl2);
-        float sum = 0.f;
+      // no branch: a row that has seen no key yet keeps m = -inf and uses 0 as
+      // the exponent offset (every term is then exp2(-inf) = 0)
+      const float mn = fmaxf(m[t], bm * a.sl2);
+      const float ms = full ? mn : (mn > -INFINITY ? mn : 0.f);
+      float sum = 0.f;
 #pragma unroll
-        for (int v = 0; v < 16; ++v) sum += __builtin_amdgcn_exp2f(fmaf(acc[v], a.sl2, -mn));
-        sm_[t] = sm_[t] * __builtin_amdgcn_exp2f(m[t] - mn) + sum;
-        m[t] = mn;
-      }
+      for (int v = 0; v < 16; ++v) sum += __builtin_amdgcn_exp2f(fmaf(acc[v], a.sl2, -ms));
+      sm_[t] = sm_[t] * __builtin_amdgcn_exp2f(m[t] - ms) + sum;
+      m[t] = mn;
       }
     }
   };
@@ -235,7 +230,7 @@ __device__ __forceinline__ void pass1(const WinArgs& a, WinSmem<D, TG>& sm, int 
     if (j0 + 31 <= safe_end) block_t(kc, j0, std::true_type{});   // wave-uniform branch
     else block_t(kc, j0, std::false_type{});
   };
-  stream_blocks<D>(k, g, kvh, jb, je, lane, block);
+  stream_blocks<D>(kh, g.n, jb, nb, lane, block);
   // halves (lanes i, i+32 share a query row), then the 4 waves, in fixed order
 #pragma unroll
   for (int t = 0; t < TG; ++t) {
@@ -267,9 +262,10 @@ template <int D, int TG>
 __device__ __forceinline__ void pass2(const WinArgs& a, WinSmem<D, TG>& sm, int l, int kvh, int wgi) {
   constexpr int S = D / 16;
   const Geo& g = a.g;
-  const int lane = threadIdx.x & 63, hf = lane >> 5, qi = lane & 31, wv = threadIdx.x / 64;
+  const int lane = threadIdx.x & 63, hf = lane >> 5, qi = lane & 31;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
   const int64_t lg = (int64_t)l * g.Hkv + kvh;
-  const uint16_t* k = (const uint16_t*)a.k.p[l];
+  const uint16_t* kh = (const uint16_t*)a.k.p[l] + (int64_t)kvh * g.n * D;   // this KV head's keys
   const int rows = g.ntiles * 32;
   stage_q<D, TG>((const uint16_t*)a.q.p[l], g, kvh, a.tile0, sm.q);
   // row normalisers from pass 1's workgroup partials: P threads per row each merge
@@ -317,6 +313,7 @@ __device__ __forceinline__ void pass2(const WinArgs& a, WinSmem<D, TG>& sm, int 
 
   const int64_t jb = ((int64_t)wgi * (NTW / 64) + wv) * KPW;
   const int64_t je = min(g.n, jb + KPW);
+  const int nb = (int)((je - jb + 31) / 32);
   const int64_t safe_end = g.n - g.w;
   const float inv_group = 1.0f / (float)(g.G * g.w), inv_w = 1.0f / (float)g.w;
   float* A = a.A;
@@ -394,7 +391,7 @@ __device__ __forceinline__ void pass2(const WinArgs& a, WinSmem<D, TG>& sm, int 
     if (j0 + 31 <= safe_end) block_t(kc, j0, std::true_type{});   // wave-uniform branch
     else block_t(kc, j0, std::false_type{});
   };
-  stream_blocks<D>(k, g, kvh, jb, je, lane, block);
+  stream_blocks<D>(kh, g.n, jb, nb, lane, block);
 }
 
 template <int D, int TG>
