@@ -21,11 +21,12 @@
 //           partner lane is the column sum, with no atomics.
 // Launch i runs pass 2 of layer chunk i-1 next to pass 1 of chunk i, so a chunk's
 // keys are read again one chunk later, while they are still in the 256 MB MALL.
-// Key rows go straight from HBM into MFMA operand registers (16 bytes per lane:
-// lane (row i, half hf) holds d/2 contiguous elements and step s of the
-// contraction uses elements hf*d/2 + 8s .. +8, the same map for Q and K, which
-// the contraction does not depend on).  Q is staged once per workgroup in LDS in
-// fragment order, one conflict-free ds_read_b128 per fragment.
+// Key rows go straight from HBM into MFMA operand registers in the instruction's
+// own k layout: step s, lane (row i, half hf) holds elements 16s + 8hf .. +8, so
+// the two halves of a wave read adjacent 16-byte pieces of each row and a load
+// instruction touches 32 cache lines, not 64 (measured 5.9 vs 4.6 TB/s for a
+// plain K stream).  Q is staged once per workgroup in LDS in fragment order, one
+// ds_read_b128 per fragment.
 #include <type_traits>
 
 #include "common.h"
@@ -39,11 +40,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 constexpr int NTW = 256;        // threads per workgroup (4 waves)
 constexpr int MAX_TILES = 8;    // G * ceil(w/32)
 constexpr int MAX_TG = 4;       // tiles per launch
-constexpr int KPW = 256;        // keys per wave
-#ifndef KVC_WIN_CHAINS
-#define KVC_WIN_CHAINS 1
-#endif
-constexpr int CH = KVC_WIN_CHAINS;  // tiles whose MFMA chains are issued interleaved
+constexpr int KPW = 512;        // keys per wave
 constexpr int MIN_WAVES = 4096; // waves per launch that fill 256 CUs
 constexpr float LOG2E = 1.4426950408889634f;
 
@@ -81,22 +78,25 @@ __device__ __forceinline__ bf16x8 as_bf16x8(const uint4& u) {
 // every key >= n), so every prefetch is unconditional; loads issued on only some
 // paths, or re-issued by the compiler at their use (the data are read-only: the
 // memory clobber pins them), would make every block wait for its own keys.
-template <int D, typename F>
+// `prologue` (the task's Q staging and workgroup barriers, run by every wave) is
+// called after the first two blocks are requested, so their latency overlaps it.
+template <int D, typename P, typename F>
 __device__ __forceinline__ void stream_blocks(const uint16_t* kh, int64_t n, int64_t jb, int nb,
-                                              int lane, F&& block) {
+                                              int lane, P&& prologue, F&& block) {
   constexpr int S = D / 16;
-  if (nb <= 0) return;
+  if (nb <= 0) { prologue(); return; }
   const int i = lane & 31, hf = lane >> 5;
   auto load = [&](int b, bf16x8 (&kf)[S]) __attribute__((always_inline)) {
     const int64_t key = min(jb + 32 * b + i, n - 1);
-    const uint16_t* p = kh + key * D + hf * (D / 2);
+    const uint16_t* p = kh + key * D + 8 * hf;
 #pragma unroll
-    for (int st = 0; st < S; ++st) kf[st] = *reinterpret_cast<const bf16x8*>(p + 8 * st);
+    for (int st = 0; st < S; ++st) kf[st] = *reinterpret_cast<const bf16x8*>(p + 16 * st);
     asm volatile("" ::: "memory");
   };
   bf16x8 k0[S], k1[S];
   load(0, k0);
   load(min(1, nb - 1), k1);
+  prologue();
   int b = 0;
 #pragma unroll 1
   for (; b + 1 < nb; b += 2) {
@@ -117,13 +117,54 @@ __device__ __forceinline__ void stage_q(const uint16_t* q, const Geo& g, int kvh
   constexpr int S = D / 16, C = D / 8;          // steps, 16-byte chunks per row
   for (int f = threadIdx.x; f < TG * 32 * C; f += NTW) {
     const int c16 = f % C, i = (f / C) % 32, t = f / (32 * C);
-    const int hf = c16 / S, st = c16 % S;
+    const int hf = c16 & 1, st = c16 >> 1;
     const int tile = tile0 + t;
     const int head = kvh * g.G + tile / g.tph;
     const int rr = (tile % g.tph) * 32 + i;
     uint4 v = make_uint4(0, 0, 0, 0);
     if (rr < g.w) v = *reinterpret_cast<const uint4*>(q + ((int64_t)head * g.w + rr) * D + c16 * 8);
     qlds[(t * S + st) * 64 + hf * 32 + i] = v;
+  }
+}
+
+// The TG tiles of one 32-key block.  Tile t+1's Q fragment reads and MFMA chain
+// are issued inside tile t's exp2 epilogue (one scheduling region per tile), so a
+// single wave keeps the matrix cores and the vector ALU busy together instead of
+// alternating between them.  KEYS_ON_M puts the keys on the M side (pass 1: S^T),
+// else the queries (pass 2: S).  epi(t, acc) is straight-line code.
+template <int S, int TG, bool KEYS_ON_M, typename Epi>
+__device__ __forceinline__ void pipelined_tiles(const bf16x8 (&kc)[S], const uint4* qlds, int qo,
+                                                Epi&& epi) {
+  constexpr int NV = (72 + S - 1) / S;           // epilogue VALU per MFMA slot
+  constexpr int PRE = S < 4 ? S : 4;             // Q reads issued before the first MFMA
+  auto chain = [&](int t, f32x16& acc) __attribute__((always_inline)) {
+    bf16x8 q[S];
+#pragma unroll
+    for (int st = 0; st < S; ++st) q[st] = as_bf16x8(qlds[(t * S + st) * 64 + qo]);
+    acc = f32x16{};
+#pragma unroll
+    for (int st = 0; st < S; ++st)
+      acc = KEYS_ON_M ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(kc[st], q[st], acc, 0, 0, 0)
+                      : __builtin_amdgcn_mfma_f32_32x32x16_bf16(q[st], kc[st], acc, 0, 0, 0);
+  };
+  f32x16 acc[2];
+  chain(0, acc[0]);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int t = 0; t < TG; ++t) {
+    if (t + 1 < TG) chain(t + 1, acc[(t + 1) & 1]);
+    epi(t, acc[t & 1]);
+    if (t + 1 < TG) {
+      __builtin_amdgcn_sched_group_barrier(0x100, PRE, 0);      // Q reads
+      __builtin_amdgcn_sched_group_barrier(0x402, NV, 0);       // VALU / transcendental
+#pragma unroll
+      for (int i = 0; i < S; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // one MFMA
+        if (i + PRE < S) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x402, NV, 0);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -148,8 +189,10 @@ __device__ __forceinline__ void pass1(const WinArgs& a, WinSmem<D, TG>& sm, int 
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
   const int64_t lg = (int64_t)l * g.Hkv + kvh;
   const uint16_t* kh = (const uint16_t*)a.k.p[l] + (int64_t)kvh * g.n * D;   // this KV head's keys
-  stage_q<D, TG>((const uint16_t*)a.q.p[l], g, kvh, a.tile0, sm.q);
-  __syncthreads();
+  auto prologue = [&]() __attribute__((always_inline)) {
+    stage_q<D, TG>((const uint16_t*)a.q.p[l], g, kvh, a.tile0, sm.q);
+    __syncthreads();
+  };
 
   int pos[TG];                                   // window position of this lane's row
 #pragma unroll
@@ -167,39 +210,14 @@ __device__ __forceinline__ void pass1(const WinArgs& a, WinSmem<D, TG>& sm, int 
   const int64_t safe_end = g.n - g.w;            // keys <= this are seen by every row
   // one 32-key block; kc holds its key fragments
   // FULL: every key of the block is visible to every row (no mask code at all)
-  auto block_t = [&](const bf16x8 (&kc)[S], int64_t j0, auto full_t) {
+  auto block_t = [&](const bf16x8 (&kc)[S], int64_t j0, auto full_t) __attribute__((always_inline)) {
     constexpr bool full = decltype(full_t)::value;
     int qo = lane;
     asm volatile("" : "+v"(qo));                 // keep the Q reads in the loop (LDS, not VGPRs)
-#pragma unroll
-    for (int t0 = 0; t0 < TG; t0 += CH) {
-      // CH independent MFMA chains issued interleaved, then their epilogues
-      f32x16 accs[CH];
-#pragma unroll
-      for (int c = 0; c < CH; ++c) accs[c] = f32x16{};
-      // all fragment reads first, then the MFMAs: each MFMA waits only for its own
-      // read (staggered lgkmcnt) instead of a full LDS round trip per step
-      bf16x8 qf[CH][S];
-#pragma unroll
-      for (int c = 0; c < CH; ++c)
-#pragma unroll
-        for (int st = 0; st < S; ++st)
-          if (t0 + c < TG) qf[c][st] = as_bf16x8(sm.q[((t0 + c) * S + st) * 64 + qo]);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int st = 0; st < S; ++st)
-#pragma unroll
-        for (int c = 0; c < CH; ++c)
-          if (t0 + c < TG)
-            accs[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kc[st], qf[c][st], accs[c], 0, 0, 0);
-#pragma unroll
-      for (int c = 0; c < CH; ++c) {
-      const int t = t0 + c;
-      if (t >= TG) break;
-      f32x16& acc = accs[c];
-      // scores in log2 units are acc * sl2 (sl2 > 0): take the block max on the raw
-      // accumulator, then one FMA and one v_exp_f32 per element (results below
-      // 2^-126 flush to zero, which changes no sum at float32 precision)
+    // scores in log2 units are acc * sl2 (sl2 > 0): take the block max on the raw
+    // accumulator, then one FMA and one v_exp_f32 per element (results below
+    // 2^-126 flush to zero, which changes no sum at float32 precision)
+    auto epi = [&](int t, f32x16 acc) __attribute__((always_inline)) {
       float bm = -INFINITY;
       if constexpr (full) {
 #pragma unroll
@@ -223,14 +241,14 @@ __device__ __forceinline__ void pass1(const WinArgs& a, WinSmem<D, TG>& sm, int 
       for (int v = 0; v < 16; ++v) sum += __builtin_amdgcn_exp2f(fmaf(acc[v], a.sl2, -ms));
       sm_[t] = sm_[t] * __builtin_amdgcn_exp2f(m[t] - ms) + sum;
       m[t] = mn;
-      }
-    }
+    };
+    pipelined_tiles<S, TG, true>(kc, sm.q, qo, epi);
   };
   auto block = [&](const bf16x8 (&kc)[S], int64_t j0) {
     if (j0 + 31 <= safe_end) block_t(kc, j0, std::true_type{});   // wave-uniform branch
     else block_t(kc, j0, std::false_type{});
   };
-  stream_blocks<D>(kh, g.n, jb, nb, lane, block);
+  stream_blocks<D>(kh, g.n, jb, nb, lane, prologue, block);
   // halves (lanes i, i+32 share a query row), then the 4 waves, in fixed order
 #pragma unroll
   for (int t = 0; t < TG; ++t) {
@@ -267,11 +285,12 @@ __device__ __forceinline__ void pass2(const WinArgs& a, WinSmem<D, TG>& sm, int 
   const int64_t lg = (int64_t)l * g.Hkv + kvh;
   const uint16_t* kh = (const uint16_t*)a.k.p[l] + (int64_t)kvh * g.n * D;   // this KV head's keys
   const int rows = g.ntiles * 32;
-  stage_q<D, TG>((const uint16_t*)a.q.p[l], g, kvh, a.tile0, sm.q);
-  // row normalisers from pass 1's workgroup partials: P threads per row each merge
-  // every P-th partial (loads issued 8 at a time), then the P results are merged
-  // in a fixed order; +inf for padding rows and rows that see no key
-  {
+  // Q to LDS and the row normalisers from pass 1's workgroup partials: P threads
+  // per row each merge every P-th partial (loads issued 8 at a time), then the P
+  // results are merged in a fixed order; +inf for padding rows and rows that see
+  // no key
+  auto prologue = [&]() __attribute__((always_inline)) {
+    stage_q<D, TG>((const uint16_t*)a.q.p[l], g, kvh, a.tile0, sm.q);
     constexpr int R = TG * 32, P = NTW / R;
     const float2* pl = a.part + lg * (int64_t)g.nwg * rows + a.tile0 * 32;
     const int r = threadIdx.x % R, j = threadIdx.x / R;
@@ -308,8 +327,8 @@ __device__ __forceinline__ void pass2(const WinArgs& a, WinSmem<D, TG>& sm, int 
       const bool pad = ((row >> 5) % g.tph) * 32 + (row & 31) >= g.w;
       sm.c[r] = (!pad && Mt > -INFINITY) ? Mt + log2f(St) : INFINITY;
     }
-  }
-  __syncthreads();
+    __syncthreads();
+  };
 
   const int64_t jb = ((int64_t)wgi * (NTW / 64) + wv) * KPW;
   const int64_t je = min(g.n, jb + KPW);
@@ -317,37 +336,16 @@ __device__ __forceinline__ void pass2(const WinArgs& a, WinSmem<D, TG>& sm, int 
   const int64_t safe_end = g.n - g.w;
   const float inv_group = 1.0f / (float)(g.G * g.w), inv_w = 1.0f / (float)g.w;
   float* A = a.A;
-  auto block_t = [&](const bf16x8 (&kc)[S], int64_t j0, auto full_t) {
+  auto block_t = [&](const bf16x8 (&kc)[S], int64_t j0, auto full_t) __attribute__((always_inline)) {
     constexpr bool full = decltype(full_t)::value;
     const int64_t key = j0 + qi;                 // this lane's key column
-    float total = 0.f, hsum = 0.f;
     int qo = lane, co = 4 * hf;
     asm volatile("" : "+v"(qo), "+v"(co));       // keep Q and c reads in the loop
-#pragma unroll
-    for (int t0 = 0; t0 < TG; t0 += CH) {
-      f32x16 accs[CH];
-#pragma unroll
-      for (int c = 0; c < CH; ++c) accs[c] = f32x16{};
-      bf16x8 qf[CH][S];
-#pragma unroll
-      for (int c = 0; c < CH; ++c)
-#pragma unroll
-        for (int st = 0; st < S; ++st)
-          if (t0 + c < TG) qf[c][st] = as_bf16x8(sm.q[((t0 + c) * S + st) * 64 + qo]);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int st = 0; st < S; ++st)
-#pragma unroll
-        for (int c = 0; c < CH; ++c)
-          if (t0 + c < TG)
-            accs[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[c][st], kc[st], accs[c], 0, 0, 0);
-#pragma unroll
-      for (int c = 0; c < CH; ++c) {
-      const int t = t0 + c;
-      if (t >= TG) break;
-      f32x16& acc = accs[c];
-      // window row of element v: base + (8*(v/4) + v%4); the key is seen by rows
-      // rr with key - (n - w) <= rr < w, and only if key < n
+    // this lane's 16 rows of tile t: exp2(s - c_r) summed (the partner lane adds
+    // the other 16 at the end of the block); the key is seen by rows rr with
+    // key - (n - w) <= rr < w, and only if key < n
+    float hs[TG];
+    auto epi = [&](int t, const f32x16& acc) __attribute__((always_inline)) {
       const int base = ((a.tile0 + t) % g.tph) * 32 + 4 * hf;
       const int lo = (int)(key - safe_end) - base;
       const int hi = (key < g.n) ? g.w - base : -1;
@@ -364,10 +362,16 @@ __device__ __forceinline__ void pass2(const WinArgs& a, WinSmem<D, TG>& sm, int 
           colsum += e;
         }
       }
-      colsum += __shfl_xor(colsum, 32, 64);
-      total += colsum;
+      hs[t] = colsum;
+    };
+    pipelined_tiles<S, TG, false>(kc, sm.q, qo, epi);
+    float total = 0.f, hsum = 0.f;
+#pragma unroll
+    for (int t = 0; t < TG; ++t) {
+      const float cs = hs[t] + __shfl_xor(hs[t], 32, 64);
+      total += cs;
       if (a.per_head) {
-        hsum += colsum;
+        hsum += cs;
         const int tile = a.tile0 + t;
         const bool last_of_head = (t == TG - 1) || ((tile + 1) % g.tph == 0);
         if (last_of_head) {
@@ -380,7 +384,6 @@ __device__ __forceinline__ void pass2(const WinArgs& a, WinSmem<D, TG>& sm, int 
           hsum = 0.f;
         }
       }
-      }
     }
     if (!a.per_head && hf == 0 && key < g.n) {
       float* dst = A + ((int64_t)l * g.Hkv + kvh) * g.n + key;
@@ -391,7 +394,7 @@ __device__ __forceinline__ void pass2(const WinArgs& a, WinSmem<D, TG>& sm, int 
     if (j0 + 31 <= safe_end) block_t(kc, j0, std::true_type{});   // wave-uniform branch
     else block_t(kc, j0, std::false_type{});
   };
-  stream_blocks<D>(kh, g.n, jb, nb, lane, block);
+  stream_blocks<D>(kh, g.n, jb, nb, lane, prologue, block);
 }
 
 template <int D, int TG>
