@@ -9,13 +9,19 @@ gated merge).  Prints one JSON line.
 
   python bench.py [--gpus 1] [--steps 10] [--warmup 2] [--workload NAME]
                   [--no-cpu-baseline]
+  python bench.py --copy-calibration      (a plain device copy of known size, run
+                                           under rocprofv3 --pmc to scale its
+                                           FETCH_SIZE / WRITE_SIZE readings)
 
 Timing: W untimed steps, then K steps between two events on the launch stream,
 with torch.cuda.synchronize() on both sides.  Inside the timed region an event
 follows every step of the path, so each kernel's average duration is measured
 live on the stream it runs on; the roofline object is computed from that.
 The cpu_baseline leg times the float64 oracle on a bounded sample of the same
-workload (stated in the output) on this host's cores.
+workload (stated in the output) on this host's cores.  roofline.traffic is the
+measured HBM traffic of the dominant kernel per step, read from the table under
+profiles/ (rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled by the copy calibration);
+it is null when that kernel's sources no longer match the ones profiled.
 """
 from __future__ import annotations
 
@@ -54,6 +60,58 @@ def algorithmic_bytes(w, k_list):
         # V read, kept K read, K_c and V'_c written, A read, ln R written
         out["merge_gated"] = L * Hkv * n * d * e + 3 * kept * d * e + L * Hkv * n * 4 + kept * 8
     return out
+
+
+# sources whose kernels each step of the path runs (a change in any of them makes
+# an earlier traffic measurement stale)
+KERNEL_SOURCES = {
+    "topk_entropy": ["topk_entropy.hip"], "repr_distance": ["repr_distance.hip"],
+    "window_attn": ["window_attn.hip"], "fuse_scores": ["fuse_scores.hip"],
+    "select_topk": ["select_topk.hip"], "compact": ["compact.hip"],
+    "vatp_union": ["selkv.hip"], "merge_gated": ["selkv.hip"],
+}
+
+
+def source_digest(kernel):
+    import hashlib
+    csrc = os.path.join(ROOT, "kv_cache_compression_softmax_amd", "csrc")
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES.get(kernel, []) + ["common.h"]:
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    with open(os.path.join(ROOT, "include", "kvc.h"), "rb") as fh:
+        h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload, kernel):
+    """HBM bytes per step of `kernel` from profiles/hbm-traffic_<workload>.md, or
+    None if absent or measured on other sources."""
+    path = os.path.join(ROOT, "profiles", f"hbm-traffic_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    digest = source_digest(kernel)
+    with open(path) as fh:
+        for line in fh:
+            cells = [c.strip() for c in line.strip().strip("|").split("|")]
+            if len(cells) >= 6 and cells[0] == kernel and cells[1] == digest:
+                try:
+                    return int(cells[5])
+                except ValueError:
+                    return None
+    return None
+
+
+def copy_calibration():
+    """A plain copy of 2 GiB, device to device, three times (torch's copy kernel)."""
+    import torch
+    n = 1 << 29
+    a = torch.ones(n, device="cuda:0", dtype=torch.float32)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "calls": 3}))
 
 
 def window_flops(w):
@@ -137,7 +195,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="llama3.1-8b-n32768-keep20-bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this path does no cross-GPU work, so --gpus "
               f"{args.gpus} has nothing to measure (a multi-GPU run would shard layers or KV "
@@ -209,7 +271,7 @@ def main():
                    if len(set(k_list)) == 1 else "adaptive", "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": None},
+                     "traffic": measured_traffic(w.name, dom), "alg_bytes": abytes[dom]},
         "path_roofline": {"alg_bytes": path_bytes,
                           "achieved_GBps": round(path_bytes / (ms * 1e-3) / 1e9, 1),
                           "frac": round(path_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)},
