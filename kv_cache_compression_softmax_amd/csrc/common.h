@@ -49,6 +49,16 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return (uint16_t)(u >> 16);
 }
 
+// 16-byte load marked non-temporal, for data read exactly once: a plain streaming
+// read reaches up to 7.1 TB/s this way against 6.2-6.3 TB/s with ordinary loads.
+// Not for data read again soon (it loses the MALL: window attention's second pass
+// over K slows from 1.03 to 1.47 ms with it).
+__device__ __forceinline__ uint4 ld_stream(const void* p) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(t.x, t.y, t.z, t.w);
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);

@@ -73,7 +73,7 @@ repr_distance_vec(ConstPtrs h, const T* __restrict__ hf, int L, int64_t n, int64
 #pragma unroll
     for (int v = 0; v < V; ++v) {
       const int vi = v * kWave + lane;
-      if (FULL || vi < nvec) a[v] = *reinterpret_cast<const uint4*>(row + (int64_t)vi * W);
+      if (FULL || vi < nvec) a[v] = ld_stream(row + (int64_t)vi * W);
       else a[v] = make_uint4(0u, 0u, 0u, 0u);      // contributes 0 to every sum
     }
     asm volatile("" ::: "memory");

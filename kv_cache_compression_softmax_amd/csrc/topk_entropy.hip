@@ -290,7 +290,7 @@ topk_entropy_kernel(const T* __restrict__ logits, int64_t rows, int64_t vocab, i
     for (int v = 0; v < NV; ++v) {
       const T* p = row + c * STEP + (int64_t)(v * 64 + lane) * VEC;
       if constexpr (ALIGNED) {
-        buf[v] = *reinterpret_cast<const uint4*>(p);
+        buf[v] = ld_stream(p);
       } else {
         const Raw* r = reinterpret_cast<const Raw*>(p);
         Raw e[VEC];
