@@ -34,8 +34,7 @@ namespace kvc {
 namespace {
 
 constexpr int NT = 256;      // 4 waves = 4 rows per workgroup
-constexpr int NV = 4;        // 16-byte vectors per lane per step
-constexpr int RESEL = 2048;  // list length that triggers a re-select (>= k rounded up)
+constexpr int RESEL = 1536;  // list length that triggers a re-select (>= k rounded up)
 
 typedef short s16x2 __attribute__((ext_vector_type(2)));
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
@@ -44,6 +43,7 @@ template <typename T> struct Tr;
 template <> struct Tr<uint16_t> {                 // bf16 bit patterns
   using Raw = uint16_t;
   static constexpr int VEC = 8;
+  static constexpr int NV = 2;                    // 16-byte vectors per lane per step
   static constexpr int DIGITS = 2;
   static constexpr Raw kMin = 0xffffu;            // bit pattern of the smallest key (0)
   __device__ static uint32_t key(Raw r) { return bf16_key(r); }
@@ -76,6 +76,7 @@ template <> struct Tr<uint16_t> {                 // bf16 bit patterns
 template <> struct Tr<float> {
   using Raw = uint32_t;
   static constexpr int VEC = 4;
+  static constexpr int NV = 4;
   static constexpr int DIGITS = 4;
   static constexpr Raw kMin = 0xffffffffu;
   __device__ static uint32_t key(Raw r) { return f32_key(__uint_as_float(r)); }
@@ -236,7 +237,10 @@ topk_entropy_kernel(const T* __restrict__ logits, int64_t rows, int64_t vocab, i
                     int k, float* __restrict__ H) {
   using Raw = typename Tr<T>::Raw;
   constexpr int VEC = Tr<T>::VEC;
+  constexpr int NV = Tr<T>::NV;
   constexpr int STEP = 64 * NV * VEC;            // elements per wave per step
+  // the first select takes the first step alone, which must hold k elements
+  static_assert(STEP >= KVC_MAX_TOPK_ENTROPY, "a step holds at least the largest k");
   static_assert(CAP == RESEL + STEP && CAP % VEC == 0, "list capacity");
   __shared__ WaveSmem<Raw, CAP> smem[NT / 64];
   const int lane = threadIdx.x & 63, wv = threadIdx.x / 64;
@@ -356,7 +360,7 @@ topk_entropy_kernel(const T* __restrict__ logits, int64_t rows, int64_t vocab, i
 template <typename T>
 void launch(const void* logits, int64_t rows, int64_t vocab, int64_t stride, int k, float* H,
             hipStream_t s) {
-  constexpr int CAP = RESEL + 64 * NV * Tr<T>::VEC;
+  constexpr int CAP = RESEL + 64 * Tr<T>::NV * Tr<T>::VEC;
   static_assert(RESEL >= KVC_MAX_TOPK_ENTROPY + 8, "a re-selected list must fit below RESEL");
   const unsigned grid = (unsigned)((rows + NT / 64 - 1) / (NT / 64));
   // every row start is 16-byte aligned iff the base and the row pitch are
