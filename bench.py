@@ -139,6 +139,7 @@ def cpu_baseline(w, inp, budget_s=20.0):
         return t.numpy().astype(np.float64)
 
     L, n = w.layers, w.n
+    t_start = time.perf_counter()
     if w.method == "infokv":
         rows = min(n, 256)
         lg = f64(inp["logits"][:rows])
@@ -185,7 +186,8 @@ def cpu_baseline(w, inp, budget_s=20.0):
                   f"last {nn} of {n} tokens of layer {lay}, scaled linearly to {n} tokens and "
                   f"{L} layers")
     return {"value": n / total, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": sample, "est_step_s": total}
+            "sample": sample, "sample_s": round(time.perf_counter() - t_start, 2),
+            "est_step_s": total}
 
 
 def main():

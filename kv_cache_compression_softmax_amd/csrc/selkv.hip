@@ -46,36 +46,65 @@ template <> struct El<float> {
 };
 
 // ------------------------------------------------------------- VATP + union
-constexpr int NT = 256;
+constexpr int NT = 256;         // 4 waves
+constexpr int VNL = 8;          // most V loads per lane (all issued before any is used)
 
+// One wave per min(VNL, LG) * 64 / LG rows (at most 64) of one (layer, KV head):
+// the rows' V are read
+// with 16-byte loads (LG lanes per row, non-temporal: the values are not reread
+// before the merge pass evicts them), squared norms are reduced per row, then
+// lane q takes row q: it reads the group's G attention values of its row
+// (coalesced across lanes) and writes U = max_h A_h * |v| and the group mean A_g.
 template <typename T, int LG>
 __global__ void __launch_bounds__(NT)
 vatp_union_kernel(const float* __restrict__ A_hq, ConstPtrs V, int Hq, int Hkv, int64_t n, int d,
-                  int64_t nblk, float* __restrict__ U, float* __restrict__ Ag) {
+                  int64_t nchunk, int64_t nwave, float* __restrict__ U, float* __restrict__ Ag) {
   constexpr int W = El<T>::N;
-  constexpr int RPI = NT / LG;                  // rows per block iteration
-  const int64_t bid = blockIdx.x;
-  const int64_t jblk = bid % nblk;
-  const int g = (int)((bid / nblk) % Hkv);
-  const int l = (int)(bid / (nblk * Hkv));
+  constexpr int RPI = 64 / LG;                  // rows per load instruction
+  constexpr int NL = LG < VNL ? LG : VNL;       // loads per lane
+  constexpr int RW = RPI * NL;                  // rows per wave (at most 64)
+  static_assert(RW <= 64, "one lane per row in the attention phase");
+  const int lane = threadIdx.x & 63;
+  const int64_t wid = (int64_t)blockIdx.x * (NT / 64) + threadIdx.x / 64;
+  if (wid >= nwave) return;                     // waves are independent (no barriers)
+  const int64_t chunk = wid % nchunk;
+  const int g = (int)((wid / nchunk) % Hkv);
+  const int l = (int)(wid / (nchunk * Hkv));
   const int G = Hq / Hkv;
-  const int r = threadIdx.x / LG, c = threadIdx.x % LG;
+  const int rg = lane / LG, c = lane % LG;
   const T* Vg = (const T*)V.p[l] + (int64_t)g * n * d;
-  const float* Ah = A_hq + ((int64_t)l * Hq + (int64_t)g * G) * n;
-  const int64_t j = jblk * RPI + r;
-  float ss = 0.f;
-  if (j < n) {
-    float x[W];
-    El<T>::unpack(*reinterpret_cast<const uint4*>(Vg + j * d + c * W), x);
+  const int64_t j0 = chunk * RW;
+  uint4 raw[NL];
 #pragma unroll
-    for (int e = 0; e < W; ++e) ss += x[e] * x[e];
+  for (int u = 0; u < NL; ++u) {
+    const int64_t j = min(j0 + u * RPI + rg, n - 1);     // rows past n: read, never used
+    raw[u] = ld_stream(Vg + j * d + c * W);
   }
-  ss = group_sum<LG>(ss);
-  if (c == 0 && j < n) {
-    const float vn = sqrtf(ss);
+  float ss[NL];
+#pragma unroll
+  for (int u = 0; u < NL; ++u) {
+    float x[W];
+    El<T>::unpack(raw[u], x);
+    float a = 0.f;
+#pragma unroll
+    for (int e = 0; e < W; ++e) a += x[e] * x[e];
+    ss[u] = group_sum<LG>(a);
+  }
+  // row q = u * RPI + r lives in register u of the lanes of row group r
+  const int q = lane;
+  float s2 = 0.f;
+#pragma unroll
+  for (int u = 0; u < NL; ++u) {
+    const float v = __shfl(ss[u], (q % RPI) * LG, 64);
+    s2 = (q / RPI == u) ? v : s2;
+  }
+  const int64_t j = j0 + q;
+  if (q < RW && j < n) {
+    const float vn = sqrtf(s2);
+    const float* Ah = A_hq + ((int64_t)l * Hq + (int64_t)g * G) * n + j;
     float mx = -INFINITY, sum = 0.f;
     for (int h = 0; h < G; ++h) {
-      const float a = Ah[(int64_t)h * n + j];
+      const float a = Ah[(int64_t)h * n];
       mx = fmaxf(mx, a * vn);
       sum += a;
     }
@@ -104,10 +133,12 @@ struct MergeTables {
   I64s task0;     // first bucket task of each layer (tasks of a layer = Hkv * nbuckets)
 };
 
+// Any bucket size: one wave per bucket, binary searches and a walk of the kept
+// list (used for buckets above 64 tokens).
 template <typename T, int LG>
 __global__ void __launch_bounds__(NTM)
-merge_kernel(MergeTables t, int lc, const float* __restrict__ Ag, int Hkv, int64_t n, int d,
-             int bucket, int64_t nbuckets, int64_t ntask) {
+merge_kernel_any(MergeTables t, int lc, const float* __restrict__ Ag, int Hkv, int64_t n, int d,
+                 int bucket, int64_t nbuckets, int64_t ntask) {
   constexpr int W = El<T>::N;
   constexpr int RPP = 64 / LG;                   // rows per wave pass
   const int lane = threadIdx.x & 63;
@@ -211,10 +242,198 @@ merge_kernel(MergeTables t, int lc, const float* __restrict__ Ag, int Hkv, int64
   }
 }
 
+// First index s in [0, m) with a[s] >= x (a ascending), by a 64-way search: each
+// round probes 64 evenly spaced entries at once, so 25600 kept indices take three
+// rounds of parallel loads instead of fifteen dependent ones.
+__device__ __forceinline__ int64_t wave_lower_bound(const int32_t* a, int64_t m, int64_t x, int lane) {
+  int64_t lo = 0, hi = m;                        // the answer lies in [lo, hi]
+  while (hi - lo > 64) {
+    const int64_t step = (hi - lo + 63) / 64;
+    const int64_t p = lo + (int64_t)lane * step;
+    const uint64_t below = __ballot(p < hi && a[p] < x);   // a prefix of the lanes
+    const int cnt = __builtin_popcountll(below);
+    if (cnt == 0) return lo;                     // a[lo] >= x
+    const int64_t nlo = lo + (int64_t)(cnt - 1) * step + 1;
+    hi = min(hi, lo + (int64_t)cnt * step);
+    lo = nlo;
+  }
+  const int64_t p = lo + lane;
+  return lo + __builtin_popcountll(__ballot(p < hi && a[p] < x));
+}
+
+// Buckets of at most 64 tokens: one wave per bucket.  The bucket's V rows are
+// requested first (they do not depend on the kept list), the kept indices of the
+// bucket come from one 64-way search and one coalesced load of the next 64 kept
+// slots, and the kept rows form a 64-bit mask, so each kept row's output slot is
+// a popcount.  Target (largest A_g, ties to the lower index), gates, sums and
+// outputs are as in merge_kernel_any, in the same order.
+template <typename T, int LG>
+__global__ void __launch_bounds__(NTM)
+merge_kernel(MergeTables t, int lc, const float* __restrict__ Ag, int Hkv, int64_t n, int d,
+             int bucket, int64_t nbuckets, int64_t ntask) {
+  constexpr int W = El<T>::N;
+  constexpr int RPP = 64 / LG;                   // rows per wave pass
+  constexpr int NP = 64 / RPP;                   // passes over a 64-row bucket
+  constexpr int KBATCH = 4;                      // K copy passes issued together
+  const int lane = threadIdx.x & 63;
+  const int64_t task = (int64_t)blockIdx.x * (NTM / 64) + threadIdx.x / 64;
+  if (task >= ntask) return;                     // waves are independent (no barriers)
+  int l = 0;
+  while (l + 1 < lc && t.task0.v[l + 1] <= task) ++l;
+  const int64_t local = task - t.task0.v[l];
+  const int g = (int)(local / nbuckets);
+  const int64_t b0 = (local % nbuckets) * bucket;
+  const int64_t b1 = min(n, b0 + bucket);
+  const int64_t m = t.m.v[l];
+  const int32_t* ip = (const int32_t*)t.idx.p[l] + (int64_t)g * m;
+  const float* A = Ag + ((int64_t)l * Hkv + g) * n;
+  const T* Vg = (const T*)t.V.p[l] + (int64_t)g * n * d;
+  const T* Kg = (const T*)t.K.p[l] + (int64_t)g * n * d;
+  T* Vo = (T*)t.Vo.p[l] + (int64_t)g * m * d;
+  T* Ko = (T*)t.Ko.p[l] + (int64_t)g * m * d;
+  float* lR = (float*)t.logR.p[l] + (int64_t)g * m;
+  const int rg = lane / LG, c = lane % LG;
+
+  // the bucket's V rows (rows past b1 are clamped to b1 - 1: read, never used)
+  uint4 raw[NP];
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    const int64_t e = min(b0 + p * RPP + rg, b1 - 1);
+    raw[p] = *reinterpret_cast<const uint4*>(Vg + e * d + c * W);
+  }
+  // kept slots of the bucket: [lo, lo + nk), lane s holding slot lo + s
+  const int64_t lo = wave_lower_bound(ip, m, b0, lane);
+  const int64_t kid = lo + lane < m ? ip[lo + lane] : INT64_MAX;
+  const bool kin = kid < b1;
+  const int nk = __builtin_popcountll(__ballot(kin));
+  if (nk == 0) return;                           // no kept token: evicted tokens dropped
+  uint64_t rowmask = kin ? (1ull << (kid - b0)) : 0ull;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) rowmask |= __shfl_xor(rowmask, o, 64);
+
+  // A of the kept tokens and K of the first KBATCH * RPP kept rows, requested
+  // together (one round trip)
+  const float av = kin ? A[kid] : -INFINITY;
+  uint4 kr[KBATCH];
+#pragma unroll
+  for (int q = 0; q < KBATCH; ++q) {
+    const int s = min(q * RPP + rg, nk - 1);
+    const int64_t src = __shfl(kid, s, 64);
+    kr[q] = *reinterpret_cast<const uint4*>(Kg + src * d + c * W);
+  }
+  // merge target: the kept token with the largest A, ties to the lower index
+  float bv = av;
+  int bs = kin ? lane : 64;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const float ov = __shfl_xor(bv, o, 64);
+    const int os = __shfl_xor(bs, o, 64);
+    if (ov > bv || (ov == bv && os < bs)) { bv = ov; bs = os; }
+  }
+  // every lane holds the same winner; the clamp only guards against NaN scores
+  const int wl = bs < nk ? bs : 0;
+  const int64_t ts = lo + wl, tt = __shfl(kid, wl, 64);
+  const float At = __shfl(av, wl, 64);
+
+  // K of the kept rows: the first batch is in flight already
+#pragma unroll
+  for (int q = 0; q < KBATCH; ++q) {
+    const int s = min(q * RPP + rg, nk - 1);     // clamped lanes rewrite the last row
+    *reinterpret_cast<uint4*>(Ko + (lo + s) * d + c * W) = kr[q];
+  }
+  // more kept rows than a batch; the loop is wave-uniform so that every lane the
+  // shuffle reads from is active
+  for (int s0 = KBATCH * RPP; s0 < nk; s0 += RPP) {
+    const int s = min(s0 + rg, nk - 1);
+    const int64_t src = __shfl(kid, s, 64);
+    *reinterpret_cast<uint4*>(Ko + (lo + s) * d + c * W) =
+        *reinterpret_cast<const uint4*>(Kg + src * d + c * W);
+  }
+
+  // the target's V row is one of the bucket rows already in registers: pass
+  // rt / RPP (wave-uniform), lanes of row group rt % RPP
+  const int rt = (int)(tt - b0);
+  const int pt = __builtin_amdgcn_readfirstlane(rt / RPP);
+  uint4 tv = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    uint32_t mk = p == pt ? ~0u : 0u;
+    asm volatile("" : "+v"(mk));                 // masks and ORs, not an indexed array
+    tv.x |= raw[p].x & mk; tv.y |= raw[p].y & mk; tv.z |= raw[p].z & mk; tv.w |= raw[p].w & mk;
+  }
+  const int tsrc = (rt % RPP) * LG + c;
+  tv.x = __shfl(tv.x, tsrc, 64); tv.y = __shfl(tv.y, tsrc, 64);
+  tv.z = __shfl(tv.z, tsrc, 64); tv.w = __shfl(tv.w, tsrc, 64);
+  float vt[W];
+  El<T>::unpack(tv, vt);
+  float nt2 = 0.f;
+#pragma unroll
+  for (int e = 0; e < W; ++e) nt2 += vt[e] * vt[e];
+  nt2 = group_sum<LG>(nt2);
+  const float nt = sqrtf(nt2);
+
+  float num[W];
+#pragma unroll
+  for (int e = 0; e < W; ++e) num[e] = 0.f;
+  float den = 0.f;
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    const int r = p * RPP + rg;                  // row within the bucket
+    const int64_t e = b0 + r;
+    if (e >= b1) continue;
+    if ((rowmask >> r) & 1ull) {                 // kept: copy its V (the target is merged below)
+      if (e != tt) {
+        const int64_t slot = lo + __builtin_popcountll(rowmask & ((1ull << r) - 1ull));
+        *reinterpret_cast<uint4*>(Vo + slot * d + c * W) = raw[p];
+        if (c == 0) lR[slot] = 0.f;
+      }
+      continue;
+    }
+    float ve[W];
+    El<T>::unpack(raw[p], ve);
+    float dot = 0.f, ne2 = 0.f;
+#pragma unroll
+    for (int i = 0; i < W; ++i) { dot += ve[i] * vt[i]; ne2 += ve[i] * ve[i]; }
+    dot = group_sum<LG>(dot);
+    ne2 = group_sum<LG>(ne2);
+    const float nd = sqrtf(ne2) * nt;
+    const float gate = nd > 0.f ? fmaxf(dot / nd, 0.f) : 0.f;
+    const float wgt = gate * A[e];
+#pragma unroll
+    for (int i = 0; i < W; ++i) num[i] += wgt * ve[i];
+    den += wgt;
+  }
+  // sum the row groups (lanes with the same chunk c)
+#pragma unroll
+  for (int o = LG; o < 64; o <<= 1) {
+#pragma unroll
+    for (int i = 0; i < W; ++i) num[i] += __shfl_xor(num[i], o, 64);
+    den += __shfl_xor(den, o, 64);
+  }
+  if (rg == 0) {
+    float out[W];
+    float lr = 0.f;
+    if (den > 0.f) {
+      const float inv = 1.0f / (At + den);
+#pragma unroll
+      for (int i = 0; i < W; ++i) out[i] = (At * vt[i] + num[i]) * inv;
+      lr = log1pf(den / At);
+      *reinterpret_cast<uint4*>(Vo + ts * d + c * W) = El<T>::pack(out);
+    } else {
+      *reinterpret_cast<uint4*>(Vo + ts * d + c * W) = tv;
+    }
+    if (c == 0) lR[ts] = lr;
+  }
+}
+
 template <typename T>
-bool launch_vatp(int LG, dim3 grid, hipStream_t s, const float* A_hq, const ConstPtrs& V, int Hq,
-                 int Hkv, int64_t n, int d, int64_t nblk, float* U, float* Ag) {
-#define KVC_V(LGV) hipLaunchKernelGGL((vatp_union_kernel<T, LGV>), grid, dim3(NT), 0, s, A_hq, V, Hq, Hkv, n, d, nblk, U, Ag)
+bool launch_vatp(int LG, int lc, hipStream_t s, const float* A_hq, const ConstPtrs& V, int Hq,
+                 int Hkv, int64_t n, int d, float* U, float* Ag) {
+  const int64_t rw = (int64_t)(64 / LG) * (LG < VNL ? LG : VNL);
+  const int64_t nchunk = (n + rw - 1) / rw;
+  const int64_t nwave = (int64_t)lc * Hkv * nchunk;
+  const dim3 grid((unsigned)((nwave + NT / 64 - 1) / (NT / 64)));
+#define KVC_V(LGV) hipLaunchKernelGGL((vatp_union_kernel<T, LGV>), grid, dim3(NT), 0, s, A_hq, V, Hq, Hkv, n, d, nchunk, nwave, U, Ag)
   switch (LG) {
     case 4: KVC_V(4); return true;
     case 8: KVC_V(8); return true;
@@ -228,7 +447,15 @@ bool launch_vatp(int LG, dim3 grid, hipStream_t s, const float* A_hq, const Cons
 template <typename T>
 bool launch_merge(int LG, dim3 grid, hipStream_t s, const MergeTables& t, int lc, const float* Ag,
                   int Hkv, int64_t n, int d, int bucket, int64_t nbuckets, int64_t ntask) {
-#define KVC_M(LGV) hipLaunchKernelGGL((merge_kernel<T, LGV>), grid, dim3(NTM), 0, s, t, lc, Ag, Hkv, n, d, bucket, nbuckets, ntask)
+#define KVC_M(LGV)                                                                                \
+  do {                                                                                            \
+    if (bucket <= 64)                                                                             \
+      hipLaunchKernelGGL((merge_kernel<T, LGV>), grid, dim3(NTM), 0, s, t, lc, Ag, Hkv, n, d,     \
+                         bucket, nbuckets, ntask);                                                \
+    else                                                                                          \
+      hipLaunchKernelGGL((merge_kernel_any<T, LGV>), grid, dim3(NTM), 0, s, t, lc, Ag, Hkv, n, d, \
+                         bucket, nbuckets, ntask);                                                \
+  } while (0)
   switch (LG) {
     case 4: KVC_M(4); return true;
     case 8: KVC_M(8); return true;
@@ -263,18 +490,18 @@ extern "C" int kvc_vatp_union(const float* A_hq, const void* const* V, int dtype
   KVC_REQUIRE(lg_ok(d, dtype, &LG), "kvc_vatp_union: need d * elsize in {64, 128, 256, 512} bytes");
   for (int l = 0; l < L; ++l)
     KVC_REQUIRE(V[l] && (uintptr_t)V[l] % 16 == 0, "kvc_vatp_union: V[%d] null or not 16-byte aligned", l);
+  KVC_REQUIRE((int64_t)kLayersPerLaunch * Hkv * ((n + 31) / 32) / 4 <= 0x7fffffffLL,
+              "kvc_vatp_union: grid too large");
   hipStream_t s = as_stream(stream);
-  const int64_t nblk = (n + NT / LG - 1) / (NT / LG);
   for (int l0 = 0; l0 < L; l0 += kLayersPerLaunch) {
     const int lc = min(kLayersPerLaunch, L - l0);
     ConstPtrs vt{};
     for (int i = 0; i < lc; ++i) vt.p[i] = V[l0 + i];
-    const dim3 grid((unsigned)((int64_t)lc * Hkv * nblk));
     const int64_t off = (int64_t)l0 * Hkv * n;
     if (dtype == KVC_BF16)
-      launch_vatp<uint16_t>(LG, grid, s, A_hq + (int64_t)l0 * Hq * n, vt, Hq, Hkv, n, d, nblk, U_out + off, Ag_out + off);
+      launch_vatp<uint16_t>(LG, lc, s, A_hq + (int64_t)l0 * Hq * n, vt, Hq, Hkv, n, d, U_out + off, Ag_out + off);
     else
-      launch_vatp<float>(LG, grid, s, A_hq + (int64_t)l0 * Hq * n, vt, Hq, Hkv, n, d, nblk, U_out + off, Ag_out + off);
+      launch_vatp<float>(LG, lc, s, A_hq + (int64_t)l0 * Hq * n, vt, Hq, Hkv, n, d, U_out + off, Ag_out + off);
   }
   return launch_status("kvc_vatp_union");
 }
