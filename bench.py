@@ -119,9 +119,11 @@ def window_flops(w):
     return 2 * 2 * w.layers * w.heads_q * w.window * w.n * w.head_dim
 
 
-def cpu_baseline(w, inp, budget_s=20.0):
-    """The oracle, as it stands, on a bounded sample of the same workload; the
-    per-component times are scaled to the whole step."""
+def cpu_baseline(w, inp, budget_s=15.0):
+    """The oracle, as it stands, on a bounded sample of the same workload: whole
+    chunks of the step are run until about `budget_s` seconds of CPU work are
+    spent, and each component's time is scaled by the share of the step its
+    chunks covered."""
     import numpy as np
     import torch
     from oracle import infokv, precision, selkv
@@ -141,50 +143,66 @@ def cpu_baseline(w, inp, budget_s=20.0):
     L, n = w.layers, w.n
     t_start = time.perf_counter()
     if w.method == "infokv":
-        rows = min(n, 256)
-        lg = f64(inp["logits"][:rows])
-        t0 = time.perf_counter()
-        H = infokv.topk_entropy(lg, w.topk_entropy)
-        t_h = (time.perf_counter() - t0) * n / rows
-        hf = f64(inp["h_final"][:rows])
-        hl = [f64(inp["h"][l][:rows]) for l in range(L)]
-        t0 = time.perf_counter()
-        Ds = [infokv.repr_distance(hl[l], hf, w.tau) for l in range(L)]
-        t_d = (time.perf_counter() - t0) * n / rows
-        lay = L // 2
-        q, k = f64(inp["q_win"][lay]), f64(inp["k"][lay])
-        t0 = time.perf_counter()
-        A = infokv.window_attention(q, k)
-        t_a = (time.perf_counter() - t0) * L
-        Dn = np.resize(Ds[lay], n)
-        Hn = np.resize(H, n)
+        # a chunk: 256 more logits rows, the same rows of every layer's hidden
+        # states, and one more layer's window attention, fuse, select and gather
         kk = infokv.uniform_budget(w.keep_fraction, n) if not w.adaptive_fraction else \
             w.adaptive_total() // L
-        t0 = time.perf_counter()
-        S, _, _, _ = infokv.fuse_scores(A, Dn, Hn, w.alpha_fuse)
-        idx = infokv.select_topk(S.astype(np.float32), kk, w.window)
-        t_s = (time.perf_counter() - t0) * L
-        kb = inp["k"][lay].cpu().view(torch.int16).numpy()
-        vb = inp["v"][lay].cpu().view(torch.int16).numpy()
-        t0 = time.perf_counter()
-        infokv.compact(kb, vb, idx)
-        t_c = (time.perf_counter() - t0) * L
-        total = t_h + t_d + t_a + t_s + t_c
-        sample = (f"oracle on {rows} of {n} logits rows and hidden-state rows (all {L} layers), "
-                  f"window attention + fuse + select + gather of layer {lay} of {L}; each part "
+        rows_step = 256
+        t_h = t_d = t_l = 0.0
+        rows = layers = 0
+        while time.perf_counter() - t_start < budget_s and (rows < n or layers < L):
+            if rows < n:
+                r0, r1 = rows, min(n, rows + rows_step)
+                lg = f64(inp["logits"][r0:r1])
+                t0 = time.perf_counter()
+                H = infokv.topk_entropy(lg, w.topk_entropy)
+                t_h += time.perf_counter() - t0
+                del lg
+                hf = f64(inp["h_final"][r0:r1])
+                hl = [f64(inp["h"][l][r0:r1]) for l in range(L)]
+                t0 = time.perf_counter()
+                Ds = [infokv.repr_distance(hl[l], hf, w.tau) for l in range(L)]
+                t_d += time.perf_counter() - t0
+                del hl, hf
+                rows = r1
+            if layers < L:
+                lay = layers
+                q, k = f64(inp["q_win"][lay]), f64(inp["k"][lay])
+                kb = inp["k"][lay].cpu().view(torch.int16).numpy()
+                vb = inp["v"][lay].cpu().view(torch.int16).numpy()
+                # D and H over the whole row set are not all computed yet: the
+                # sampled rows' values are tiled to length n (only the time of
+                # fuse and select matters here, and neither depends on values)
+                Dn, Hn = np.resize(Ds[lay % len(Ds)], n), np.resize(H, n)
+                t0 = time.perf_counter()
+                A = infokv.window_attention(q, k)
+                S, _, _, _ = infokv.fuse_scores(A, Dn, Hn, w.alpha_fuse)
+                idx = infokv.select_topk(S.astype(np.float32), kk, w.window)
+                infokv.compact(kb, vb, idx)
+                t_l += time.perf_counter() - t0
+                del q, k, kb, vb
+                layers += 1
+        total = t_h * n / rows + t_d * n / rows + t_l * L / layers
+        sample = (f"oracle run for {time.perf_counter() - t_start:.1f} s: top-k entropy and "
+                  f"representation distance on {rows} of {n} token rows (all {L} layers), window "
+                  f"attention + fuse + select + gather on {layers} of {L} layers; each part "
                   f"scaled by rows or layers to the whole step")
     else:
-        lay = L // 2
-        nn = min(n, 16384)
-        q = f64(inp["q_win"][lay])
-        k = f64(inp["k"][lay][:, n - nn:])
-        v = f64(inp["v"][lay][:, n - nn:])
-        t0 = time.perf_counter()
-        selkv.selkv_layer(q, k, v, int(w.keep_fraction * nn), w.window, w.bucket)
-        total = (time.perf_counter() - t0) * L * (n / nn) ** 1.0
-        sample = (f"oracle SelKV layer (attention, union, select, route, gate, merge) on the "
-                  f"last {nn} of {n} tokens of layer {lay}, scaled linearly to {n} tokens and "
-                  f"{L} layers")
+        # a chunk: one whole layer (attention, union, select, route, gate, merge)
+        t_l = 0.0
+        layers = 0
+        while layers < L and (layers == 0 or time.perf_counter() - t_start < budget_s):
+            lay = layers
+            q, k, v = f64(inp["q_win"][lay]), f64(inp["k"][lay]), f64(inp["v"][lay])
+            t0 = time.perf_counter()
+            selkv.selkv_layer(q, k, v, int(w.keep_fraction * n), w.window, w.bucket)
+            t_l += time.perf_counter() - t0
+            del q, k, v
+            layers += 1
+        total = t_l * L / layers
+        sample = (f"oracle run for {time.perf_counter() - t_start:.1f} s: the SelKV layer "
+                  f"(attention, union, select, route, gate, merge) on all {n} tokens of {layers} "
+                  f"of {L} layers, scaled by layers to the whole step")
     return {"value": n / total, "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": sample, "sample_s": round(time.perf_counter() - t_start, 2),
             "est_step_s": total}
