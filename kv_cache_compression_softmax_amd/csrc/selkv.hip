@@ -12,6 +12,8 @@
 //
 // Both kernels are bound by the V stream.  Rows are read as 16-byte lanes, LG
 // lanes per row (LG = row bytes / 16), so a wave covers 64/LG rows per load.
+#include <type_traits>
+
 #include "common.h"
 
 namespace kvc {
@@ -242,41 +244,77 @@ merge_kernel_any(MergeTables t, int lc, const float* __restrict__ Ag, int Hkv, i
   }
 }
 
-// First index s in [0, m) with a[s] >= x (a ascending), by a 64-way search: each
-// round probes 64 evenly spaced entries at once, so 25600 kept indices take three
-// rounds of parallel loads instead of fifteen dependent ones.
-__device__ __forceinline__ int64_t wave_lower_bound(const int32_t* a, int64_t m, int64_t x, int lane) {
-  int64_t lo = 0, hi = m;                        // the answer lies in [lo, hi]
-  while (hi - lo > 64) {
-    const int64_t step = (hi - lo + 63) / 64;
-    const int64_t p = lo + (int64_t)lane * step;
-    const uint64_t below = __ballot(p < hi && a[p] < x);   // a prefix of the lanes
-    const int cnt = __builtin_popcountll(below);
-    if (cnt == 0) return lo;                     // a[lo] >= x
+// Kept slots of one bucket, in two steps.  search_kept narrows [lo, hi], the range
+// that holds the first index s in [0, m) with a[s] >= x (a ascending, m >= 1), to
+// at most 64 entries: the first round probes 128 evenly spaced entries at once (2
+// per lane), rounds of 64 follow while needed.  The caller then loads the
+// 128-entry window a[lo .. lo + 127], and finish_kept takes from it both the exact
+// first slot and the 64 entries after it.  For 25600 kept indices that is three
+// dependent round trips, against fifteen for a binary search and one more for
+// the entries.  (Scattered probes are costly: with 512 in the first round, one
+// round trip fewer, the merge ran 12% slower.)
+__device__ __forceinline__ void search_kept(const int32_t* a, int64_t m, int64_t x, int lane,
+                                            int64_t& lo, int64_t& hi) {
+  lo = 0; hi = m;
+  // one probe round: probe k (0 <= k < 64 * U) at lo + k * step; the probes below
+  // x form a prefix in k.  Loads are unconditional (clamped into [lo, hi)) so that
+  // all U of a lane are in flight together.
+  auto round = [&](auto U_t) __attribute__((always_inline)) {
+    constexpr int U = decltype(U_t)::value;
+    const int64_t step = (hi - lo + 64 * U - 1) / (64 * U);
+    int v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = a[min(lo + (int64_t)(64 * u + lane) * step, hi - 1)];
+    int cnt = 0;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t p = lo + (int64_t)(64 * u + lane) * step;
+      cnt += __builtin_popcountll(__ballot(p < hi && v[u] < x));
+    }
+    if (cnt == 0) { hi = lo; return; }           // a[lo] >= x
     const int64_t nlo = lo + (int64_t)(cnt - 1) * step + 1;
     hi = min(hi, lo + (int64_t)cnt * step);
     lo = nlo;
-  }
-  const int64_t p = lo + lane;
-  return lo + __builtin_popcountll(__ballot(p < hi && a[p] < x));
+  };
+  if (hi - lo > 64) round(std::integral_constant<int, 2>{});
+  while (hi - lo > 64) round(std::integral_constant<int, 1>{});
 }
 
-// Buckets of at most 64 tokens: one wave per bucket.  The bucket's V rows are
-// requested first (they do not depend on the kept list), the kept indices of the
-// bucket come from one 64-way search and one coalesced load of the next 64 kept
-// slots, and the kept rows form a 64-bit mask, so each kept row's output slot is
-// a popcount.  Target (largest A_g, ties to the lower index), gates, sums and
-// outputs are as in merge_kernel_any, in the same order.
+// w0 = a[lo + lane], w1 = a[lo + 64 + lane] (clamped loads).  Returns the first
+// slot; lane s receives a[first + s], INT64_MAX past m.
+__device__ __forceinline__ int64_t finish_kept(int64_t m, int x, int lane, int64_t lo,
+                                               int64_t hi, int w0, int w1, int64_t& out) {
+  // 32-bit compare: a widening of w0 would be placed right after its load, and
+  // wait for it there
+  const int off = __builtin_popcountll(__ballot(lo + lane < hi && w0 < x));
+  const int src = (off + lane) & 63;
+  const int e0 = __shfl(w0, src, 64), e1 = __shfl(w1, src, 64);
+  const int64_t first = lo + off;
+  out = first + lane < m ? (int64_t)(off + lane < 64 ? e0 : e1) : INT64_MAX;
+  return first;
+}
+
+// Buckets of at most 64 tokens: one wave per bucket.  The kept list of the
+// bucket takes three dependent round trips (two rounds of search_kept, then a
+// window load that finish_kept reads), and K of its first 4 * RPP kept rows a
+// fourth; the bucket's V rows and A values (lane r holds A of row r; shuffles
+// hand each row group its value) are requested right after the window, so they
+// arrive meanwhile.
+// The kept rows form a 64-bit mask, so a kept row's output slot is a popcount.
+// Target (largest A_g, ties to the lower index), gates, sums and outputs are as in
+// merge_kernel_any, in the same order.  (Ag is not __restrict__ here: a restrict
+// read-only load may be moved past the memory clobber that pins it.)
 template <typename T, int LG>
 __global__ void __launch_bounds__(NTM)
-merge_kernel(MergeTables t, int lc, const float* __restrict__ Ag, int Hkv, int64_t n, int d,
+merge_kernel(MergeTables t, int lc, const float* Ag, int Hkv, int64_t n, int d,
              int bucket, int64_t nbuckets, int64_t ntask) {
   constexpr int W = El<T>::N;
   constexpr int RPP = 64 / LG;                   // rows per wave pass
   constexpr int NP = 64 / RPP;                   // passes over a 64-row bucket
-  constexpr int KBATCH = 4;                      // K copy passes issued together
   const int lane = threadIdx.x & 63;
-  const int64_t task = (int64_t)blockIdx.x * (NTM / 64) + threadIdx.x / 64;
+  // wave-uniform, so that the per-layer pointers are scalar loads
+  const int64_t task = (int64_t)blockIdx.x * (NTM / 64) +
+                       __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
   if (task >= ntask) return;                     // waves are independent (no barriers)
   int l = 0;
   while (l + 1 < lc && t.task0.v[l + 1] <= task) ++l;
@@ -284,6 +322,7 @@ merge_kernel(MergeTables t, int lc, const float* __restrict__ Ag, int Hkv, int64
   const int g = (int)(local / nbuckets);
   const int64_t b0 = (local % nbuckets) * bucket;
   const int64_t b1 = min(n, b0 + bucket);
+  const int nrow = (int)(b1 - b0);
   const int64_t m = t.m.v[l];
   const int32_t* ip = (const int32_t*)t.idx.p[l] + (int64_t)g * m;
   const float* A = Ag + ((int64_t)l * Hkv + g) * n;
@@ -294,16 +333,29 @@ merge_kernel(MergeTables t, int lc, const float* __restrict__ Ag, int Hkv, int64
   float* lR = (float*)t.logR.p[l] + (int64_t)g * m;
   const int rg = lane / LG, c = lane % LG;
 
-  // the bucket's V rows (rows past b1 are clamped to b1 - 1: read, never used)
+  if (m == 0) return;                            // nothing kept in this layer
+  // the kept list is narrowed to <= 64 candidates, then three groups of loads go
+  // out in this order: the 128-entry window of the kept list, the bucket's V rows
+  // (rows past b1 are clamped to b1 - 1: read, never used) and its A values.
+  // Loads complete in order, so the window arrives without waiting for V.
+  int64_t slo, shi;
+  search_kept(ip, m, b0, lane, slo, shi);
+  const int w0 = ip[min(slo + lane, m - 1)], w1 = ip[min(slo + 64 + lane, m - 1)];
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
   uint4 raw[NP];
 #pragma unroll
   for (int p = 0; p < NP; ++p) {
     const int64_t e = min(b0 + p * RPP + rg, b1 - 1);
-    raw[p] = *reinterpret_cast<const uint4*>(Vg + e * d + c * W);
+    raw[p] = ld_stream(Vg + e * d + c * W);      // read once
   }
-  // kept slots of the bucket: [lo, lo + nk), lane s holding slot lo + s
-  const int64_t lo = wave_lower_bound(ip, m, b0, lane);
-  const int64_t kid = lo + lane < m ? ip[lo + lane] : INT64_MAX;
+  const float arow = A[b0 + min(lane, nrow - 1)];
+  // keeps the loads above here: otherwise they are sunk into the branch below,
+  // or scheduled after the first use of the window
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+  int64_t kid;
+  const int64_t lo = finish_kept(m, (int)b0, lane, slo, shi, w0, w1, kid);
   const bool kin = kid < b1;
   const int nk = __builtin_popcountll(__ballot(kin));
   if (nk == 0) return;                           // no kept token: evicted tokens dropped
@@ -311,39 +363,40 @@ merge_kernel(MergeTables t, int lc, const float* __restrict__ Ag, int Hkv, int64
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) rowmask |= __shfl_xor(rowmask, o, 64);
 
-  // A of the kept tokens and K of the first KBATCH * RPP kept rows, requested
-  // together (one round trip)
-  const float av = kin ? A[kid] : -INFINITY;
-  uint4 kr[KBATCH];
-#pragma unroll
-  for (int q = 0; q < KBATCH; ++q) {
+  // K of the first 4 * RPP kept rows (four named registers: an array here is
+  // placed in LDS by the compiler, with a wait after every load)
+  auto kload = [&](int q) __attribute__((always_inline)) {
     const int s = min(q * RPP + rg, nk - 1);
     const int64_t src = __shfl(kid, s, 64);
-    kr[q] = *reinterpret_cast<const uint4*>(Kg + src * d + c * W);
-  }
-  // merge target: the kept token with the largest A, ties to the lower index
-  float bv = av;
-  int bs = kin ? lane : 64;
+    return *reinterpret_cast<const uint4*>(Kg + src * d + c * W);
+  };
+  auto kstore = [&](int q, const uint4& v) __attribute__((always_inline)) {
+    const int s = min(q * RPP + rg, nk - 1);     // clamped lanes rewrite the last row
+    *reinterpret_cast<uint4*>(Ko + (lo + s) * d + c * W) = v;
+  };
+  const uint4 k0 = kload(0), k1 = kload(1), k2 = kload(2), k3 = kload(3);
+
+  // merge target: the kept row with the largest A, ties to the lower row (the
+  // lower token index)
+  const bool rkept = lane < nrow && ((rowmask >> lane) & 1ull);
+  float bv = rkept ? arow : -INFINITY;
+  int bs = rkept ? lane : 64;
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) {
     const float ov = __shfl_xor(bv, o, 64);
     const int os = __shfl_xor(bs, o, 64);
     if (ov > bv || (ov == bv && os < bs)) { bv = ov; bs = os; }
   }
-  // every lane holds the same winner; the clamp only guards against NaN scores
-  const int wl = bs < nk ? bs : 0;
-  const int64_t ts = lo + wl, tt = __shfl(kid, wl, 64);
-  const float At = __shfl(av, wl, 64);
+  // every lane holds the same winner; the fallback only guards against NaN scores
+  const int rt = bs < 64 ? bs : __builtin_ctzll(rowmask);
+  const int64_t tt = b0 + rt;
+  const int64_t ts = lo + __builtin_popcountll(rowmask & ((1ull << rt) - 1ull));
+  const float At = __shfl(arow, rt, 64);
 
-  // K of the kept rows: the first batch is in flight already
-#pragma unroll
-  for (int q = 0; q < KBATCH; ++q) {
-    const int s = min(q * RPP + rg, nk - 1);     // clamped lanes rewrite the last row
-    *reinterpret_cast<uint4*>(Ko + (lo + s) * d + c * W) = kr[q];
-  }
+  kstore(0, k0); kstore(1, k1); kstore(2, k2); kstore(3, k3);
   // more kept rows than a batch; the loop is wave-uniform so that every lane the
   // shuffle reads from is active
-  for (int s0 = KBATCH * RPP; s0 < nk; s0 += RPP) {
+  for (int s0 = 4 * RPP; s0 < nk; s0 += RPP) {
     const int s = min(s0 + rg, nk - 1);
     const int64_t src = __shfl(kid, s, 64);
     *reinterpret_cast<uint4*>(Ko + (lo + s) * d + c * W) =
@@ -352,7 +405,6 @@ merge_kernel(MergeTables t, int lc, const float* __restrict__ Ag, int Hkv, int64
 
   // the target's V row is one of the bucket rows already in registers: pass
   // rt / RPP (wave-uniform), lanes of row group rt % RPP
-  const int rt = (int)(tt - b0);
   const int pt = __builtin_amdgcn_readfirstlane(rt / RPP);
   uint4 tv = make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
@@ -379,6 +431,7 @@ merge_kernel(MergeTables t, int lc, const float* __restrict__ Ag, int Hkv, int64
 #pragma unroll
   for (int p = 0; p < NP; ++p) {
     const int r = p * RPP + rg;                  // row within the bucket
+    const float ae = __shfl(arow, r, 64);        // A of row r (uniform control flow here)
     const int64_t e = b0 + r;
     if (e >= b1) continue;
     if ((rowmask >> r) & 1ull) {                 // kept: copy its V (the target is merged below)
@@ -398,7 +451,7 @@ merge_kernel(MergeTables t, int lc, const float* __restrict__ Ag, int Hkv, int64
     ne2 = group_sum<LG>(ne2);
     const float nd = sqrtf(ne2) * nt;
     const float gate = nd > 0.f ? fmaxf(dot / nd, 0.f) : 0.f;
-    const float wgt = gate * A[e];
+    const float wgt = gate * ae;
 #pragma unroll
     for (int i = 0; i < W; ++i) num[i] += wgt * ve[i];
     den += wgt;

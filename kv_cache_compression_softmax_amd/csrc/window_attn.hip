@@ -339,8 +339,10 @@ __device__ __forceinline__ void pass2(const WinArgs& a, WinSmem<D, TG>& sm, int 
   auto block_t = [&](const bf16x8 (&kc)[S], int64_t j0, auto full_t) __attribute__((always_inline)) {
     constexpr bool full = decltype(full_t)::value;
     const int64_t key = j0 + qi;                 // this lane's key column
-    int qo = lane, co = 4 * hf;
-    asm volatile("" : "+v"(qo), "+v"(co));       // keep Q and c reads in the loop
+    // keep the Q and c reads in the loop; c is indexed in float4 units so that
+    // each read is one aligned ds_read_b128 with an immediate offset
+    int qo = lane, co = hf;
+    asm volatile("" : "+v"(qo), "+v"(co));
     // this lane's 16 rows of tile t: exp2(s - c_r) summed (the partner lane adds
     // the other 16 at the end of the block); the key is seen by rows rr with
     // key - (n - w) <= rr < w, and only if key < n
@@ -352,7 +354,7 @@ __device__ __forceinline__ void pass2(const WinArgs& a, WinSmem<D, TG>& sm, int 
       float colsum = 0.f;
 #pragma unroll
       for (int qd = 0; qd < 4; ++qd) {
-        const float4 c4 = *reinterpret_cast<const float4*>(&sm.c[t * 32 + 8 * qd + co]);
+        const float4 c4 = reinterpret_cast<const float4*>(sm.c)[t * 8 + 2 * qd + co];
         const float cc[4] = {c4.x, c4.y, c4.z, c4.w};
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
