@@ -50,6 +50,7 @@ template <> struct El<float> {
 // ------------------------------------------------------------- VATP + union
 constexpr int NT = 256;         // 4 waves
 constexpr int VNL = 8;          // most V loads per lane (all issued before any is used)
+constexpr int MAXG = 8;         // query heads per KV head whose A loads are issued up front
 
 // One wave per min(VNL, LG) * 64 / LG rows (at most 64) of one (layer, KV head):
 // the rows' V are read
@@ -59,7 +60,7 @@ constexpr int VNL = 8;          // most V loads per lane (all issued before any 
 // (coalesced across lanes) and writes U = max_h A_h * |v| and the group mean A_g.
 template <typename T, int LG>
 __global__ void __launch_bounds__(NT)
-vatp_union_kernel(const float* __restrict__ A_hq, ConstPtrs V, int Hq, int Hkv, int64_t n, int d,
+vatp_union_kernel(const float* A_hq, ConstPtrs V, int Hq, int Hkv, int64_t n, int d,
                   int64_t nchunk, int64_t nwave, float* __restrict__ U, float* __restrict__ Ag) {
   constexpr int W = El<T>::N;
   constexpr int RPI = 64 / LG;                  // rows per load instruction
@@ -67,21 +68,39 @@ vatp_union_kernel(const float* __restrict__ A_hq, ConstPtrs V, int Hq, int Hkv, 
   constexpr int RW = RPI * NL;                  // rows per wave (at most 64)
   static_assert(RW <= 64, "one lane per row in the attention phase");
   const int lane = threadIdx.x & 63;
-  const int64_t wid = (int64_t)blockIdx.x * (NT / 64) + threadIdx.x / 64;
-  if (wid >= nwave) return;                     // waves are independent (no barriers)
-  const int64_t chunk = wid % nchunk;
-  const int g = (int)((wid / nchunk) % Hkv);
-  const int l = (int)(wid / (nchunk * Hkv));
+  // wave-uniform (scalar pointer loads); the launch keeps wave counts below 2^31,
+  // so the index arithmetic is 32-bit
+  const uint32_t wid = blockIdx.x * (NT / 64) + __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
+  if (wid >= (uint64_t)nwave) return;           // waves are independent (no barriers)
+  const uint32_t nch = (uint32_t)nchunk;
+  const uint32_t chunk = wid % nch;
+  const int g = (int)((wid / nch) % (uint32_t)Hkv);
+  const int l = (int)(wid / (nch * (uint32_t)Hkv));
   const int G = Hq / Hkv;
   const int rg = lane / LG, c = lane % LG;
   const T* Vg = (const T*)V.p[l] + (int64_t)g * n * d;
-  const int64_t j0 = chunk * RW;
+  const int64_t j0 = (int64_t)chunk * RW;
   uint4 raw[NL];
 #pragma unroll
   for (int u = 0; u < NL; ++u) {
     const int64_t j = min(j0 + u * RPI + rg, n - 1);     // rows past n: read, never used
     raw[u] = ld_stream(Vg + j * d + c * W);
   }
+  // lane q takes row j0 + q; its attention values for the group's first MAXG heads
+  // are requested together with the V rows (unconditional, clamped loads: loads
+  // on a branch or in a runtime loop each wait for their own round trip)
+  const int q = lane;
+  const int64_t j = j0 + q;
+  const float* Ah = A_hq + ((int64_t)l * Hq + (int64_t)g * G) * n + min(j, n - 1);
+  float av[MAXG];
+#pragma unroll
+  for (int h = 0; h < MAXG; ++h) av[h] = Ah[(int64_t)min(h, G - 1) * n];
+  // every load above is issued before any result is used: without this the
+  // attention loads are sunk into the branch below and the first V row is
+  // waited for before the others are requested (A_hq is not __restrict__ for
+  // the same reason: a restrict read-only load may be moved past the clobber)
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
   float ss[NL];
 #pragma unroll
   for (int u = 0; u < NL; ++u) {
@@ -93,19 +112,23 @@ vatp_union_kernel(const float* __restrict__ A_hq, ConstPtrs V, int Hq, int Hkv, 
     ss[u] = group_sum<LG>(a);
   }
   // row q = u * RPI + r lives in register u of the lanes of row group r
-  const int q = lane;
   float s2 = 0.f;
 #pragma unroll
   for (int u = 0; u < NL; ++u) {
     const float v = __shfl(ss[u], (q % RPI) * LG, 64);
     s2 = (q / RPI == u) ? v : s2;
   }
-  const int64_t j = j0 + q;
   if (q < RW && j < n) {
     const float vn = sqrtf(s2);
-    const float* Ah = A_hq + ((int64_t)l * Hq + (int64_t)g * G) * n + j;
     float mx = -INFINITY, sum = 0.f;
-    for (int h = 0; h < G; ++h) {
+#pragma unroll
+    for (int h = 0; h < MAXG; ++h) {
+      if (h < G) {
+        mx = fmaxf(mx, av[h] * vn);
+        sum += av[h];
+      }
+    }
+    for (int h = MAXG; h < G; ++h) {             // groups above MAXG heads
       const float a = Ah[(int64_t)h * n];
       mx = fmaxf(mx, a * vn);
       sum += a;
