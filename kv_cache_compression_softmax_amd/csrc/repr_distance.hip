@@ -100,26 +100,34 @@ repr_distance_vec(ConstPtrs h, const T* __restrict__ hf, int L, int64_t n, int64
     asm volatile("" : "+v"(dist));               // computed by every lane, then selected
     mine = lane == l ? dist : mine;
   };
-  // Layers in pairs, two rows in turn.  Loads are unconditional (past the last
-  // layer they re-read it, an L2 hit) and no exit sits between the halves, so the
-  // compiler never has to wait for the row that is still in flight.
+  // Layers in pairs, two rows in turn.  Inside the loop every load is
+  // unconditional and no exit sits between the halves, so the compiler never has
+  // to wait for the row that is still in flight.  The loop stops while two or
+  // three layers remain, so no load reaches past the last layer (a clamped
+  // re-read of it would miss L2: its rows were read non-temporally).
   uint4 a0[V], a1[V];
-  const int last = L - 1;
   load((const T*)h.p[0] + roff, a0);
-  load((const T*)h.p[min(1, last)] + roff, a1);
+  if (L > 1) load((const T*)h.p[1] + roff, a1);
   int l = 0;
 #pragma unroll 1
-  for (; l + 1 < L; l += 2) {
+  for (; l + 3 < L; l += 2) {
     // the barriers keep each refill behind the last read of its buffer, so the
     // new row lands in the same registers (no copies of rows still in flight)
     layer(l, a0);
     __builtin_amdgcn_sched_barrier(0);
-    load((const T*)h.p[min(l + 2, last)] + roff, a0);
+    load((const T*)h.p[l + 2] + roff, a0);
     layer(l + 1, a1);
     __builtin_amdgcn_sched_barrier(0);
-    load((const T*)h.p[min(l + 3, last)] + roff, a1);
+    load((const T*)h.p[l + 3] + roff, a1);
   }
-  if (l < L) layer(l, a0);
+  // 1, 2 or 3 layers remain: l, l + 1 (in a1), l + 2 (reloaded into a0)
+  layer(l, a0);
+  if (l + 2 < L) {
+    __builtin_amdgcn_sched_barrier(0);
+    load((const T*)h.p[l + 2] + roff, a0);
+  }
+  if (l + 1 < L) layer(l + 1, a1);
+  if (l + 2 < L) layer(l + 2, a0);
   if (lane < L) D[(int64_t)lane * n + tok] = mine;
 }
 

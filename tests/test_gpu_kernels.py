@@ -137,6 +137,7 @@ DIST_CASES = [
     (2, 64, 4100, torch.bfloat16),       # width not a multiple of 8: element path
     (2, 65, 8192, torch.bfloat16),       # 16 vectors per lane
     (4, 300, 4096, torch.float32),       # float32, 16 vectors per lane
+    (5, 129, 4096, torch.bfloat16),      # odd layer count: loop, then a three-layer tail
     (35, 130, 512, torch.bfloat16),      # more layers than one launch holds
     (64, 40, 256, torch.bfloat16),       # two full launches
 ]
