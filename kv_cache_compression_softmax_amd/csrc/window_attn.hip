@@ -41,7 +41,8 @@ constexpr int NTW = 256;        // threads per workgroup (4 waves)
 constexpr int MAX_TILES = 8;    // G * ceil(w/32)
 constexpr int MAX_TG = 4;       // tiles per launch
 constexpr int KPW = 512;        // keys per wave
-constexpr int MIN_WAVES = 4096; // waves per launch that fill 256 CUs
+constexpr int64_t kMallBytes = 256ll << 20;  // MI355X last-level cache (MALL)
+constexpr int kLargeChunk = 16;  // layers per chunk when a layer's keys exceed half the MALL
 constexpr float LOG2E = 1.4426950408889634f;
 
 struct Geo {
@@ -501,9 +502,14 @@ void make_plan(int L, int Hq, int Hkv, int64_t n, int w, int d, int dtype, Plan*
   P->g = g;
   P->mfma = (dtype == KVC_BF16);
   const int lg_max = L < kLayersPerLaunch ? L : kLayersPerLaunch;
-  // chunk: enough layers that a launch (two chunks) has MIN_WAVES waves
-  const int64_t waves_per_layer = (int64_t)Hkv * ((n + KPW - 1) / KPW);
-  int64_t lch = (MIN_WAVES + 2 * waves_per_layer - 1) / (2 * waves_per_layer);
+  // Layers per chunk (a launch runs pass 2 of one chunk beside pass 1 of the
+  // next).  While two layers' keys fit the MALL, a chunk holds about one MALL of
+  // keys, so that pass 2 re-reads them from there (8B shape at 32K tokens: 4
+  // layers, 1.00 ms against 1.06-1.09 with 3, 5, 6 or 8).  Larger layers cannot
+  // be re-read from it at all, and fewer launches win (102400 tokens: 3.04 ms
+  // with 8-32 layers per chunk against 3.20 with 2).
+  const int64_t layer_k = (int64_t)Hkv * n * d * (dtype == KVC_BF16 ? 2 : 4);
+  int64_t lch = 2 * layer_k <= kMallBytes ? (kMallBytes + layer_k / 2) / layer_k : kLargeChunk;
   lch = lch < 1 ? 1 : (lch > lg_max ? lg_max : lch);
   P->lch = (int)lch;
   if (P->mfma) {
