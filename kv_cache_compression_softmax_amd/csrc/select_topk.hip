@@ -13,21 +13,48 @@
 //      k - w - cgt keys == T in index order.  Output positions come from a block
 //      scan of (count > T, count == T) per thread, so the indices come out
 //      ascending and the result is exact and deterministic.
-// The score row (at most a few hundred KB) is re-read from L2 by each pass.
+// The score row (at most a few hundred KB) is re-read from L2 by each pass; each
+// thread keeps several loads in flight, and the histograms are per wave with
+// wave-aggregated increments where lanes crowd into one bin.
 #include "common.h"
 
 namespace kvc {
 namespace {
 
 constexpr int NT = 1024;
+constexpr int NW = NT / 64;     // waves
 constexpr int EPT = 4;          // consecutive elements per thread in the output pass
+constexpr int HU = 8;           // elements per thread loaded together in a histogram pass
+
+// Adds 1 to hist[bin] for every active lane with valid set.  When many lanes share
+// the first valid lane's bin (scores spread over few binades make the high digits
+// crowd into a few bins) the wave counts each distinct bin with a ballot and one
+// lane adds the count; otherwise every lane adds its own 1.
+__device__ __forceinline__ void hist_add(int* hist, bool valid, int bin) {
+  uint64_t act = __ballot(valid);
+  if (act == 0) return;
+  const int b0 = __builtin_amdgcn_readlane(bin, __builtin_ctzll(act));
+  if (__builtin_popcountll(__ballot(valid && bin == b0)) < 16) {
+    if (valid) atomicAdd(&hist[bin], 1);
+    return;
+  }
+  const int lane = threadIdx.x & 63;
+  while (act) {                                   // one round per distinct bin
+    const int lead = __builtin_ctzll(act);
+    const int b = __builtin_amdgcn_readlane(bin, lead);
+    const uint64_t same = __ballot(valid && bin == b);
+    if (lane == lead) atomicAdd(&hist[b], __builtin_popcountll(same));
+    act &= ~same;
+  }
+}
 
 __global__ void __launch_bounds__(NT)
 select_kernel(const float* __restrict__ S, int Hkv, int64_t n, I64s kk, int w, MutPtrs idx) {
-  __shared__ int hist[256];
+  __shared__ int hist[NW][256];                   // one histogram per wave
   __shared__ int scan[NT / 64];
   __shared__ int pick[2];
   const int tid = threadIdx.x;
+  const int wv = tid / 64;
   const int l = blockIdx.x / Hkv, g = blockIdx.x % Hkv;
   const int64_t k = kk.v[l];
   const float* row = S + ((int64_t)l * Hkv + g) * n;
@@ -49,14 +76,26 @@ select_kernel(const float* __restrict__ S, int Hkv, int64_t n, I64s kk, int w, M
   for (int p = 3; p >= 0; --p) {
     const int shift = 8 * p;
     const uint32_t hi_mask = (p == 3) ? 0u : (uint32_t)(~0ull << (shift + 8));
-    if (tid < 256) hist[tid] = 0;
+    for (int i = tid; i < NW * 256; i += NT) (&hist[0][0])[i] = 0;
     __syncthreads();
-    for (int64_t i = tid; i < nb; i += NT) {
-      const uint32_t key = f32_key(row[i]);
-      if ((key & hi_mask) == (prefix & hi_mask)) atomicAdd(&hist[(key >> shift) & 255], 1);
+#pragma unroll 1
+    for (int64_t i0 = 0; i0 < nb; i0 += (int64_t)NT * HU) {
+      float v[HU];                                // HU loads in flight per thread
+#pragma unroll
+      for (int u = 0; u < HU; ++u) v[u] = row[min(i0 + (int64_t)u * NT + tid, nb - 1)];
+#pragma unroll
+      for (int u = 0; u < HU; ++u) {
+        const uint32_t key = f32_key(v[u]);
+        const bool ok = i0 + (int64_t)u * NT + tid < nb && (key & hi_mask) == (prefix & hi_mask);
+        hist_add(hist[wv], ok, (int)((key >> shift) & 255));
+      }
     }
     __syncthreads();
-    const int c = tid < 256 ? hist[255 - tid] : 0;
+    int c = 0;
+    if (tid < 256) {
+#pragma unroll
+      for (int x = 0; x < NW; ++x) c += hist[x][255 - tid];
+    }
     int tot;
     const int incl = block_exclusive_scan<NT>(c, scan, &tot) + c;
     if (tid < 256 && incl >= rem && incl - c < rem) { pick[0] = 255 - tid; pick[1] = incl - c; }
@@ -68,20 +107,28 @@ select_kernel(const float* __restrict__ S, int Hkv, int64_t n, I64s kk, int w, M
   }
   const uint32_t T = prefix;
   const int64_t take_eq = need - above;           // >= 1 copies of T are kept
-  // ---- 2. ordered output of [0, nb)
+  // ---- 2. ordered output of [0, nb); the next chunk's scores are requested
+  // before this chunk's block scan
   int64_t run_gt = 0, run_eq = 0;
+  float cur[EPT];
+  auto fetch = [&](int64_t c0, float (&v)[EPT]) __attribute__((always_inline)) {
+    const int64_t i0 = c0 + (int64_t)tid * EPT;
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) v[e] = row[min(i0 + e, nb - 1)];
+  };
+  fetch(0, cur);
 #pragma unroll 1
   for (int64_t c0 = 0; c0 < nb; c0 += (int64_t)NT * EPT) {
     const int64_t i0 = c0 + (int64_t)tid * EPT;
     uint32_t gt = 0, eq = 0;
 #pragma unroll
     for (int e = 0; e < EPT; ++e) {
-      if (i0 + e < nb) {
-        const uint32_t key = f32_key(row[i0 + e]);
-        gt |= (uint32_t)(key > T) << e;
-        eq |= (uint32_t)(key == T) << e;
-      }
+      const uint32_t key = f32_key(cur[e]);
+      const bool in = i0 + e < nb;
+      gt |= (uint32_t)(in && key > T) << e;
+      eq |= (uint32_t)(in && key == T) << e;
     }
+    fetch(min(c0 + (int64_t)NT * EPT, nb - 1), cur);
     const int packed = __builtin_popcount(gt) | (__builtin_popcount(eq) << 16);
     int tot;
     const int ex = block_exclusive_scan<NT>(packed, scan, &tot);
