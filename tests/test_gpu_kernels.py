@@ -304,6 +304,9 @@ SELKV_CASES = [
     (1, 8, 2, 1000, 32, 128, 250, 64),       # last bucket partial
     (1, 4, 2, 700, 16, 64, 300, 50),         # head dim 64, odd bucket
     (1, 4, 4, 520, 32, 128, 40, 128),        # MHA, some buckets with no kept token
+    (1, 4, 2, 2048, 32, 128, 40, 64),        # 40 kept: no search round, most buckets empty
+    (1, 4, 2, 1000, 16, 64, 990, 64),        # nearly all kept: long kept runs, few merges
+    (1, 8, 2, 3001, 32, 128, 1500, 32),      # bucket 32, ragged last bucket
 ]
 
 
