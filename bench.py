@@ -297,6 +297,21 @@ def main():
                           "frac": round(path_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)},
         "kernels": kernels,
     }
+    if w.method == "selkv":
+        # row a12's decode check (compensated decode over the compacted cache and
+        # plain decode over the full cache, one query per head and layer), timed
+        # apart: it checks the compressed cache rather than producing it
+        plan.decode_check(inp)
+        torch.cuda.synchronize()
+        d0 = torch.cuda.Event(enable_timing=True)
+        d1 = torch.cuda.Event(enable_timing=True)
+        d0.record(stream)
+        for _ in range(args.steps):
+            plan.decode_check(inp)
+        d1.record(stream)
+        torch.cuda.synchronize()
+        out["decode_check"] = {"ms": round(d0.elapsed_time(d1) / args.steps, 4),
+                               "timed": "separately, after the steps; not in ms_per_step"}
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(w, inp)
