@@ -310,13 +310,30 @@ SELKV_CASES = [
 ]
 
 
+# float32 K/V: 16-byte lanes hold 4 values, so a d = 128 row takes 32 lanes
+SELKV_F32_CASES = [
+    (1, 8, 2, 1000, 32, 128, 250, 64),
+    (1, 4, 2, 700, 16, 64, 300, 50),
+    (1, 4, 2, 2048, 32, 128, 40, 64),
+]
+
+
 @pytest.mark.parametrize("case", SELKV_CASES, ids=str)
 def test_selkv_pieces(dev, case):
+    _selkv_pieces(dev, case, torch.bfloat16)
+
+
+@pytest.mark.parametrize("case", SELKV_F32_CASES, ids=str)
+def test_selkv_pieces_f32(dev, case):
+    _selkv_pieces(dev, case, torch.float32)
+
+
+def _selkv_pieces(dev, case, dtype):
     L, Hq, Hkv, n, w, d, m, bucket = case
-    announce("selkv", case)
-    q = [gen((Hq, w, d), 200 + l, dev) for l in range(L)]
-    K = [gen((Hkv, n, d), 220 + l, dev) for l in range(L)]
-    V = [gen((Hkv, n, d), 240 + l, dev) for l in range(L)]
+    announce("selkv", case, dtype)
+    q = [gen((Hq, w, d), 200 + l, dev, dtype) for l in range(L)]
+    K = [gen((Hkv, n, d), 220 + l, dev, dtype) for l in range(L)]
+    V = [gen((Hkv, n, d), 240 + l, dev, dtype) for l in range(L)]
     A_hq = torch.empty(L, Hq, n, device=dev)
     B().kvc_score_window_attn(q, K, 1 / math.sqrt(d), True, A_hq)
     U = torch.empty(L, Hkv, n, device=dev)
@@ -339,7 +356,7 @@ def test_selkv_pieces(dev, case):
         np.testing.assert_array_equal(idx[0].cpu().numpy(), ref_o["idx"])
         # merge given identical inputs: the oracle's idx and float32-rounded A_g
         Ag32 = ref_o["A_g"].astype(np.float32)
-        Kc = [torch.empty(Hkv, m, d, dtype=torch.bfloat16, device=dev)]
+        Kc = [torch.empty(Hkv, m, d, dtype=dtype, device=dev)]
         Vc = [torch.empty_like(Kc[0])]
         lr = [torch.empty(Hkv, m, device=dev)]
         B().kvc_merge_gated([K[l]], [V[l]], torch.from_numpy(Ag32).to(dev)[None].contiguous(), idx, [m],
