@@ -178,7 +178,8 @@ int kvc_compact(const void* const* K, const void* const* V, int dtype, int L, in
  *   Ag_out[l, g, j] = mean over the group's heads of A_hq (the group's prefill
  *                     attention used for routing and merge weights)
  *   A_hq       device float32 [L, Hq, n] (kvc_score_window_attn, per_query_head=1).
- *   V          host array of L device pointers, each [Hkv, n, d] of dtype.
+ *   V          host array of L device pointers, each [Hkv, n, d] of dtype,
+ *              16-byte aligned; d * element size in {64, 128, 256, 512} bytes.
  *   U_out, Ag_out  device float32 [L, Hkv, n].
  */
 int kvc_vatp_union(const float* A_hq, const void* const* V, int dtype, int L, int Hq,
@@ -201,7 +202,9 @@ int kvc_vatp_union(const float* A_hq, const void* const* V, int dtype, int L, in
  *   Ag         device float32 [L, Hkv, n].
  *   idx        host array of L device pointers, each int32 [Hkv, m_keep[l]],
  *              ascending, every entry in [0, n).
- *   m_keep     host int64 [L];  bucket >= 1;  d in {64, 128}.
+ *   m_keep     host int64 [L], each in [1, n];  bucket >= 1;
+ *              d * element size in {64, 128, 256, 512} bytes; K, V, K_out,
+ *              V_out 16-byte aligned.
  *   K_out, V_out  host arrays of L device pointers, each [Hkv, m_keep[l], d].
  *   logR_out   host array of L device pointers, each float32 [Hkv, m_keep[l]].
  */
