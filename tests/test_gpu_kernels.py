@@ -328,6 +328,20 @@ def test_selkv_pieces_f32(dev, case):
     _selkv_pieces(dev, case, torch.float32)
 
 
+def test_selkv_random_sweep(dev):
+    """60 seeded random shapes: head counts, window, length, bucket (below, at and
+    above 64 tokens), budgets from 1 token to all of them, head dim, dtype."""
+    import random
+    rng = random.Random(1234)
+    for _ in range(60):
+        Hkv, G, w = rng.choice([1, 2]), rng.choice([1, 2, 4]), rng.choice([8, 16, 32])
+        n = rng.randint(w + 2, 4000)
+        bucket = rng.choice([8, 16, 32, 50, 64, 65, 100])
+        m = rng.choice([rng.randint(1, n), rng.randint(max(1, n // 5), n // 3 + 1), n, w, max(1, w - 3)])
+        case = (1, G * Hkv, Hkv, n, w, rng.choice([64, 128]), max(1, min(n, m)), bucket)
+        _selkv_pieces(dev, case, rng.choice([torch.bfloat16, torch.bfloat16, torch.float32]))
+
+
 def _selkv_pieces(dev, case, dtype):
     L, Hq, Hkv, n, w, d, m, bucket = case
     announce("selkv", case, dtype)
