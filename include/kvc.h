@@ -65,7 +65,9 @@ const char* kvc_last_error(void);
 /*
  * Top-k restricted entropy of each logits row ([InfoKV] Method; Glossary).
  * For row i: T = the k largest logits (as a multiset), p_t = softmax over T
- * only, H[i] = -sum_t p_t ln p_t (natural log).  0 <= H <= ln k.
+ * only, H[i] = -sum_t p_t ln p_t (natural log).  0 <= H <= ln k.  Logits may
+ * be -inf (a masked vocabulary): a term with p_t = 0 contributes 0, the limit
+ * of p ln p; a row with no finite logit gives NaN.  NaN logits are unsupported.
  *   logits     device, [rows, row_stride] of dtype; the first `vocab` columns
  *              of each row are used.
  *   rows >= 0; 1 <= topk <= min(vocab, KVC_MAX_TOPK_ENTROPY); row_stride >= vocab.

@@ -351,10 +351,13 @@ topk_entropy_kernel(const T* __restrict__ logits, int64_t rows, int64_t vocab, i
   float hloc = 0.f;
   for (int i = lane; i < k; i += 64) {
     const float t = Tr<T>::value(Tr<T>::key(cand[i]));
-    hloc += expf(t - m) * invZ * ((m - t) + lnZ);   // -p ln p, every term >= 0
+    const float e = expf(t - m);
+    // -p ln p, every term >= 0; p = 0 (a -inf logit held because fewer than k
+    // are finite, or an underflow) contributes its limit 0, not 0 * inf
+    if (e > 0.f) hloc += e * invZ * ((m - t) + lnZ);
   }
   const float h = wave_sum(hloc);
-  if (lane == 0) H[rowi] = h;
+  if (lane == 0) H[rowi] = m == -INFINITY ? NAN : h;   // no finite logit: no entropy
 }
 
 template <typename T>

@@ -41,10 +41,11 @@ def topk_entropy(logits: np.ndarray, k: int) -> np.ndarray:
 
     For row i take the multiset T of its k largest logits, form the softmax
     over T only (p_t = e^(t - m) / Z with m = max T, Z = sum over T of e^(t - m))
-    and return H_i = -sum_t p_t ln p_t.  ln p_t is written as (t - m) - ln Z so
-    that a p_t that underflows to 0 contributes 0 rather than 0 * (-inf).
-    Which of several equal logits at the k-th place are taken does not matter:
-    the multiset of values is the same.
+    and return H_i = -sum_t p_t ln p_t.  A term with p_t = 0 (a -inf logit
+    taken because fewer than k logits are finite, or one that underflows)
+    contributes 0, the limit of p ln p; a row with no finite logit has no
+    entropy and gives NaN.  Which of several equal logits at the k-th place are
+    taken does not matter: the multiset of values is the same.
     """
     z = np.asarray(logits, dtype=np.float64)
     rows, vocab = z.shape
@@ -52,11 +53,15 @@ def topk_entropy(logits: np.ndarray, k: int) -> np.ndarray:
         raise ValueError("need 1 <= k <= vocab")
     top = np.partition(z, vocab - k, axis=1)[:, vocab - k:]        # [rows, k]
     m = top.max(axis=1, keepdims=True)
-    e = np.exp(top - m)
-    Z = e.sum(axis=1, keepdims=True)
-    p = e / Z
-    logp = (top - m) - np.log(Z)
-    return -(p * logp).sum(axis=1)
+    with np.errstate(invalid="ignore"):          # -inf - -inf in a row with no finite logit
+        e = np.exp(top - m)
+        Z = e.sum(axis=1, keepdims=True)
+        p = e / Z
+        logp = (top - m) - np.log(Z)
+        terms = np.where(p > 0, p * logp, 0.0)
+    H = -terms.sum(axis=1)
+    H[~np.isfinite(m[:, 0])] = np.nan            # no finite logit in the row
+    return H
 
 
 def repr_distance(h_l: np.ndarray, h_final: np.ndarray, tau: float) -> np.ndarray:

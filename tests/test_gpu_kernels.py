@@ -56,6 +56,7 @@ ENTROPY_CASES = [
     (8, 5000, 5000, 1000, torch.bfloat16, "zeros"),        # -0 above a negative threshold
     (8, 5000, 5000, 1000, torch.float32, "zeros"),
     (8, 9000, 9000, 256, torch.bfloat16, "neginf"),        # 90% -inf (masked vocabulary)
+    (8, 2048, 2049, 810, torch.float32, "neginf"),         # fewer than k finite: p = 0 terms
     (5, 1000, 1000, 256, torch.bfloat16, "normal4"),       # row shorter than one step
     (5, 700, 701, 100, torch.float32, "normal4"),          # the same in float32, odd pitch
     (6, 9000, 9000, 256, torch.bfloat16, "descending"),
@@ -116,6 +117,53 @@ def test_topk_entropy(dev, case):
         assert_rel(got, ref, 1e-3, what="H")
     if kind == "flat":
         np.testing.assert_allclose(got, math.log(k), rtol=1e-6)
+
+
+def test_topk_entropy_random_sweep(dev):
+    """40 seeded random shapes: widths around and between step sizes, padded row
+    pitches, k from 1 to 1024, both dtypes, every value distribution above."""
+    import random
+    rng = random.Random(4321)
+    kinds = ["normal4", "spiked", "ties", "zeros", "logprob", "neginf", "ascending", "descending"]
+    for i in range(40):
+        vocab = rng.choice([rng.randint(1, 3000), rng.randint(3000, 40000), 1024 * rng.randint(1, 8)])
+        stride = vocab + rng.choice([0, 0, 1, 3, 8])
+        k = rng.randint(1, min(vocab, 1024))
+        dtype = rng.choice([torch.bfloat16, torch.float32])
+        kind = rng.choice(kinds)
+        rows = rng.randint(1, 9)
+        z = entropy_input(rows, stride, kind, dtype, dev, seed=1000 + i)
+        H = torch.full((rows,), -1.0, device=dev)
+        B().kvc_topk_entropy(z, k, H, vocab=vocab)
+        torch.cuda.synchronize()
+        ref = infokv.topk_entropy(host_f64(z)[:, :vocab], k)
+        got = H.cpu().numpy()
+        what = (rows, vocab, stride, k, dtype, kind)
+        nan = np.isnan(ref)                      # rows with no finite logit
+        np.testing.assert_array_equal(np.isnan(got), nan, err_msg=str(what))
+        if k == 1:
+            assert np.all(got[~nan] == 0), what
+        elif np.any(~nan):
+            assert_rel(got[~nan], ref[~nan], 1e-3, what=f"H {what}")
+
+
+def test_topk_entropy_masked_rows(dev):
+    """Rows with fewer than k finite logits (p = 0 terms add 0) and a row with
+    none (NaN), in both dtypes."""
+    for dtype in (torch.bfloat16, torch.float32):
+        z = gen((4, 3000), 77, dev, torch.float32, 4.0)
+        z[0, 100:] = -math.inf                   # 100 finite < k
+        z[1, ::2] = -math.inf
+        z[2, :] = -math.inf                      # no finite logit
+        z = z.to(dtype)
+        H = torch.empty(4, device=dev)
+        B().kvc_topk_entropy(z, 256, H)
+        torch.cuda.synchronize()
+        ref = infokv.topk_entropy(host_f64(z), 256)
+        got = H.cpu().numpy()
+        assert np.isnan(got[2]) and np.isnan(ref[2])
+        keep = [0, 1, 3]
+        assert_rel(got[keep], ref[keep], 1e-3, what="H masked")
 
 
 def test_topk_entropy_deterministic(dev):

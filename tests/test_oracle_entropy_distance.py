@@ -78,6 +78,23 @@ def test_matches_scipy_entropy_of_sorted_topk():
             assert abs(H[i] - scipy.stats.entropy(p)) < 1e-10
 
 
+def test_masked_logits_fewer_than_k_finite():
+    """-inf logits (a masked vocabulary): with fewer than k finite values the
+    zero-probability entries contribute 0 (the limit of p ln p), so H is the
+    entropy of the finite part (scipy.stats.entropy, which uses the same
+    convention).  A row with no finite logit has no entropy."""
+    z = 4.0 * rng.normal(size=(6, 500))
+    z[:, 40:] = -np.inf                          # 40 finite values per row
+    z[5, :] = -np.inf
+    H = infokv.topk_entropy(z, 200)
+    for i in range(5):
+        fin = z[i][np.isfinite(z[i])]
+        assert abs(H[i] - scipy.stats.entropy(np.exp(fin - fin.max()))) < 1e-10
+    assert np.isnan(H[5])
+    # the same rows with the masked entries simply absent
+    np.testing.assert_allclose(H[:5], infokv.topk_entropy(z[:5, :40], 40), atol=1e-12)
+
+
 def test_brute_force_python():
     z = rng.normal(size=(4, 40))
     k = 7
