@@ -457,3 +457,32 @@ def test_decode_attention(dev, Hq, Hkv, length, d, bias):
                                          host_f64(lr[l]) if bias else None, 0.7 if bias else 0.0)
         assert np.max(np.abs(o[l].cpu().numpy() - ro)) <= 1e-3
         assert_rel(lse[l].cpu().numpy(), rl, 1e-4, what="lse")
+
+
+# ----------------------------------------------------------------- random sweep
+def test_infokv_random_sweep(dev):
+    """20 seeded rounds of random shapes for window attention (both output forms,
+    bf16 and float32, one or two tiles per head), representation distance (any
+    width and layer count), select + compact (budgets from 1 to n, ties, window
+    from 0) and fusion."""
+    import random
+    rng = random.Random(97)
+    for _ in range(20):
+        dtype = rng.choice([torch.bfloat16, torch.bfloat16, torch.float32])
+        Hkv, w = rng.choice([1, 2, 4]), rng.randint(1, 64)
+        tph = (w + 31) // 32
+        G = rng.choice([g for g in (1, 2, 3, 4, 8) if g * tph <= 8])
+        if dtype == torch.float32:
+            d = rng.choice([16, 32, 64, 128])
+            while G * w * d * 4 > 65536:
+                d //= 2
+        else:
+            d = rng.choice([64, 128])
+        test_window_attention(dev, (1, G * Hkv, Hkv, rng.randint(w, 3000), w, d, dtype), rng.random() < 0.5)
+        test_repr_distance(dev, (rng.randint(1, 40), rng.randint(1, 400),
+                                 rng.choice([rng.randint(1, 9000), 8 * rng.randint(1, 1100)]),
+                                 rng.choice([torch.bfloat16, torch.float32])))
+        n = rng.randint(1, 5000)
+        test_select_and_compact(dev, (1, rng.randint(1, 4), n, rng.randint(1, n),
+                                      rng.randint(0, min(n, 64)), rng.choice([0, 0, 1, 3, 5])))
+        test_fuse_scores(dev, rng.randint(1, 3), rng.randint(1, 8), rng.randint(1, 30000))
