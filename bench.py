@@ -303,15 +303,34 @@ def main():
         # apart: it checks the compressed cache rather than producing it
         plan.decode_check(inp)
         torch.cuda.synchronize()
-        d0 = torch.cuda.Event(enable_timing=True)
-        d1 = torch.cuda.Event(enable_timing=True)
-        d0.record(stream)
+        dmarks = []
+
+        def dmark(name):
+            ev = torch.cuda.Event(enable_timing=True)
+            ev.record(stream)
+            dmarks.append((name, ev))
+
         for _ in range(args.steps):
-            plan.decode_check(inp)
-        d1.record(stream)
+            plan.decode_check(inp, mark=dmark)
         torch.cuda.synchronize()
-        out["decode_check"] = {"ms": round(d0.elapsed_time(d1) / args.steps, 4),
-                               "timed": "separately, after the steps; not in ms_per_step"}
+        dper = {}
+        for (n0, e0), (n1, e1) in zip(dmarks[:-1], dmarks[1:]):
+            if n1 != "start":
+                dper.setdefault(n1, []).append(e0.elapsed_time(e1))
+        e = 2 if w.dtype == "bf16" else 4
+        L, Hq, Hkv, d = w.layers, w.heads_q, w.heads_kv, w.head_dim
+        m = plan.m[0]
+        # K and V rows read once, ln R once (compacted), the query and the output
+        dbytes = {"decode_compacted": L * Hkv * m * (2 * d * e + 4) + L * Hq * d * (e + 4),
+                  "decode_full": L * Hkv * w.n * 2 * d * e + L * Hq * d * (e + 4)}
+        dec = {}
+        for k, v in dper.items():
+            t = sum(v) / len(v)
+            dec[k] = {"ms": round(t, 4), "alg_bytes": dbytes[k],
+                      "GBps": round(dbytes[k] / (t * 1e-3) / 1e9, 1),
+                      "frac_hbm": round(dbytes[k] / (t * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+        dec["timed"] = "separately, after the steps; not in ms_per_step"
+        out["decode_check"] = dec
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(w, inp)

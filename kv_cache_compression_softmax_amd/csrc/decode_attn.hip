@@ -6,20 +6,51 @@
 // tokens it stands for.  The same kernel over the full and the compacted cache
 // gives the outputs compared by [RECAS] section 2.B's dropped-mass bound.
 //
-// Split over the cache length: a workgroup handles one (layer, KV head, chunk of
-// CK keys) for all G query heads of the group, so each key/value row is read
-// once per group.  LG lanes hold one row (16 bytes each); per key the G dot
-// products are reduced inside the lane group, then an online softmax keeps
-// (max, sum, output) per head.  Lane groups, then waves, are merged in a fixed
-// order; a second kernel merges the chunks.
+// Both kernels split the cache length into chunks and keep, per chunk and query
+// head, the triple (max logit, sum of exp, unnormalised output); a second kernel
+// merges a head's chunks in index order.  Each K/V row is read once per KV head,
+// for all G query heads of its group.
+//
+// decode_mfma (bf16, d = 64 or 128, G <= 4): one wave per chunk of keys, in
+// tiles of 16 keys.  The cache is split into equal chunks (a multiple of 32
+// keys) so that the grid holds about one wave per SIMD (kWaveTarget): one long
+// stream per SIMD ran at 6.7 TB/s where 512-key chunks (13 waves per SIMD)
+// ran at 5.3 TB/s and unequal chunks left SIMDs idle at the end.
+//   * Logits on the matrix core: v_mfma_f32_16x16x32_bf16 with the query heads
+//     on M (row c holds head c mod 4, so every lane sees all four heads of its
+//     key column) and 16 keys on N.  Each lane loads its key row's 16-byte
+//     pieces in the instruction's own k layout: one load instruction reads 64
+//     contiguous bytes of each of 16 rows.
+//   * Online softmax in base 2 once per tile and head: a 16-lane max and one
+//     exp2 per (key, head).  The reference max moves only when a logit passes it
+//     by more than 2^8, so the accumulators are rarely rescaled.  The tile's
+//     probabilities go through LDS (16 bytes per key).
+//   * P V on the vector ALU: lane l owns 8 values of one V row (16-byte loads,
+//     rows d/8 lanes wide), so the output accumulators are 8 per head.
+//   * The next tile's K, V and ln R loads are in flight during this tile's work.
+// decode_partial (the general kernel: float32, other d, G up to 8): a workgroup
+// handles one (layer, KV head, chunk of CK keys); LG lanes hold one row (16
+// bytes each); per key the G dot products are reduced inside the lane group,
+// then an online softmax keeps (max, sum, output) per head.  Lane groups, then
+// waves, are merged in a fixed order.
 #include "common.h"
 
 namespace kvc {
 namespace {
 
 constexpr int NT = 256;
-constexpr int CK = 1024;          // keys per workgroup
+constexpr int CK = 1024;          // keys per workgroup (decode_partial)
+constexpr int kWaveTarget = 1024;  // decode_mfma waves per launch: MI355X's 256 CUs x 4 SIMDs
+constexpr int kSets = 2;           // decode_mfma register sets (tiles) per wave
 constexpr int MAXG = 8;           // query heads per KV head
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LN2 = 0.6931471805599453f;
+constexpr float kLazy = 8.f;     // decode_mfma: rescale threshold, base-2 logits
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 template <typename T> struct DE;
 template <> struct DE<uint16_t> {
@@ -39,7 +70,7 @@ template <> struct DE<float> {
 
 struct DecTables { ConstPtrs q, K, V, logR; };
 
-// partial layout: [lc, Hq, nchunk] x (m, l, o[d])
+// partial layout: [lc, Hq, nchunk] x (m, l, -, -, o[d]), 16-byte aligned rows
 template <typename T, int LG, int G>
 __global__ void __launch_bounds__(NT)
 decode_partial(DecTables t, int Hq, int Hkv, int64_t len, int d, float scale, float alpha_bias,
@@ -129,9 +160,195 @@ decode_partial(DecTables t, int Hq, int Hkv, int64_t len, int d, float scale, fl
       S += sm_l[w2][h] * a;
       O += sm_o[w2][h][e] * a;
     }
-    float* p = part + (((int64_t)l * Hq + g * G + h) * nchunk + ch) * (d + 2);
+    float* p = part + (((int64_t)l * Hq + g * G + h) * nchunk + ch) * (d + 4);
     if (e == 0) { p[0] = M; p[1] = S; }
-    p[2 + e] = O;
+    p[4 + e] = O;
+  }
+}
+
+// One tile's loads: K in MFMA B-operand order (key l%16, d = 32s + 8(l/16) .. +8),
+// V as 4 values per lane (key 16 t/... see decode_mfma), ln R of key l%16.
+template <int D>
+struct DecTile {
+  static constexpr int KB = D / 32;          // 16x16x32 k-blocks per key row
+  static constexpr int VL = D / 8;           // lanes per V row (8 values each)
+  static constexpr int VI = 16 * VL / 64;    // V load instructions per tile
+  bf16x8 k[KB];
+  u32x4 v[VI];
+  float lr;
+};
+
+template <int D, bool BIAS>
+__device__ __forceinline__ void dec_load(DecTile<D>& t, const uint16_t* K, const uint16_t* V,
+                                         const float* lr, int64_t jb, int64_t jlast, int lane) {
+  constexpr int VL = DecTile<D>::VL, KPI = 64 / VL;
+  const int64_t kk = min(jb + (lane & 15), jlast);
+  const uint16_t* kr = K + kk * D + 8 * (lane >> 4);
+#pragma unroll
+  for (int s = 0; s < DecTile<D>::KB; ++s) {
+    const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kr + 32 * s));
+    t.k[s] = __builtin_bit_cast(bf16x8, x);
+  }
+#pragma unroll
+  for (int i = 0; i < DecTile<D>::VI; ++i) {
+    const int64_t kv = min(jb + i * KPI + lane / VL, jlast);
+    t.v[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(V + kv * D + 8 * (lane % VL)));
+  }
+  t.lr = BIAS ? lr[kk] : 0.f;
+}
+
+// partial layout as decode_partial: [lc, Hq, nchunk] x (m, l, -, -, o[d]), m in natural
+// log units.  `nw` = lc * Hkv * nchunk waves in all.
+// Max over the 16 lanes of a DPP row (quad swaps, then half-row and row mirrors).
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false)));
+  return v;
+}
+
+template <int D, bool BIAS>
+__global__ void __launch_bounds__(NT)
+decode_mfma(DecTables t, int Hq, int Hkv, int G, int64_t len, float sl2, float bl2, int nchunk,
+            int64_t ckm, int64_t nw, float* __restrict__ part) {
+  constexpr int KB = DecTile<D>::KB, VL = DecTile<D>::VL, VI = DecTile<D>::VI, KPI = 64 / VL;
+  __shared__ f32x4 sp[NT / 64][16];
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t wid = (int64_t)blockIdx.x * (NT / 64) + wv;
+  if (wid >= nw) return;
+  const int ch = (int)(wid % nchunk);
+  const int g = (int)((wid / nchunk) % Hkv);
+  const int l = (int)(wid / ((int64_t)nchunk * Hkv));
+  const uint16_t* q = (const uint16_t*)t.q.p[l];
+  const uint16_t* K = (const uint16_t*)t.K.p[l] + (int64_t)g * len * D;
+  const uint16_t* V = (const uint16_t*)t.V.p[l] + (int64_t)g * len * D;
+  const float* lr = BIAS ? (const float*)t.logR.p[l] + (int64_t)g * len : nullptr;
+
+  // A operand: row c = lane % 16 holds query head c % 4 (zero if that head is >= G)
+  bf16x8 qa[KB];
+  {
+    const int h = (lane & 15) & 3;
+    const unsigned keep = h < G ? ~0u : 0u;
+    const uint16_t* qr = q + (int64_t)(g * G + (h < G ? h : 0)) * D + 8 * (lane >> 4);
+#pragma unroll
+    for (int s = 0; s < KB; ++s) {
+      u32x4 x = *reinterpret_cast<const u32x4*>(qr + 32 * s);
+      x &= keep;
+      qa[s] = __builtin_bit_cast(bf16x8, x);
+    }
+  }
+  const int64_t j0 = (int64_t)ch * ckm, j1 = min(len, j0 + ckm), jlast = j1 - 1;
+  const int ntile = (int)((j1 - j0 + 15) / 16);
+  float m[4], ls[4], o[4][8];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    m[e] = -INFINITY; ls[e] = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[e][i] = 0.f;
+  }
+  // one tile: logits on the matrix core, online softmax, P V on the vector ALU
+  auto tile = [&](const DecTile<D>& c, int64_t jb) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < KB; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[s], c.k[s], acc, 0, 0, 0);
+    // this lane: key jb + lane % 16, head e in acc[e]
+    const bool valid = jb + (lane & 15) <= jlast;
+    const float b = BIAS ? bl2 * c.lr : 0.f;
+    // The reference max m moves only when a logit exceeds it by more than
+    // kLazy (base 2), so probabilities stay below 2^kLazy and the accumulators
+    // are rescaled on few tiles (always on the first, where m = -inf).  The tile
+    // max is the same in all four rows of 16 lanes, so the branch is uniform.
+    float x[4], tm[4];
+    bool grow = false;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[e] = valid ? acc[e] * sl2 + b : -INFINITY;
+      tm[e] = row16_max(x[e]);                          // finite: a tile holds a valid key
+      grow |= tm[e] > m[e] + kLazy;
+    }
+    if (__builtin_amdgcn_ballot_w64(grow)) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float mn = fmaxf(m[e], tm[e]);
+        const float al = __builtin_amdgcn_exp2f(m[e] - mn);   // 0 when m = -inf
+        m[e] = mn;
+        ls[e] *= al;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) o[e][i] *= al;
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      // v_exp_f32 without the denormal path: a probability below 2^-126 of the
+      // largest is flushed to 0
+      x[e] = __builtin_amdgcn_exp2f(x[e] - m[e]);
+      ls[e] += x[e];
+    }
+    if (lane < 16) sp[wv][lane] = f32x4{x[0], x[1], x[2], x[3]};
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int i = 0; i < VI; ++i) {
+      const f32x4 p = sp[wv][i * KPI + lane / VL];
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) { v[2 * u] = bf16_lo(c.v[i][u]); v[2 * u + 1] = bf16_hi(c.v[i][u]); }
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int u = 0; u < 8; ++u) o[e][u] += p[e] * v[u];
+    }
+    // the products are complete here: nothing of this tile is sunk below the
+    // refill of its register set (which would rename the set)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+      for (int u = 0; u < 8; ++u) asm volatile("" : "+v"(o[e][u]));
+    asm volatile("" ::: "memory");
+  };
+  // tiles from a ring of kSets register sets, kSets - 1 tiles' loads always in
+  // flight.  Loads past the chunk's last tile are clamped to it (a re-read of rows
+  // just fetched); a tile past the end is fully masked and changes nothing.
+  const int64_t jl = j0 + (int64_t)(ntile - 1) * 16;      // the last tile
+  DecTile<D> ts[kSets];
+#pragma unroll
+  for (int u = 0; u + 1 < kSets; ++u) dec_load<D, BIAS>(ts[u], K, V, lr, min(j0 + 16 * u, jl), jlast, lane);
+  for (int ti = 0; ti < ntile; ti += kSets) {
+    const int64_t jb = j0 + (int64_t)ti * 16;
+#pragma unroll
+    for (int u = 0; u < kSets; ++u) {
+      // the scheduling barrier keeps each refill below the last use of the set it
+      // overwrites (otherwise the sets are renamed and copied, with a wait per copy)
+      __builtin_amdgcn_sched_barrier(0);
+      dec_load<D, BIAS>(ts[(u + kSets - 1) % kSets], K, V, lr, min(jb + 16 * (u + kSets - 1), jl), jlast, lane);
+      asm volatile("" ::: "memory");
+      tile(ts[u], jb + 16 * u);
+    }
+  }
+  // sum of exp per head over the 16 key lanes; output over the lanes sharing a d-slice
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    ls[e] += __shfl_xor(ls[e], 1, 64);
+    ls[e] += __shfl_xor(ls[e], 2, 64);
+    ls[e] += __shfl_xor(ls[e], 4, 64);
+    ls[e] += __shfl_xor(ls[e], 8, 64);
+#pragma unroll
+    for (int off = VL; off < 64; off <<= 1)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) o[e][i] += __shfl_xor(o[e][i], off, 64);
+  }
+  if (lane < VL) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (e >= G) break;
+      float* p = part + (((int64_t)l * Hq + g * G + e) * nchunk + ch) * (D + 4);
+      if (lane == 0) { p[0] = m[e] * LN2; p[1] = ls[e]; }
+      *reinterpret_cast<float4*>(p + 4 + 8 * lane) = make_float4(o[e][0], o[e][1], o[e][2], o[e][3]);
+      *reinterpret_cast<float4*>(p + 8 + 8 * lane) = make_float4(o[e][4], o[e][5], o[e][6], o[e][7]);
+    }
   }
 }
 
@@ -139,23 +356,35 @@ __global__ void decode_combine(const float* __restrict__ part, int nchunk, int d
                                float* __restrict__ o, float* __restrict__ lse) {
   const int64_t hh = blockIdx.x;                 // (layer, query head)
   if (hh >= nhead) return;
-  const float* p = part + hh * nchunk * (d + 2);
+  const float* p = part + hh * nchunk * (d + 4);
   float M = -INFINITY;
-  for (int c = 0; c < nchunk; ++c) M = fmaxf(M, p[(int64_t)c * (d + 2)]);
+  for (int c = 0; c < nchunk; ++c) M = fmaxf(M, p[(int64_t)c * (d + 4)]);
   float S = 0.f;
   for (int c = 0; c < nchunk; ++c) {
-    const float* pc = p + (int64_t)c * (d + 2);
+    const float* pc = p + (int64_t)c * (d + 4);
     S += pc[1] * (M > -INFINITY ? expf(pc[0] - M) : 0.f);
   }
   for (int e = threadIdx.x; e < d; e += blockDim.x) {
     float O = 0.f;
     for (int c = 0; c < nchunk; ++c) {
-      const float* pc = p + (int64_t)c * (d + 2);
-      O += pc[2 + e] * (M > -INFINITY ? expf(pc[0] - M) : 0.f);
+      const float* pc = p + (int64_t)c * (d + 4);
+      O += pc[4 + e] * (M > -INFINITY ? expf(pc[0] - M) : 0.f);
     }
     o[hh * d + e] = O / S;
   }
   if (lse && threadIdx.x == 0) lse[hh] = M + logf(S);
+}
+
+// decode_mfma's chunks per (layer, KV head): about kWaveTarget waves in all,
+// at least 32 keys each.  The chunk length is then ceil(len / nchunk) rounded up
+// to whole rings of kSets tiles.
+int64_t mfma_chunks(int lc, int Hkv, int64_t len) {
+  const int64_t per = (kWaveTarget + (int64_t)lc * Hkv - 1) / ((int64_t)lc * Hkv);
+  return max((int64_t)1, min(per, (len + 31) / 32));
+}
+int64_t mfma_chunk_len(int64_t len, int64_t nchunk) {
+  constexpr int q = 16 * kSets;
+  return ((len + nchunk - 1) / nchunk + q - 1) / q * q;
 }
 
 template <typename T, int LG>
@@ -193,9 +422,15 @@ using namespace kvc;
 
 extern "C" size_t kvc_decode_attn_workspace_size(int L, int Hq, int64_t len, int d) {
   if (L < 1 || Hq < 1 || len < 1 || d < 1) return 0;
+  // partials of one launch (at most kLayersPerLaunch layers), for either kernel and
+  // any Hkv >= 1; the last launch of L layers may cover fewer layers
+  auto launch_bytes = [&](int lc) {
+    const int64_t nchunk = max((len + CK - 1) / CK, mfma_chunks(lc, 1, len));
+    return (size_t)lc * Hq * nchunk * (d + 4) * sizeof(float);
+  };
   const int lc = L < kLayersPerLaunch ? L : kLayersPerLaunch;
-  const int64_t nchunk = (len + CK - 1) / CK;
-  return (size_t)lc * Hq * nchunk * (d + 2) * sizeof(float) + 256;
+  const int rest = L % kLayersPerLaunch;
+  return max(launch_bytes(lc), rest ? launch_bytes(rest) : (size_t)0) + 256;
 }
 
 extern "C" int kvc_decode_attn(const void* const* q, const void* const* K, const void* const* V,
@@ -223,9 +458,10 @@ extern "C" int kvc_decode_attn(const void* const* q, const void* const* K, const
   if (!ws || ws_bytes < need)
     return KVC_FAIL(KVC_ERR_WORKSPACE, "kvc_decode_attn: workspace needs %zu bytes", need);
   float* part = (float*)(((uintptr_t)ws + 255) & ~(uintptr_t)255);
-  const int nchunk = (int)((len + CK - 1) / CK);
   hipStream_t s = as_stream(stream);
   const int G = Hq / Hkv;
+  const bool mfma = dtype == KVC_BF16 && G <= 4 && (d == 64 || d == 128);
+  const int nchunk_g = (int)((len + CK - 1) / CK);
   for (int l0 = 0; l0 < L; l0 += kLayersPerLaunch) {
     const int lc = min(kLayersPerLaunch, L - l0);
     DecTables t{};
@@ -233,9 +469,22 @@ extern "C" int kvc_decode_attn(const void* const* q, const void* const* K, const
       t.q.p[i] = q[l0 + i]; t.K.p[i] = K[l0 + i]; t.V.p[i] = V[l0 + i];
       t.logR.p[i] = logR ? logR[l0 + i] : nullptr;
     }
-    const dim3 grid((unsigned)((int64_t)lc * Hkv * nchunk));
-    if (dtype == KVC_BF16) launch_dec<uint16_t>(LG, G, grid, s, t, Hq, Hkv, len, d, scale, alpha_bias, nchunk, part);
-    else launch_dec<float>(LG, G, grid, s, t, Hq, Hkv, len, d, scale, alpha_bias, nchunk, part);
+    int nchunk = nchunk_g;
+    if (mfma) {
+      const int64_t ckm = mfma_chunk_len(len, mfma_chunks(lc, Hkv, len));
+      nchunk = (int)((len + ckm - 1) / ckm);
+      const int64_t nw = (int64_t)lc * Hkv * nchunk;
+      const dim3 grid((unsigned)((nw + NT / 64 - 1) / (NT / 64)));
+      const float sl2 = scale * LOG2E, bl2 = alpha_bias * LOG2E;
+#define KVC_M(DD, BB) hipLaunchKernelGGL((decode_mfma<DD, BB>), grid, dim3(NT), 0, s, t, Hq, Hkv, G, len, sl2, bl2, nchunk, ckm, nw, part)
+      if (d == 128) { if (logR) KVC_M(128, true); else KVC_M(128, false); }
+      else { if (logR) KVC_M(64, true); else KVC_M(64, false); }
+#undef KVC_M
+    } else {
+      const dim3 grid((unsigned)((int64_t)lc * Hkv * nchunk));
+      if (dtype == KVC_BF16) launch_dec<uint16_t>(LG, G, grid, s, t, Hq, Hkv, len, d, scale, alpha_bias, nchunk, part);
+      else launch_dec<float>(LG, G, grid, s, t, Hq, Hkv, len, d, scale, alpha_bias, nchunk, part);
+    }
     const int64_t nhead = (int64_t)lc * Hq;
     hipLaunchKernelGGL(decode_combine, dim3((unsigned)nhead), dim3(128), 0, s, (const float*)part, nchunk,
                        d, nhead, o_out + (int64_t)l0 * Hq * d, lse_out ? lse_out + (int64_t)l0 * Hq : nullptr);

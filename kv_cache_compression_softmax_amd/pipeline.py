@@ -142,17 +142,30 @@ class SelKVPlan:
         mark("merge_gated")
         return self
 
-    def decode_check(self, inp: dict, stream=None):
+    def _decode_buffers(self):
+        if getattr(self, "_dec", None) is None:
+            w = self.w
+            L, Hq, d, dev = w.layers, w.heads_q, w.head_dim, self.U.device
+            f32 = torch.float32
+            nbytes = B.kvc_decode_attn_workspace_size(L, Hq, w.n, d)   # the full length bounds both
+            self._dec = (torch.empty(L, Hq, d, dtype=f32, device=dev), torch.empty(L, Hq, dtype=f32, device=dev),
+                         torch.empty(L, Hq, d, dtype=f32, device=dev), torch.empty(L, Hq, dtype=f32, device=dev),
+                         torch.empty(max(1, nbytes), dtype=torch.uint8, device=dev))
+        return self._dec
+
+    def decode_check(self, inp: dict, stream=None, mark=None):
         """Compensated decode over the compacted cache and plain decode over the
-        full cache, one query per head and layer: (o', lse', o, lse)."""
+        full cache, one query per head and layer: (o', lse', o, lse).  The output
+        buffers are the plan's own (allocated on the first call) and are
+        overwritten by the next call."""
         w = self.w
-        L, Hq, d = w.layers, w.heads_q, w.head_dim
-        q = [inp["q_dec"][l] for l in range(L)]
-        o_c = torch.empty(L, Hq, d, dtype=torch.float32, device=self.U.device)
-        l_c = torch.empty(L, Hq, dtype=torch.float32, device=self.U.device)
-        o_f = torch.empty_like(o_c)
-        l_f = torch.empty_like(l_c)
+        mark = mark or (lambda name: None)
+        q = [inp["q_dec"][l] for l in range(w.layers)]
+        o_c, l_c, o_f, l_f, ws = self._decode_buffers()
+        mark("start")
         B.kvc_decode_attn(q, self.Kc, self.Vc, self.logR, w.alpha_bias, self.scale, o_c, l_c,
-                          stream=stream)
-        B.kvc_decode_attn(q, inp["k"], inp["v"], None, 0.0, self.scale, o_f, l_f, stream=stream)
+                          ws=ws, stream=stream)
+        mark("decode_compacted")
+        B.kvc_decode_attn(q, inp["k"], inp["v"], None, 0.0, self.scale, o_f, l_f, ws=ws, stream=stream)
+        mark("decode_full")
         return o_c, l_c, o_f, l_f

@@ -439,14 +439,26 @@ def _selkv_pieces(dev, case, dtype):
 
 
 # ----------------------------------------------------------------- decode
-@pytest.mark.parametrize("Hq,Hkv,length,d,bias", [(32, 8, 3000, 128, True), (4, 2, 100, 64, False),
-                                                  (8, 8, 1025, 128, True), (6, 2, 2049, 64, True)])
-def test_decode_attention(dev, Hq, Hkv, length, d, bias):
+# bf16 with d in {64, 128} and G <= 4 runs the matrix-core kernel (16-key tiles,
+# 512-key chunks): lengths cover one key, ragged tiles, whole and ragged chunks;
+# float32, G > 4 and d = 256 run the general kernel.
+DECODE_CASES = [(32, 8, 3000, 128, True, torch.bfloat16), (4, 2, 100, 64, False, torch.bfloat16),
+                (8, 8, 1025, 128, True, torch.bfloat16), (6, 2, 2049, 64, True, torch.bfloat16),
+                (4, 1, 1, 128, True, torch.bfloat16), (8, 2, 15, 128, False, torch.bfloat16),
+                (8, 4, 16, 128, True, torch.bfloat16), (4, 2, 17, 64, True, torch.bfloat16),
+                (32, 8, 512, 128, True, torch.bfloat16), (32, 8, 513, 128, False, torch.bfloat16),
+                (12, 4, 1023, 128, True, torch.bfloat16), (2, 1, 4097, 64, True, torch.bfloat16),
+                (16, 2, 700, 128, True, torch.bfloat16), (4, 2, 300, 256, True, torch.bfloat16),
+                (8, 2, 777, 64, True, torch.float32), (4, 4, 33, 128, False, torch.float32)]
+
+
+@pytest.mark.parametrize("Hq,Hkv,length,d,bias,dtype", DECODE_CASES)
+def test_decode_attention(dev, Hq, Hkv, length, d, bias, dtype):
     L = 2
-    announce("decode", Hq, Hkv, length, d, bias)
-    q = [gen((Hq, d), 300 + l, dev) for l in range(L)]
-    K = [gen((Hkv, length, d), 320 + l, dev) for l in range(L)]
-    V = [gen((Hkv, length, d), 340 + l, dev) for l in range(L)]
+    announce("decode", Hq, Hkv, length, d, bias, dtype)
+    q = [gen((Hq, d), 300 + l, dev, dtype) for l in range(L)]
+    K = [gen((Hkv, length, d), 320 + l, dev, dtype) for l in range(L)]
+    V = [gen((Hkv, length, d), 340 + l, dev, dtype) for l in range(L)]
     lr = [torch.rand(Hkv, length, device=dev) * 2 for _ in range(L)] if bias else None
     o = torch.empty(L, Hq, d, device=dev)
     lse = torch.empty(L, Hq, device=dev)
