@@ -69,6 +69,7 @@ KERNEL_SOURCES = {
     "window_attn": ["window_attn.hip"], "fuse_scores": ["fuse_scores.hip"],
     "select_topk": ["select_topk.hip"], "compact": ["compact.hip"],
     "vatp_union": ["selkv.hip"], "merge_gated": ["selkv.hip"],
+    "decode_compacted": ["decode_attn.hip"], "decode_full": ["decode_attn.hip"],
 }
 
 
@@ -79,8 +80,6 @@ def source_digest(kernel):
     for f in KERNEL_SOURCES.get(kernel, []) + ["common.h"]:
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(fh.read())
-    with open(os.path.join(ROOT, "include", "kvc.h"), "rb") as fh:
-        h.update(fh.read())
     return h.hexdigest()[:16]
 
 
@@ -328,7 +327,8 @@ def main():
             t = sum(v) / len(v)
             dec[k] = {"ms": round(t, 4), "alg_bytes": dbytes[k],
                       "GBps": round(dbytes[k] / (t * 1e-3) / 1e9, 1),
-                      "frac_hbm": round(dbytes[k] / (t * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+                      "frac_hbm": round(dbytes[k] / (t * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                      "traffic": measured_traffic(w.name, k)}
         dec["timed"] = "separately, after the steps; not in ms_per_step"
         out["decode_check"] = dec
     if not args.no_cpu_baseline:
