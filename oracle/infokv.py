@@ -28,6 +28,13 @@ Readings taken where the page is silent or garbled (listed again in the design doc):
     goes to the highest S, ties to the lower index; output indices ascend.
   * Budgets round down; the adaptive budget gives the remainder to the lowest
     layer indices.
+  * Compression during decoding (the Technical-detail section applies it at
+    prefill and again every 1024 generated tokens): each period re-scores the
+    cache as it stands -- the kept slots of every (layer, KV head) followed by
+    the new tokens -- with the same S, a fresh window (the last w new tokens)
+    and the same budget.  A kept slot reuses the E = D * H its token had; a new
+    token's E comes from its own logits row and hidden states.  Kept sets differ
+    per KV head, so the softmax of E runs over each head's own slots.
 """
 from __future__ import annotations
 
@@ -286,3 +293,53 @@ def infokv_layer(q_win, k, D_l, H, alpha: float, k_keep: int, w: int,
     S32 = S.astype(np.float32)
     idx = select_topk(S32, k_keep, w)
     return A, S, S32, Ebar, idx
+
+
+def fuse_scores_slots(A: np.ndarray, E: np.ndarray, alpha: float):
+    """Importance fusion over the cache slots of one layer, one row per KV head
+    ([InfoKV] Method: the fusion formula; Technical detail: compression during
+    decoding).
+
+    E[g, j] is the entropy score of the token held by slot j of head g;
+    sigma[g] = softmax of E[g] over the head's slots;
+    S[g, j] = alpha * A[g, j] + (1 - alpha) * sigma[g, j].  Ebar = mean of E.
+    Returns (S [Hkv, n], Ebar, sigma [Hkv, n]).
+    """
+    A = np.asarray(A, dtype=np.float64)
+    E = np.asarray(E, dtype=np.float64)
+    sigma = np.empty_like(E)
+    for g in range(E.shape[0]):
+        e = np.exp(E[g] - E[g].max())
+        sigma[g] = e / e.sum()
+    S = alpha * A + (1.0 - alpha) * sigma
+    return S, float(E.mean()), sigma
+
+
+def recompress_period(q_win, K_cache, V_cache, E_kept, D_new, H_new, alpha: float,
+                      k_keep: int, w: int, scale: float | None = None):
+    """One period of compression during decoding, for one layer ([InfoKV]
+    Technical detail: compression every 1024 generated tokens; Method).
+
+    K_cache, V_cache [Hkv, k_old + t, d]: each head's kept slots (ascending
+    positions) followed by the t new tokens.  E_kept [Hkv, k_old]: the entropy
+    scores the kept slots carry.  D_new [t], H_new [t]: the new tokens'
+    representation distance at this layer and top-k entropy.  q_win [Hq, w, d]:
+    the fresh window, the queries of the last w new tokens.
+
+    E = [E_kept | D_new * H_new] per head; A = window attention over the cache;
+    S = fuse_scores_slots(A, E); the k_keep slots kept per head (the last w
+    always); the kept slots' K, V and E are gathered in slot order.
+    Returns a dict with A, E, S, S32, idx, Kc, Vc, E_next.
+    """
+    E_kept = np.asarray(E_kept, dtype=np.float64)
+    e_new = np.asarray(D_new, dtype=np.float64) * np.asarray(H_new, dtype=np.float64)
+    Hkv = E_kept.shape[0]
+    E = np.concatenate([E_kept, np.repeat(e_new[None, :], Hkv, axis=0)], axis=1)
+    A = window_attention(q_win, K_cache, scale)
+    S, _, _ = fuse_scores_slots(A, E, alpha)
+    S32 = S.astype(np.float32)
+    idx = select_topk(S32, k_keep, w)
+    Kc, Vc = compact(K_cache, V_cache, idx)
+    E_next = np.take_along_axis(E, idx.astype(np.int64), axis=1)
+    return {"A": A, "E": E, "S": S, "S32": S32, "idx": idx, "Kc": Kc, "Vc": Vc,
+            "E_next": E_next}
