@@ -128,6 +128,39 @@ int kvc_fuse_scores(const float* A, const float* D, const float* H, int L, int H
                     void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Importance fusion over cache slots, for compression repeated during decoding
+ * ([InfoKV] Technical detail: compression is applied at prefill and again during
+ * decoding, e.g. every 1024 generated tokens; Method: the fusion formula).
+ * After a compaction each KV head holds its own token set, so the entropy score
+ * is a row per (layer, KV head): slot j of head g carries E = D * H of the token
+ * it holds (kept slots keep the value they had; new tokens get it from
+ * kvc_append_entropy_scores).  Per (l, g):
+ *   S_out[l, g, j] = alpha_fuse * A[l, g, j] + (1 - alpha_fuse) * softmax_j(E[l, g, :])
+ *   Ebar_out[l]    = mean of E[l, :, :] over heads and slots
+ * With equal rows across heads this is kvc_fuse_scores' result.
+ *   A, E       device float32 [L, Hkv, n];  S_out device float32 [L, Hkv, n].
+ *   Ebar_out   device float32 [L], or NULL.
+ *   n >= 1; L * Hkv <= 65535; 0 <= alpha_fuse <= 1.
+ */
+size_t kvc_fuse_scores_slots_workspace_size(int L, int Hkv, int64_t n);
+int kvc_fuse_scores_slots(const float* A, const float* E, int L, int Hkv, int64_t n,
+                          float alpha_fuse, float* S_out, float* Ebar_out, void* ws,
+                          size_t ws_bytes, void* stream);
+
+/*
+ * Entropy scores of newly generated tokens appended to the slot rows
+ * ([InfoKV] Method: E = D * H; Technical detail: compression during decoding):
+ *   E[l, g, offset + i] = D[l, i] * H[i]   for every KV head g and i < t
+ * so the old slots' scores are reused and only the new tokens' H and D are
+ * computed (kvc_topk_entropy and kvc_repr_distance over their rows).
+ *   D          device float32 [L, t];  H device float32 [t].
+ *   E          device float32 [L, Hkv, cap]; slots [offset, offset + t) written.
+ *   t >= 1; 0 <= offset; offset + t <= cap; L * Hkv <= 65535.
+ */
+int kvc_append_entropy_scores(const float* D, const float* H, int L, int Hkv, int64_t t,
+                              float* E, int64_t cap, int64_t offset, void* stream);
+
+/*
  * Uniform layer budget ([InfoKV] Contributions, Technical detail; host only):
  * k = floor(keep_fraction * n), clamped to [w, n].  Writes *k_out.
  */
@@ -172,6 +205,20 @@ int kvc_select_topk(const float* S, int L, int Hkv, int64_t n, const int64_t* k_
 int kvc_compact(const void* const* K, const void* const* V, int dtype, int L, int Hkv,
                 int64_t n, int d, const int32_t* const* idx, const int64_t* k_keep,
                 void* const* K_out, void* const* V_out, void* stream);
+
+/*
+ * kvc_compact with a fixed output head stride, for a cache that keeps growing
+ * after the compaction ([InfoKV] Technical detail: compression during decoding):
+ *   K_out[l][g * out_rows + j, :] = K[l][g, idx[l][g, j], :], same for V,
+ * so each head's kept rows fill the front of an [Hkv, out_rows, d] buffer and
+ * rows [k_keep[l], out_rows) stay free for the tokens decoded next.  With d = 1
+ * and float32 it gathers per-slot scores (kvc_fuse_scores_slots' E rows).
+ *   Arguments as kvc_compact; out_rows >= every k_keep[l].  The outputs must not
+ *   overlap the inputs.
+ */
+int kvc_compact_into(const void* const* K, const void* const* V, int dtype, int L, int Hkv,
+                     int64_t n, int d, const int32_t* const* idx, const int64_t* k_keep,
+                     int64_t out_rows, void* const* K_out, void* const* V_out, void* stream);
 
 /*
  * VATP importance and its GQA union ([SelKV] section 2, pipeline steps 1-2):

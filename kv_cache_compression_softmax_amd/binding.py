@@ -41,6 +41,11 @@ _SIGNATURES = {
     "kvc_vatp_union": ([_vp, _vp, _i32, _i32, _i32, _i32, _i64, _i32, _vp, _vp, _vp], _i32),
     "kvc_merge_gated": ([_vp, _vp, _i32, _vp, _i32, _i32, _i64, _i32, _vp, _c_i64p, _i32, _vp, _vp,
                          _vp, _vp], _i32),
+    "kvc_compact_into": ([_vp, _vp, _i32, _i32, _i32, _i64, _i32, _vp, _c_i64p, _i64, _vp, _vp, _vp],
+                         _i32),
+    "kvc_fuse_scores_slots_workspace_size": ([_i32, _i32, _i64], _sz),
+    "kvc_fuse_scores_slots": ([_vp, _vp, _i32, _i32, _i64, _f32, _vp, _vp, _vp, _sz, _vp], _i32),
+    "kvc_append_entropy_scores": ([_vp, _vp, _i32, _i32, _i64, _vp, _i64, _i64, _vp], _i32),
     "kvc_decode_attn_workspace_size": ([_i32, _i32, _i64, _i32], _sz),
     "kvc_decode_attn": ([_vp, _vp, _vp, _i32, _vp, _f32, _i32, _i32, _i32, _i64, _i32, _f32, _vp,
                          _vp, _vp, _sz, _vp], _i32),
@@ -228,6 +233,56 @@ def kvc_compact(K, V, idx, k_keep, K_out, V_out, stream=None):
         kp, vp[0] if vp else None, _dtype(K[0]), L, Hkv, n, d, ip, _i64s(k_keep), kop,
         vop[0] if vop else None, _stream(stream)))
     return K_out, V_out
+
+
+def kvc_compact_into(K, V, idx, k_keep, K_out, V_out, stream=None):
+    """K_out[l][g, j] = K[l][g, idx[l][g, j]] for j < k_keep[l] (and V), where
+    K_out[l] is [Hkv, out_rows, d]: rows past k_keep[l] are left as they are."""
+    L = len(K)
+    Hkv, n, d = K[0].shape
+    out_rows = K_out[0].shape[1]
+    dt = K[0].dtype
+    for t in K_out + (V_out or []):
+        if tuple(t.shape) != (Hkv, out_rows, d):
+            raise ValueError("K_out / V_out must all be [Hkv, out_rows, d]")
+    kp, a1 = _ptrs(K, dt)
+    vp = _ptrs(V, dt)
+    ip, a2 = _ptrs(idx, torch.int32)
+    kop, a3 = _ptrs(K_out, dt)
+    vop = _ptrs(V_out, dt)
+    _check("kvc_compact_into", lib().kvc_compact_into(
+        kp, vp[0] if vp else None, _dtype(K[0]), L, Hkv, n, d, ip, _i64s(k_keep), out_rows, kop,
+        vop[0] if vop else None, _stream(stream)))
+    return K_out, V_out
+
+
+def kvc_fuse_scores_slots_workspace_size(L, Hkv, n) -> int:
+    return lib().kvc_fuse_scores_slots_workspace_size(L, Hkv, n)
+
+
+def kvc_fuse_scores_slots(A, E, alpha_fuse: float, S_out, Ebar_out=None, ws=None, stream=None):
+    """S_out [L, Hkv, n] = alpha*A + (1-alpha)*softmax over each row of E [L, Hkv, n]."""
+    L, Hkv, n = A.shape
+    if tuple(E.shape) != (L, Hkv, n):
+        raise ValueError("E must be shaped like A")
+    ws = _ws(kvc_fuse_scores_slots_workspace_size(L, Hkv, n), A.device, ws)
+    _check("kvc_fuse_scores_slots", lib().kvc_fuse_scores_slots(
+        _ptr(A, torch.float32), _ptr(E, torch.float32), L, Hkv, n, alpha_fuse,
+        _ptr(S_out, torch.float32), _ptr(Ebar_out, torch.float32) if Ebar_out is not None else None,
+        _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+    return S_out
+
+
+def kvc_append_entropy_scores(D, H, E, offset: int, stream=None):
+    """E[l, g, offset + i] = D[l, i] * H[i] for every KV head g; E is [L, Hkv, cap]."""
+    L, t = D.shape
+    _, Hkv, cap = E.shape
+    if H.shape[0] != t or E.shape[0] != L:
+        raise ValueError("shape mismatch")
+    _check("kvc_append_entropy_scores", lib().kvc_append_entropy_scores(
+        _ptr(D, torch.float32), _ptr(H, torch.float32), L, Hkv, t, _ptr(E, torch.float32), cap,
+        offset, _stream(stream)))
+    return E
 
 
 def kvc_vatp_union(A_hq: torch.Tensor, V, U_out: torch.Tensor, Ag_out: torch.Tensor, stream=None):

@@ -21,6 +21,7 @@ struct Tables {
   ConstPtrs K, V, idx;
   MutPtrs Ko, Vo;
   I64s k;
+  I64s orows;                   // output rows per KV head (the head stride of K_out, V_out)
   I64s blk0;                    // first block of each layer
 };
 
@@ -38,8 +39,8 @@ compact_kernel(Tables t, int lc, int Hkv, int64_t n, int rowbytes) {
   const int32_t* idx = (const int32_t*)t.idx.p[l] + (int64_t)g * k;
   const char* K = (const char*)t.K.p[l] + (int64_t)g * n * rowbytes;
   const char* V = t.V.p[l] ? (const char*)t.V.p[l] + (int64_t)g * n * rowbytes : nullptr;
-  char* Ko = (char*)t.Ko.p[l] + (int64_t)g * k * rowbytes;
-  char* Vo = V ? (char*)t.Vo.p[l] + (int64_t)g * k * rowbytes : nullptr;
+  char* Ko = (char*)t.Ko.p[l] + (int64_t)g * t.orows.v[l] * rowbytes;
+  char* Vo = V ? (char*)t.Vo.p[l] + (int64_t)g * t.orows.v[l] * rowbytes : nullptr;
   if (VEC) {
     const int lpr = rowbytes / 16;                 // lanes per row
     const int rpi = NT / lpr;                      // rows per iteration
@@ -70,23 +71,26 @@ compact_kernel(Tables t, int lc, int Hkv, int64_t n, int rowbytes) {
 
 using namespace kvc;
 
-extern "C" int kvc_compact(const void* const* K, const void* const* V, int dtype, int L, int Hkv,
-                           int64_t n, int d, const int32_t* const* idx, const int64_t* k_keep,
-                           void* const* K_out, void* const* V_out, void* stream) {
+namespace {
+
+int compact_impl(const char* fn, const void* const* K, const void* const* V, int dtype, int L,
+                 int Hkv, int64_t n, int d, const int32_t* const* idx, const int64_t* k_keep,
+                 int64_t out_rows, void* const* K_out, void* const* V_out, void* stream) {
   clear_error();
-  if (!dtype_ok(dtype)) return KVC_FAIL(KVC_ERR_DTYPE, "kvc_compact: dtype %d", dtype);
-  KVC_REQUIRE(L >= 1 && L <= KVC_MAX_LAYERS, "kvc_compact: need 1 <= L <= %d", KVC_MAX_LAYERS);
-  KVC_REQUIRE(Hkv >= 1 && n >= 1 && d >= 1 && d <= 4096, "kvc_compact: need Hkv, n >= 1 and 1 <= d <= 4096");
-  KVC_REQUIRE(K && idx && k_keep && K_out, "kvc_compact: null pointer");
-  KVC_REQUIRE((V == nullptr) == (V_out == nullptr), "kvc_compact: V and V_out must both be set or both NULL");
+  if (!dtype_ok(dtype)) return KVC_FAIL(KVC_ERR_DTYPE, "%s: dtype %d", fn, dtype);
+  KVC_REQUIRE(L >= 1 && L <= KVC_MAX_LAYERS, "%s: need 1 <= L <= %d", fn, KVC_MAX_LAYERS);
+  KVC_REQUIRE(Hkv >= 1 && n >= 1 && d >= 1 && d <= 4096, "%s: need Hkv, n >= 1 and 1 <= d <= 4096", fn);
+  KVC_REQUIRE(K && idx && k_keep && K_out, "%s: null pointer", fn);
+  KVC_REQUIRE((V == nullptr) == (V_out == nullptr), "%s: V and V_out must both be set or both NULL", fn);
   KVC_REQUIRE((int64_t)kLayersPerLaunch * Hkv * ((n + ROWS - 1) / ROWS) <= 0x7fffffffLL,
-              "kvc_compact: too many rows for one launch");
+              "%s: too many rows for one launch", fn);
   const int rowbytes = d * dtype_size(dtype);
   bool vec = rowbytes % 16 == 0 && rowbytes / 16 <= NT;
   for (int l = 0; l < L; ++l) {
-    KVC_REQUIRE(K[l] && idx[l] && K_out[l], "kvc_compact: null pointer in layer %d", l);
-    KVC_REQUIRE(!V || (V[l] && V_out[l]), "kvc_compact: null V pointer in layer %d", l);
-    KVC_REQUIRE(k_keep[l] >= 1 && k_keep[l] <= n, "kvc_compact: k_keep[%d] outside [1, n]", l);
+    KVC_REQUIRE(K[l] && idx[l] && K_out[l], "%s: null pointer in layer %d", fn, l);
+    KVC_REQUIRE(!V || (V[l] && V_out[l]), "%s: null V pointer in layer %d", fn, l);
+    KVC_REQUIRE(k_keep[l] >= 1 && k_keep[l] <= n, "%s: k_keep[%d] outside [1, n]", fn, l);
+    KVC_REQUIRE(out_rows <= 0 || k_keep[l] <= out_rows, "%s: k_keep[%d] > out_rows", fn, l);
     vec = vec && (uintptr_t)K[l] % 16 == 0 && (uintptr_t)K_out[l] % 16 == 0;
     if (V) vec = vec && (uintptr_t)V[l] % 16 == 0 && (uintptr_t)V_out[l] % 16 == 0;
   }
@@ -102,11 +106,32 @@ extern "C" int kvc_compact(const void* const* K, const void* const* V, int dtype
       t.Ko.p[i] = K_out[l0 + i];
       t.Vo.p[i] = V ? V_out[l0 + i] : nullptr;
       t.k.v[i] = k_keep[l0 + i];
+      t.orows.v[i] = out_rows > 0 ? out_rows : k_keep[l0 + i];
       t.blk0.v[i] = blocks;
       blocks += (int64_t)Hkv * ((k_keep[l0 + i] + ROWS - 1) / ROWS);
     }
     if (vec) hipLaunchKernelGGL(compact_kernel<true>, dim3((unsigned)blocks), dim3(NT), 0, s, t, lc, Hkv, n, rowbytes);
     else hipLaunchKernelGGL(compact_kernel<false>, dim3((unsigned)blocks), dim3(NT), 0, s, t, lc, Hkv, n, rowbytes);
   }
-  return launch_status("kvc_compact");
+  return launch_status(fn);
+}
+
+}  // namespace
+
+extern "C" int kvc_compact(const void* const* K, const void* const* V, int dtype, int L, int Hkv,
+                           int64_t n, int d, const int32_t* const* idx, const int64_t* k_keep,
+                           void* const* K_out, void* const* V_out, void* stream) {
+  return compact_impl("kvc_compact", K, V, dtype, L, Hkv, n, d, idx, k_keep, 0, K_out, V_out, stream);
+}
+
+extern "C" int kvc_compact_into(const void* const* K, const void* const* V, int dtype, int L,
+                                int Hkv, int64_t n, int d, const int32_t* const* idx,
+                                const int64_t* k_keep, int64_t out_rows, void* const* K_out,
+                                void* const* V_out, void* stream) {
+  if (out_rows < 1) {
+    clear_error();
+    return KVC_FAIL(KVC_ERR_ARG, "kvc_compact_into: out_rows < 1");
+  }
+  return compact_impl("kvc_compact_into", K, V, dtype, L, Hkv, n, d, idx, k_keep, out_rows, K_out,
+                      V_out, stream);
 }

@@ -73,6 +73,75 @@ fuse_apply(const float* __restrict__ A, const float* __restrict__ D, const float
   }
 }
 
+// ---- cache slots: one entropy score per (layer, KV head, slot) ----------------
+// After a compaction each KV head holds its own token set, so E is a row per
+// (layer, KV head) and the softmax runs over that row.
+
+__global__ void __launch_bounds__(NT)
+slot_stats(const float* __restrict__ E, int64_t n, int nchunk, Part* __restrict__ part) {
+  __shared__ float red[NT / 64];
+  const int64_t row = blockIdx.y;
+  const int c = blockIdx.x;
+  const int64_t i0 = (int64_t)c * CHUNK, i1 = min(n, i0 + CHUNK);
+  const float* Er = E + row * n;
+  float m = -INFINITY, esum = 0.f;
+  for (int64_t i = i0 + threadIdx.x; i < i1; i += NT) {
+    const float e = Er[i];
+    m = fmaxf(m, e);
+    esum += e;
+  }
+  const float M = block_max<NT>(m, red);
+  float s = 0.f;
+  for (int64_t i = i0 + threadIdx.x; i < i1; i += NT) s += expf(Er[i] - M);
+  const float S = block_sum<NT>(s, red);
+  const float ES = block_sum<NT>(esum, red);
+  if (threadIdx.x == 0) part[row * nchunk + c] = Part{M, S, ES};
+}
+
+// one thread per row merges its chunks in index order; one thread per layer sums
+// its rows' E in (head, chunk) order for Ebar
+__global__ void slot_stats_merge(const Part* __restrict__ part, int nchunk, int L, int Hkv,
+                                 int64_t n, float2* __restrict__ stats, float* __restrict__ Ebar) {
+  const int r = blockIdx.x * blockDim.x + threadIdx.x;
+  if (r < L * Hkv) {
+    const Part* p = part + (int64_t)r * nchunk;
+    float M = -INFINITY;
+    for (int c = 0; c < nchunk; ++c) M = fmaxf(M, p[c].m);
+    float S = 0.f;
+    for (int c = 0; c < nchunk; ++c) S += p[c].s * expf(p[c].m - M);
+    stats[r] = make_float2(M, 1.0f / S);
+  }
+  if (Ebar && r < L) {
+    const Part* p = part + (int64_t)r * Hkv * nchunk;
+    float ES = 0.f;
+    for (int c = 0; c < Hkv * nchunk; ++c) ES += p[c].e;
+    Ebar[r] = ES / ((float)Hkv * (float)n);
+  }
+}
+
+__global__ void __launch_bounds__(NT)
+slot_apply(const float* __restrict__ A, const float* __restrict__ E, const float2* __restrict__ stats,
+           int64_t n, float alpha, float* __restrict__ S) {
+  const int64_t row = blockIdx.y;               // (layer, KV head)
+  const float2 st = stats[row];
+  const float* Ar = A + row * n;
+  const float* Er = E + row * n;
+  float* Sr = S + row * n;
+  const float beta = 1.0f - alpha;
+  for (int64_t i = (int64_t)blockIdx.x * NT + threadIdx.x; i < n; i += (int64_t)gridDim.x * NT)
+    Sr[i] = alpha * Ar[i] + beta * (expf(Er[i] - st.x) * st.y);
+}
+
+// E[l, g, offset + i] = D[l, i] * H[i] for every KV head g
+__global__ void __launch_bounds__(NT)
+slot_append(const float* __restrict__ D, const float* __restrict__ H, int Hkv, int64_t t,
+            int64_t cap, int64_t offset, float* __restrict__ E) {
+  const int64_t row = blockIdx.y;               // (layer, KV head)
+  const int64_t l = row / Hkv;
+  for (int64_t i = (int64_t)blockIdx.x * NT + threadIdx.x; i < t; i += (int64_t)gridDim.x * NT)
+    E[row * cap + offset + i] = D[l * t + i] * H[i];
+}
+
 }  // namespace
 }  // namespace kvc
 
@@ -112,4 +181,54 @@ extern "C" int kvc_fuse_scores(const float* A, const float* D, const float* H, i
   hipLaunchKernelGGL(fuse_apply, dim3(gx, (unsigned)rows), dim3(NT), 0, s, A, D, H,
                      (const float2*)stats, Hkv, n, alpha_fuse, S_out);
   return launch_status("kvc_fuse_scores");
+}
+
+extern "C" size_t kvc_fuse_scores_slots_workspace_size(int L, int Hkv, int64_t n) {
+  if (L < 1 || Hkv < 1 || n < 1) return 0;
+  const int64_t nchunk = (n + CHUNK - 1) / CHUNK;
+  return (size_t)L * Hkv * nchunk * sizeof(Part) + (size_t)L * Hkv * sizeof(float2) + 256;
+}
+
+extern "C" int kvc_fuse_scores_slots(const float* A, const float* E, int L, int Hkv, int64_t n,
+                                     float alpha_fuse, float* S_out, float* Ebar_out, void* ws,
+                                     size_t ws_bytes, void* stream) {
+  clear_error();
+  KVC_REQUIRE(L >= 1 && L <= KVC_MAX_LAYERS, "kvc_fuse_scores_slots: need 1 <= L <= %d", KVC_MAX_LAYERS);
+  KVC_REQUIRE(Hkv >= 1 && n >= 1, "kvc_fuse_scores_slots: need Hkv >= 1 and n >= 1");
+  KVC_REQUIRE(alpha_fuse >= 0.f && alpha_fuse <= 1.f, "kvc_fuse_scores_slots: alpha_fuse outside [0, 1]");
+  KVC_REQUIRE(A && E && S_out, "kvc_fuse_scores_slots: null pointer");
+  const int64_t nchunk = (n + CHUNK - 1) / CHUNK;
+  const int64_t rows = (int64_t)L * Hkv;
+  KVC_REQUIRE(rows <= 65535 && nchunk <= 0x7fffffff, "kvc_fuse_scores_slots: L * Hkv > 65535");
+  const size_t need = kvc_fuse_scores_slots_workspace_size(L, Hkv, n);
+  if (!ws || ws_bytes < need)
+    return KVC_FAIL(KVC_ERR_WORKSPACE, "kvc_fuse_scores_slots: workspace needs %zu bytes", need);
+  char* base = (char*)(((uintptr_t)ws + 255) & ~(uintptr_t)255);
+  Part* part = (Part*)base;
+  float2* stats = (float2*)(base + (size_t)rows * nchunk * sizeof(Part));
+  hipStream_t s = as_stream(stream);
+  hipLaunchKernelGGL(slot_stats, dim3((unsigned)nchunk, (unsigned)rows), dim3(NT), 0, s, E, n,
+                     (int)nchunk, part);
+  const int64_t nt = rows > L ? rows : L;
+  hipLaunchKernelGGL(slot_stats_merge, dim3((unsigned)((nt + 63) / 64)), dim3(64), 0, s,
+                     (const Part*)part, (int)nchunk, L, Hkv, n, stats, Ebar_out);
+  const int64_t gx64 = (n + NT * 4 - 1) / (NT * 4);
+  const unsigned gx = (unsigned)(gx64 < 1024 ? gx64 : 1024);
+  hipLaunchKernelGGL(slot_apply, dim3(gx, (unsigned)rows), dim3(NT), 0, s, A, E,
+                     (const float2*)stats, n, alpha_fuse, S_out);
+  return launch_status("kvc_fuse_scores_slots");
+}
+
+extern "C" int kvc_append_entropy_scores(const float* D, const float* H, int L, int Hkv, int64_t t,
+                                         float* E, int64_t cap, int64_t offset, void* stream) {
+  clear_error();
+  KVC_REQUIRE(L >= 1 && L <= KVC_MAX_LAYERS, "kvc_append_entropy_scores: need 1 <= L <= %d", KVC_MAX_LAYERS);
+  KVC_REQUIRE(Hkv >= 1 && t >= 1 && (int64_t)L * Hkv <= 65535, "kvc_append_entropy_scores: need Hkv, t >= 1");
+  KVC_REQUIRE(offset >= 0 && offset + t <= cap, "kvc_append_entropy_scores: need 0 <= offset and offset + t <= cap");
+  KVC_REQUIRE(D && H && E, "kvc_append_entropy_scores: null pointer");
+  const int64_t gx64 = (t + NT - 1) / NT;
+  const unsigned gx = (unsigned)(gx64 < 1024 ? gx64 : 1024);
+  hipLaunchKernelGGL(slot_append, dim3(gx, (unsigned)((int64_t)L * Hkv)), dim3(NT), 0,
+                     as_stream(stream), D, H, Hkv, t, cap, offset, E);
+  return launch_status("kvc_append_entropy_scores");
 }

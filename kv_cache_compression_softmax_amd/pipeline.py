@@ -105,6 +105,99 @@ class InfoKVPlan:
         return self
 
 
+class InfoKVDecodePlan:
+    """Compression repeated during decoding ([InfoKV] Technical detail: at
+    prefill and again every ``period`` generated tokens, e.g. 1024).
+
+    After the prefill compaction every (layer, KV head) holds k kept slots.  The
+    cache buffers hold cap = k + period rows per head: the kept slots first, then
+    the tokens decoded since.  A period re-scores all cap slots -- window
+    attention with the fresh window, E = D * H carried by the kept slots and
+    computed for the new tokens only, the per-head slot softmax -- keeps k per
+    head (the last w always) and gathers K, V and E into the other buffer, whose
+    rows [k, cap) then take the next period's tokens.  Uniform budget only.
+    """
+
+    def __init__(self, w: Workload, period: int = 1024, device="cuda"):
+        assert w.method == "infokv" and not w.adaptive_fraction
+        self.w, self.period, self.device = w, period, device
+        L, Hq, Hkv, d = w.layers, w.heads_q, w.heads_kv, w.head_dim
+        f32 = torch.float32
+        dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+        dtc = B.KVC_BF16 if w.dtype == "bf16" else B.KVC_F32
+        self.scale = 1.0 / math.sqrt(d)
+        self.k = B.kvc_uniform_budget(w.keep_fraction, w.n, w.window)
+        self.cap = cap = self.k + period
+        self.K = [[torch.empty(Hkv, cap, d, dtype=dt, device=device) for _ in range(L)] for _ in range(2)]
+        self.V = [[torch.empty(Hkv, cap, d, dtype=dt, device=device) for _ in range(L)] for _ in range(2)]
+        self.E = [torch.empty(L, Hkv, cap, dtype=f32, device=device) for _ in range(2)]
+        self.cur = 0
+        self.H = torch.empty(period, dtype=f32, device=device)
+        self.D = torch.empty(L, period, dtype=f32, device=device)
+        self.A = torch.empty(L, Hkv, cap, dtype=f32, device=device)
+        self.S = torch.empty(L, Hkv, cap, dtype=f32, device=device)
+        self.idx = [torch.empty(Hkv, self.k, dtype=torch.int32, device=device) for _ in range(L)]
+        self.ws_attn = torch.empty(max(1, B.kvc_score_window_attn_workspace_size(
+            L, Hq, Hkv, cap, w.window, d, dtc)), dtype=torch.uint8, device=device)
+        self.ws_fuse = torch.empty(max(1, B.kvc_fuse_scores_slots_workspace_size(L, Hkv, cap)),
+                                   dtype=torch.uint8, device=device)
+
+    def _e_rows(self, E):
+        return [E[l].unsqueeze(-1) for l in range(self.w.layers)]      # [Hkv, rows, 1] views
+
+    def start(self, prefill: "InfoKVPlan", inp: dict, stream=None):
+        """The slots after the prefill compaction: the kept K and V rows and the
+        E = D * H of their tokens (per head, gathered by the kept indices)."""
+        w = self.w
+        if list(prefill.k) != [self.k] * w.layers:
+            raise ValueError("the prefill plan must use the same uniform budget")
+        B.kvc_compact_into(inp["k"], inp["v"], prefill.idx, prefill.k, self.K[0], self.V[0],
+                           stream=stream)
+        E_full = torch.empty(w.layers, w.heads_kv, w.n, dtype=torch.float32, device=self.device)
+        B.kvc_append_entropy_scores(prefill.D, prefill.H, E_full, 0, stream=stream)
+        B.kvc_compact_into(self._e_rows(E_full), None, prefill.idx, prefill.k,
+                           self._e_rows(self.E[0]), None, stream=stream)
+        self.cur = 0
+        return self
+
+    def append(self, new: dict):
+        """The decoder's own writes, outside the compression path: the new
+        tokens' K and V rows go after the kept slots of the current buffer."""
+        for l in range(self.w.layers):
+            self.K[self.cur][l][:, self.k:].copy_(new["k"][l])
+            self.V[self.cur][l][:, self.k:].copy_(new["v"][l])
+
+    def run(self, new: dict, stream=None, mark=None):
+        """One period over the current buffer.  ``new`` holds the period's
+        logits [period, vocab], hidden states h (L x [period, hidden]) and
+        h_final, and the fresh window queries q_win (L x [Hq, w, d])."""
+        w = self.w
+        L, k = w.layers, self.k
+        cur, nxt = self.cur, 1 - self.cur
+        mark = mark or (lambda name: None)
+        mark("start")
+        B.kvc_topk_entropy(new["logits"], w.topk_entropy, self.H, stream=stream)
+        mark("topk_entropy")
+        B.kvc_repr_distance(new["h"], new["h_final"], w.tau, self.D, stream=stream)
+        mark("repr_distance")
+        B.kvc_score_window_attn(new["q_win"], self.K[cur], self.scale, False, self.A,
+                                ws=self.ws_attn, stream=stream)
+        mark("window_attn")
+        B.kvc_append_entropy_scores(self.D, self.H, self.E[cur], k, stream=stream)
+        B.kvc_fuse_scores_slots(self.A, self.E[cur], w.alpha_fuse, self.S, ws=self.ws_fuse,
+                                stream=stream)
+        mark("fuse_scores")
+        B.kvc_select_topk(self.S, [k] * L, w.window, self.idx, stream=stream)
+        mark("select_topk")
+        B.kvc_compact_into(self.K[cur], self.V[cur], self.idx, [k] * L, self.K[nxt], self.V[nxt],
+                           stream=stream)
+        B.kvc_compact_into(self._e_rows(self.E[cur]), None, self.idx, [k] * L,
+                           self._e_rows(self.E[nxt]), None, stream=stream)
+        mark("compact")
+        self.cur = nxt
+        return self
+
+
 class SelKVPlan:
     def __init__(self, w: Workload, device="cuda"):
         assert w.method == "selkv"

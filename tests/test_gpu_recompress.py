@@ -1,0 +1,181 @@
+"""GPU parity of compression during decoding ([InfoKV] Technical detail: at
+prefill and again every 1024 generated tokens) against the oracle.
+
+Kernels: the per-slot fusion, the entropy-score append and the gather into a
+fixed head stride, element by element.  Path: a reduced Llama-shaped workload is
+compressed at prefill, then two periods of new tokens are appended and the
+cache is re-compressed each time; the oracle runs the same chain from host
+copies of the same input bytes.  A head whose kept set at the previous step
+differs from the oracle's (only possible inside the 1e-3 band around the
+threshold) holds other tokens from then on and is checked by properties only.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from kv_cache_compression_softmax_amd import configs, synth
+from oracle import infokv
+from tests.gpu_util import announce, assert_rel, host_bits, host_f64, kept_sets_match, need_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    d = need_gpu()
+    from kv_cache_compression_softmax_amd import binding
+    binding.lib()
+    return d
+
+
+def B():
+    from kv_cache_compression_softmax_amd import binding
+    return binding
+
+
+@pytest.mark.parametrize("L,Hkv,n", [(1, 1, 1), (2, 4, 777), (3, 8, 20001)])
+def test_fuse_scores_slots(dev, L, Hkv, n):
+    announce("fuse slots", L, Hkv, n)
+    g = torch.Generator(device=dev); g.manual_seed(n)
+    A = torch.rand(L, Hkv, n, generator=g, device=dev)
+    E = torch.randn(L, Hkv, n, generator=g, device=dev) * 4
+    S = torch.empty_like(A)
+    Ebar = torch.empty(L, device=dev)
+    B().kvc_fuse_scores_slots(A, E, 0.9, S, Ebar)
+    torch.cuda.synchronize()
+    for l in range(L):
+        Sr, Eb, _ = infokv.fuse_scores_slots(host_f64(A[l]), host_f64(E[l]), 0.9)
+        assert_rel(S[l].cpu().numpy(), Sr, 1e-3, what="S")
+        assert_rel([Ebar[l].item()], [Eb], 1e-3, floor=1e-3, what="Ebar")
+
+
+def test_append_entropy_scores(dev):
+    announce("append entropy scores")
+    L, Hkv, t, cap, off = 3, 5, 1000, 1400, 333
+    g = torch.Generator(device=dev); g.manual_seed(5)
+    D = torch.rand(L, t, generator=g, device=dev) + 1
+    H = torch.rand(t, generator=g, device=dev) * 5
+    E = torch.full((L, Hkv, cap), -7.0, device=dev)
+    B().kvc_append_entropy_scores(D, H, E, off)
+    torch.cuda.synchronize()
+    e = E.cpu().numpy()
+    want = (D.cpu().numpy() * H.cpu().numpy()[None, :]).astype(np.float32)   # one float32 product
+    for gg in range(Hkv):
+        np.testing.assert_array_equal(e[:, gg, off:off + t], want)
+    assert (e[:, :, :off] == -7.0).all() and (e[:, :, off + t:] == -7.0).all()
+
+
+@pytest.mark.parametrize("dtype,d", [(torch.bfloat16, 128), (torch.bfloat16, 64), (torch.float32, 1),
+                                     (torch.float32, 3)])
+def test_compact_into(dev, dtype, d):
+    announce("compact into", dtype, d)
+    L, Hkv, n, out_rows = 2, 3, 1000, 700
+    ks = [300, 555]
+    g = torch.Generator(device=dev); g.manual_seed(d)
+    K = [torch.randn(Hkv, n, d, generator=g, device=dev).to(dtype) for _ in range(L)]
+    V = [torch.randn(Hkv, n, d, generator=g, device=dev).to(dtype) for _ in range(L)]
+    idx = [torch.sort(torch.randperm(n, generator=g, device=dev)[:k])[0].to(torch.int32)
+           .expand(Hkv, k).contiguous() for k in ks]
+    Ko = [torch.full((Hkv, out_rows, d), 2.5, device=dev).to(dtype) for _ in range(L)]
+    Vo = [torch.full((Hkv, out_rows, d), 2.5, device=dev).to(dtype) for _ in range(L)]
+    B().kvc_compact_into(K, V, idx, ks, Ko, Vo)
+    torch.cuda.synchronize()
+    for l in range(L):
+        kr, vr = infokv.compact(host_bits(K[l]), host_bits(V[l]), idx[l].cpu().numpy())
+        np.testing.assert_array_equal(host_bits(Ko[l])[:, :ks[l]], kr)
+        np.testing.assert_array_equal(host_bits(Vo[l])[:, :ks[l]], vr)
+        assert (host_f64(Ko[l])[:, ks[l]:] == 2.5).all() and (host_f64(Vo[l])[:, ks[l]:] == 2.5).all()
+
+
+def _new_tokens(w, period, seed, dev):
+    """One period of synthetic decoded tokens: the generators of the prefill
+    workload with another seed, at period rows."""
+    return synth.make_inputs(configs.reduced(w, n=period, seed=seed), dev)
+
+
+@pytest.mark.parametrize("w,period", [
+    (configs.reduced(configs.LLAMA8B_32K, layers=2, n=2048, vocab=8192, hidden=512), 256),
+    (configs.reduced(configs.LLAMA3B_16K, layers=2, n=1500, vocab=4099, hidden=384), 300),
+    (configs.reduced(configs.TINY, n=700), 129),
+], ids=lambda x: getattr(x, "name", str(x)))
+def test_decode_recompression_end_to_end(dev, w, period):
+    from kv_cache_compression_softmax_amd import pipeline
+    announce("decode recompression", w.name, period)
+    inp = synth.make_inputs(w, dev)
+    pre = pipeline.InfoKVPlan(w, dev).run(inp)
+    dec = pipeline.InfoKVDecodePlan(w, period, dev).start(pre, inp)
+    torch.cuda.synchronize()
+    L, Hkv, k, win = w.layers, w.heads_kv, dec.k, w.window
+    # oracle prefill, from the same bytes
+    H = infokv.topk_entropy(host_f64(inp["logits"]), w.topk_entropy)
+    hf = host_f64(inp["h_final"])
+    slots, same = [], np.zeros((L, Hkv), dtype=bool)
+    for l in range(L):
+        D = infokv.repr_distance(host_f64(inp["h"][l]), hf, w.tau)
+        _, S, S32, _, idx = infokv.infokv_layer(host_f64(inp["q_win"][l]), host_f64(inp["k"][l]),
+                                                D, H, w.alpha_fuse, k, win)
+        Kc, Vc = infokv.compact(host_bits(inp["k"][l]), host_bits(inp["v"][l]), idx)
+        E_kept = np.take_along_axis(np.tile(D * H, (Hkv, 1)), idx.astype(np.int64), axis=1)
+        slots.append({"Kc": Kc, "Vc": Vc, "E": E_kept})
+        same[l] = (pre.idx[l].cpu().numpy() == idx).all(axis=1)
+        # the slots the decode plan starts from
+        for g in np.nonzero(same[l])[0]:
+            np.testing.assert_array_equal(host_bits(dec.K[0][l][g, :k]), Kc[g])
+            np.testing.assert_array_equal(host_bits(dec.V[0][l][g, :k]), Vc[g])
+            assert_rel(dec.E[0][l, g, :k].cpu().numpy(), E_kept[g], 1e-3, what="prefill E slots")
+    for p in range(2):
+        new = _new_tokens(w, period, 1000 + 17 * p + w.seed, dev)
+        dec.append(new)
+        cur = dec.cur
+        dec.run(new)
+        torch.cuda.synchronize()
+        Hn = infokv.topk_entropy(host_f64(new["logits"]), w.topk_entropy)
+        hfn = host_f64(new["h_final"])
+        assert_rel(dec.H.cpu().numpy(), Hn, 1e-3, what="H of the new tokens")
+        compared = 0
+        for l in range(L):
+            Dn = infokv.repr_distance(host_f64(new["h"][l]), hfn, w.tau)
+            assert_rel(dec.D[l].cpu().numpy(), Dn, 1e-3, what="D of the new tokens")
+            kn, vn = host_bits(new["k"][l]), host_bits(new["v"][l])
+            A_gpu, S_gpu = dec.A[l].cpu().numpy(), dec.S[l].cpu().numpy()
+            gi = dec.idx[l].cpu().numpy()
+            nxt = dec.cur
+            for g in range(Hkv):
+                # properties on the GPU's own scores, any head
+                ii = gi[g]
+                assert np.all(np.diff(ii) > 0) and ii[-win:].tolist() == list(range(dec.cap - win, dec.cap))
+                np.testing.assert_array_equal(host_bits(dec.K[nxt][l][g, :k]), host_bits(dec.K[cur][l][g])[ii])
+                np.testing.assert_array_equal(host_bits(dec.V[nxt][l][g, :k]), host_bits(dec.V[cur][l][g])[ii])
+                if not same[l, g]:
+                    continue
+                s = slots[l]
+                K_cache = np.concatenate([s["Kc"][g], kn[g]])[None]
+                V_cache = np.concatenate([s["Vc"][g], vn[g]])[None]
+                q = host_f64(new["q_win"][l])
+                G = w.group
+                out = infokv.recompress_period(
+                    q[g * G:(g + 1) * G], infokv_bits_f64(K_cache, w), infokv_bits_f64(V_cache, w),
+                    s["E"][g:g + 1], Dn, Hn, w.alpha_fuse, k, win)
+                assert_rel(A_gpu[g], out["A"][0], 1e-3, what="A")
+                assert_rel(S_gpu[g], out["S"][0], 1e-3, what="S")
+                kept_sets_match(gi[g:g + 1], out["S"][0:1], k, win)
+                if np.array_equal(gi[g], out["idx"][0]):
+                    Kc, Vc = infokv.compact(K_cache, V_cache, out["idx"])
+                    np.testing.assert_array_equal(host_bits(dec.K[nxt][l][g, :k]), Kc[0])
+                    np.testing.assert_array_equal(host_bits(dec.V[nxt][l][g, :k]), Vc[0])
+                    assert_rel(dec.E[nxt][l, g, :k].cpu().numpy(), out["E_next"][0], 1e-3, what="E slots")
+                    s["Kc"][g], s["Vc"][g], s["E"][g] = Kc[0], Vc[0], out["E_next"][0]
+                    compared += 1
+                else:
+                    same[l, g] = False
+        assert compared >= (L * Hkv + 1) // 2, f"period {p}: only {compared} heads followed the oracle"
+
+
+def infokv_bits_f64(bits, w):
+    """float64 values of a raw bit array of the workload's dtype."""
+    from oracle import precision
+    if w.dtype == "bf16":
+        return precision.bf16_bits_to_f64(bits)
+    return precision.f32_bits_to_f64(bits)
