@@ -113,6 +113,25 @@ def copy_calibration():
     print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "calls": 3}))
 
 
+def decode_period_bytes(w, k, period):
+    """Bytes one period of compression during decoding must move: the new
+    tokens' logits and hidden-state rows, the cache keys (window attention), the
+    slot score rows, and the kept rows' K, V and E read and written once."""
+    e = 2 if w.dtype == "bf16" else 4
+    L, Hq, Hkv, d = w.layers, w.heads_q, w.heads_kv, w.head_dim
+    cap = k + period
+    kept = L * Hkv * k
+    return {
+        "topk_entropy": period * w.vocab * e + period * 4,
+        "repr_distance": (L + 1) * period * w.hidden * e + L * period * 4,
+        "window_attn": L * Hkv * cap * d * e + L * Hq * w.window * d * e + L * Hkv * cap * 4,
+        # E of the new tokens appended (D, H read), then A and E read and S written
+        "fuse_scores": L * Hkv * period * 4 + L * period * 4 + period * 4 + 3 * L * Hkv * cap * 4,
+        "select_topk": L * Hkv * cap * 4 + kept * 4,
+        "compact": 2 * 2 * kept * d * e + 2 * kept * 4 + 2 * kept * 4,
+    }
+
+
 def window_flops(w):
     """MFMA flops of one window-attention call (two passes of Q K^T)."""
     return 2 * 2 * w.layers * w.heads_q * w.window * w.n * w.head_dim
@@ -207,6 +226,68 @@ def cpu_baseline(w, inp, budget_s=15.0):
             "est_step_s": total}
 
 
+def cpu_baseline_period(w, plan, new, period, budget_s=15.0):
+    """The oracle on a bounded sample of one decode period: the new tokens' H
+    and D on row chunks, and the re-compression (attention, slot fusion,
+    select, gather) of whole layers, each part scaled to the whole period."""
+    import numpy as np
+    import torch
+    from oracle import infokv, precision
+
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:
+        cores = 1
+
+    def f64(t):
+        t = t.detach().cpu().contiguous()
+        if t.dtype == torch.bfloat16:
+            return precision.bf16_bits_to_f64(t.view(torch.int16).numpy().view(np.uint16))
+        return t.numpy().astype(np.float64)
+
+    L, G = w.layers, w.group
+    t_start = time.perf_counter()
+    rows = layers = 0
+    t_h = t_d = t_l = 0.0
+    k = plan.k
+    while time.perf_counter() - t_start < budget_s and (rows < period or layers < L):
+        if rows < period:
+            r0, r1 = rows, min(period, rows + 128)
+            lg = f64(new["logits"][r0:r1])
+            t0 = time.perf_counter()
+            H = infokv.topk_entropy(lg, w.topk_entropy)
+            t_h += time.perf_counter() - t0
+            hf = f64(new["h_final"][r0:r1])
+            hl = [f64(new["h"][l][r0:r1]) for l in range(L)]
+            t0 = time.perf_counter()
+            Ds = [infokv.repr_distance(hl[l], hf, w.tau) for l in range(L)]
+            t_d += time.perf_counter() - t0
+            rows = r1
+        if layers < L:
+            lay = layers
+            q = f64(new["q_win"][lay])
+            Kf = f64(plan.K[plan.cur][lay])
+            Vb = plan.V[plan.cur][lay].cpu()
+            Vb = Vb.view(torch.int16).numpy().view(np.uint16) if Vb.dtype == torch.bfloat16 else Vb.numpy()
+            E = plan.E[plan.cur][lay].cpu().numpy().astype(np.float64)
+            Dn, Hn = np.resize(Ds[lay % len(Ds)], period), np.resize(H, period)
+            t0 = time.perf_counter()
+            for g in range(w.heads_kv):
+                infokv.recompress_period(q[g * G:(g + 1) * G], Kf[g:g + 1], Vb[g:g + 1],
+                                         E[g:g + 1, :k], Dn, Hn, w.alpha_fuse, k, w.window)
+            t_l += time.perf_counter() - t0
+            layers += 1
+    total = t_h * period / rows + t_d * period / rows + t_l * L / layers
+    sample = (f"oracle run for {time.perf_counter() - t_start:.1f} s: top-k entropy and "
+              f"representation distance on {rows} of {period} new token rows, re-compression of "
+              f"{layers} of {L} layers (all KV heads); each part scaled by rows or layers to the "
+              f"whole period")
+    return {"value": plan.cap / total, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": sample, "sample_s": round(time.perf_counter() - t_start, 2),
+            "est_step_s": total}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -215,6 +296,10 @@ def main():
     ap.add_argument("--workload", default="llama3.1-8b-n32768-keep20-bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--decode-period", type=int, default=0,
+                    help="time one period of compression during decoding (the cache of "
+                         "k kept slots plus this many new tokens, re-compressed to k) instead "
+                         "of the prefill compression")
     args = ap.parse_args()
     if args.copy_calibration:
         copy_calibration()
@@ -234,6 +319,19 @@ def main():
     inp = synth.make_inputs(w, dev)
     plan = pipeline.InfoKVPlan(w, dev) if w.method == "infokv" else pipeline.SelKVPlan(w, dev)
     stream = torch.cuda.current_stream()
+    period = args.decode_period
+    if period:
+        if w.method != "infokv" or w.adaptive_fraction:
+            sys.exit("--decode-period needs a uniform-budget InfoKV workload")
+        # untimed: the prefill compression, the slots it leaves, one period of new
+        # tokens (same generators, another seed) written by the decoder
+        plan.run(inp)
+        dplan = pipeline.InfoKVDecodePlan(w, period, dev).start(plan, inp)
+        new = synth.make_inputs(configs.reduced(w, n=period, seed=w.seed + 1000), dev)
+        dplan.append(new)
+        del inp
+        torch.cuda.empty_cache()
+        inp, plan = new, dplan
     for _ in range(args.warmup):
         plan.run(inp)
     torch.cuda.synchronize()
@@ -259,8 +357,13 @@ def main():
         per.setdefault(n1, []).append(e0.elapsed_time(e1))
     per_ms = {k: sum(v) / len(v) for k, v in per.items()}
 
-    k_list = plan.k if w.method == "infokv" else plan.m
-    abytes = algorithmic_bytes(w, k_list)
+    if period:
+        abytes = decode_period_bytes(w, plan.k, period)
+        n_step = plan.cap
+    else:
+        k_list = plan.k if w.method == "infokv" else plan.m
+        abytes = algorithmic_bytes(w, k_list)
+        n_step = w.n
     dom = max(per_ms, key=per_ms.get)
     achieved = abytes[dom] / (per_ms[dom] * 1e-3) / 1e9
     path_bytes = sum(abytes.values())
@@ -268,9 +371,10 @@ def main():
                    "GBps": round(abytes[k] / (per_ms[k] * 1e-3) / 1e9, 1),
                    "frac_hbm": round(abytes[k] / (per_ms[k] * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
                for k in per_ms}
-    kernels["window_attn"]["mfma_TFLOPs"] = round(window_flops(w) / (per_ms["window_attn"] * 1e-3) / 1e12, 1)
+    wfl = window_flops(w) * (n_step / w.n)
+    kernels["window_attn"]["mfma_TFLOPs"] = round(wfl / (per_ms["window_attn"] * 1e-3) / 1e12, 1)
 
-    value = w.n / (ms * 1e-3)
+    value = n_step / (ms * 1e-3)
     out = {
         "metric": "tokens scored+compacted/sec (all layers, 1 GPU) at 8B/32K; % of HBM roofline",
         "value": round(value, 1),
@@ -284,13 +388,15 @@ def main():
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic (seeded Llama-shaped tensors, inputs resident in HBM)",
-        "config": {"workload": w.name, "layers": w.layers, "heads_q": w.heads_q,
-                   "heads_kv": w.heads_kv, "head_dim": w.head_dim, "n": w.n, "window": w.window,
-                   "hidden": w.hidden, "vocab": w.vocab, "kept_per_layer": k_list[0]
-                   if len(set(k_list)) == 1 else "adaptive", "parallelism": "none (1 GPU)"},
+        "config": {"workload": w.name + (f"-decode{period}" if period else ""), "layers": w.layers,
+                   "heads_q": w.heads_q, "heads_kv": w.heads_kv, "head_dim": w.head_dim, "n": w.n,
+                   "window": w.window, "hidden": w.hidden, "vocab": w.vocab,
+                   "kept_per_layer": (plan.k if period else k_list[0] if len(set(k_list)) == 1
+                                      else "adaptive"), "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": measured_traffic(w.name, dom), "alg_bytes": abytes[dom]},
+                     "traffic": measured_traffic(w.name + (f"-decode{period}" if period else ""), dom),
+                     "alg_bytes": abytes[dom]},
         "path_roofline": {"alg_bytes": path_bytes,
                           "achieved_GBps": round(path_bytes / (ms * 1e-3) / 1e9, 1),
                           "frac": round(path_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)},
@@ -331,9 +437,14 @@ def main():
                       "traffic": measured_traffic(w.name, k)}
         dec["timed"] = "separately, after the steps; not in ms_per_step"
         out["decode_check"] = dec
+    if period:
+        out["decode_period"] = {"period": period, "slots_per_step": n_step,
+                                "note": "value counts the slots re-scored and compacted per period "
+                                        "(k kept + period new) per second"}
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(w, inp)
+        out["cpu_baseline"] = (cpu_baseline_period(w, plan, inp, period) if period
+                               else cpu_baseline(w, inp))
     print(json.dumps(out), flush=True)
 
 

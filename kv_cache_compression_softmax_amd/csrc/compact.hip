@@ -25,7 +25,8 @@ struct Tables {
   I64s blk0;                    // first block of each layer
 };
 
-template <bool VEC>
+// MODE: 0 any row size (2-byte words), 1 rows of 16-byte multiples, 2 four-byte rows
+template <int MODE>
 __global__ void __launch_bounds__(NT)
 compact_kernel(Tables t, int lc, int Hkv, int64_t n, int rowbytes) {
   const int64_t b = blockIdx.x;
@@ -41,7 +42,7 @@ compact_kernel(Tables t, int lc, int Hkv, int64_t n, int rowbytes) {
   const char* V = t.V.p[l] ? (const char*)t.V.p[l] + (int64_t)g * n * rowbytes : nullptr;
   char* Ko = (char*)t.Ko.p[l] + (int64_t)g * t.orows.v[l] * rowbytes;
   char* Vo = V ? (char*)t.Vo.p[l] + (int64_t)g * t.orows.v[l] * rowbytes : nullptr;
-  if (VEC) {
+  if (MODE == 1) {
     const int lpr = rowbytes / 16;                 // lanes per row
     const int rpi = NT / lpr;                      // rows per iteration
     const int r = threadIdx.x / lpr, c = threadIdx.x % lpr;
@@ -53,6 +54,14 @@ compact_kernel(Tables t, int lc, int Hkv, int64_t n, int rowbytes) {
       if (V) vv = *reinterpret_cast<const uint4*>(V + src * rowbytes + c * 16);
       *reinterpret_cast<uint4*>(Ko + j * rowbytes + c * 16) = kv;
       if (V) *reinterpret_cast<uint4*>(Vo + j * rowbytes + c * 16) = vv;
+    }
+  } else if (MODE == 2) {
+    // one 4-byte row per thread (per-slot float32 scores)
+    const int64_t j = j0 + threadIdx.x;
+    if (threadIdx.x < ROWS && j < k) {
+      const int64_t src = idx[j];
+      *reinterpret_cast<uint32_t*>(Ko + j * 4) = *reinterpret_cast<const uint32_t*>(K + src * 4);
+      if (V) *reinterpret_cast<uint32_t*>(Vo + j * 4) = *reinterpret_cast<const uint32_t*>(V + src * 4);
     }
   } else {
     const int half = rowbytes / 2;                 // 2-byte words per row
@@ -86,6 +95,7 @@ int compact_impl(const char* fn, const void* const* K, const void* const* V, int
               "%s: too many rows for one launch", fn);
   const int rowbytes = d * dtype_size(dtype);
   bool vec = rowbytes % 16 == 0 && rowbytes / 16 <= NT;
+  bool word = rowbytes == 4;
   for (int l = 0; l < L; ++l) {
     KVC_REQUIRE(K[l] && idx[l] && K_out[l], "%s: null pointer in layer %d", fn, l);
     KVC_REQUIRE(!V || (V[l] && V_out[l]), "%s: null V pointer in layer %d", fn, l);
@@ -93,6 +103,8 @@ int compact_impl(const char* fn, const void* const* K, const void* const* V, int
     KVC_REQUIRE(out_rows <= 0 || k_keep[l] <= out_rows, "%s: k_keep[%d] > out_rows", fn, l);
     vec = vec && (uintptr_t)K[l] % 16 == 0 && (uintptr_t)K_out[l] % 16 == 0;
     if (V) vec = vec && (uintptr_t)V[l] % 16 == 0 && (uintptr_t)V_out[l] % 16 == 0;
+    word = word && (uintptr_t)K[l] % 4 == 0 && (uintptr_t)K_out[l] % 4 == 0;
+    if (V) word = word && (uintptr_t)V[l] % 4 == 0 && (uintptr_t)V_out[l] % 4 == 0;
   }
   hipStream_t s = as_stream(stream);
   for (int l0 = 0; l0 < L; l0 += kLayersPerLaunch) {
@@ -110,8 +122,9 @@ int compact_impl(const char* fn, const void* const* K, const void* const* V, int
       t.blk0.v[i] = blocks;
       blocks += (int64_t)Hkv * ((k_keep[l0 + i] + ROWS - 1) / ROWS);
     }
-    if (vec) hipLaunchKernelGGL(compact_kernel<true>, dim3((unsigned)blocks), dim3(NT), 0, s, t, lc, Hkv, n, rowbytes);
-    else hipLaunchKernelGGL(compact_kernel<false>, dim3((unsigned)blocks), dim3(NT), 0, s, t, lc, Hkv, n, rowbytes);
+    if (vec) hipLaunchKernelGGL(compact_kernel<1>, dim3((unsigned)blocks), dim3(NT), 0, s, t, lc, Hkv, n, rowbytes);
+    else if (word) hipLaunchKernelGGL(compact_kernel<2>, dim3((unsigned)blocks), dim3(ROWS), 0, s, t, lc, Hkv, n, rowbytes);
+    else hipLaunchKernelGGL(compact_kernel<0>, dim3((unsigned)blocks), dim3(NT), 0, s, t, lc, Hkv, n, rowbytes);
   }
   return launch_status(fn);
 }
