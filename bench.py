@@ -339,22 +339,26 @@ def main():
 
     marks = []
 
-    def mark(name):
+    def mark(name, s=None):
+        # an event on the stream the step runs on (the launch stream, or a side
+        # stream for steps that run beside it)
+        s = s or stream
         ev = torch.cuda.Event(enable_timing=True)
-        ev.record(stream)
-        marks.append((name, ev))
+        ev.record(s)
+        marks.append((name, s.cuda_stream, ev))
 
     torch.cuda.synchronize()
     for _ in range(args.steps):
         plan.run(inp, mark=mark)
     torch.cuda.synchronize()
-    total_ms = marks[0][1].elapsed_time(marks[-1][1])
+    total_ms = marks[0][2].elapsed_time(marks[-1][2])
     ms = total_ms / args.steps
-    per = {}
-    for (n0, e0), (n1, e1) in zip(marks[:-1], marks[1:]):
-        if n1 == "start":
-            continue
-        per.setdefault(n1, []).append(e0.elapsed_time(e1))
+    # a step's duration: from the previous mark on the same stream to its own mark
+    per, last = {}, {}
+    for name, sid, ev in marks:
+        if name != "start" and ":" not in name and name != "join" and sid in last:
+            per.setdefault(name, []).append(last[sid].elapsed_time(ev))
+        last[sid] = ev
     per_ms = {k: sum(v) / len(v) for k, v in per.items()}
 
     if period:
