@@ -59,6 +59,11 @@ class InfoKVPlan:
             self.k = None
             total = w.adaptive_total()
         self.total = total
+        # logits processed in row chunks: consecutive chunks alternate between the
+        # launch stream and this one, so one chunk's last round of rows overlaps
+        # the next chunk's first (the chunks are independent)
+        self.side = torch.cuda.Stream(device=device) if w.logits_chunk_rows else None
+        self.ev = [torch.cuda.Event(), torch.cuda.Event()]
         self.idx_pool = torch.empty(Hkv * total, dtype=torch.int32, device=device)
         self.kc_pool = torch.empty(Hkv * total * d, dtype=dt, device=device)
         self.vc_pool = torch.empty(Hkv * total * d, dtype=dt, device=device)
@@ -79,9 +84,19 @@ class InfoKVPlan:
         mark("start")
         chunk = w.logits_chunk_rows or w.n
         logits = inp["logits"]
-        for r0 in range(0, w.n, chunk):
-            r1 = min(w.n, r0 + chunk)
-            B.kvc_topk_entropy(logits[r0:r1], w.topk_entropy, self.H[r0:r1], stream=stream)
+        if chunk >= w.n:
+            B.kvc_topk_entropy(logits, w.topk_entropy, self.H, stream=stream)
+        else:
+            s0 = stream if isinstance(stream, torch.cuda.Stream) else \
+                (torch.cuda.ExternalStream(stream) if stream is not None else torch.cuda.current_stream())
+            self.ev[0].record(s0)
+            self.side.wait_event(self.ev[0])
+            for ci, r0 in enumerate(range(0, w.n, chunk)):
+                r1 = min(w.n, r0 + chunk)
+                B.kvc_topk_entropy(logits[r0:r1], w.topk_entropy, self.H[r0:r1],
+                                   stream=s0 if ci % 2 == 0 else self.side)
+            self.ev[1].record(self.side)
+            s0.wait_event(self.ev[1])
         mark("topk_entropy")
         B.kvc_repr_distance(inp["h"], inp["h_final"], w.tau, self.D, stream=stream)
         mark("repr_distance")
