@@ -62,7 +62,8 @@ class InfoKVPlan:
         # logits processed in row chunks: consecutive chunks alternate between the
         # launch stream and this one, so one chunk's last round of rows overlaps
         # the next chunk's first (the chunks are independent)
-        self.side = torch.cuda.Stream(device=device) if w.logits_chunk_rows else None
+        self.entropy_rows = w.logits_chunk_rows or n
+        self.side = torch.cuda.Stream(device=device)
         self.ev = [torch.cuda.Event(), torch.cuda.Event()]
         self.idx_pool = torch.empty(Hkv * total, dtype=torch.int32, device=device)
         self.kc_pool = torch.empty(Hkv * total * d, dtype=dt, device=device)
@@ -82,7 +83,7 @@ class InfoKVPlan:
         w = self.w
         mark = mark or (lambda name: None)
         mark("start")
-        chunk = w.logits_chunk_rows or w.n
+        chunk = self.entropy_rows
         logits = inp["logits"]
         if chunk >= w.n:
             B.kvc_topk_entropy(logits, w.topk_entropy, self.H, stream=stream)
