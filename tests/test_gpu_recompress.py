@@ -179,3 +179,80 @@ def infokv_bits_f64(bits, w):
     if w.dtype == "bf16":
         return precision.bf16_bits_to_f64(bits)
     return precision.f32_bits_to_f64(bits)
+
+
+def test_decode_recompression_full_size_sampled(dev):
+    """One period at the 8B / 32K shape in the bench's launch configuration (6553
+    kept slots + 1024 new tokens per head).  The new tokens' H and D on sampled
+    rows and one (layer, KV head)'s window attention over its slot cache are
+    recomputed by the oracle; the cache rows are first checked to be exactly the
+    input rows of the kept indices.  Selection and gathers by properties that
+    hold at any size."""
+    from kv_cache_compression_softmax_amd import pipeline
+    w, period = configs.LLAMA8B_32K, 1024
+    announce("decode recompression full", w.name, period)
+    inp = synth.make_inputs(w, dev)
+    pre = pipeline.InfoKVPlan(w, dev).run(inp)
+    dec = pipeline.InfoKVDecodePlan(w, period, dev).start(pre, inp)
+    new = synth.make_inputs(configs.reduced(w, n=period, seed=w.seed + 1000), dev)
+    dec.append(new)
+    cur, k, win, L = dec.cur, dec.k, w.window, w.layers
+    torch.cuda.synchronize()
+    # the slots the period starts from: the input rows of the prefill's kept indices
+    E0 = (pre.D[:, None, :] * pre.H[None, None, :]).expand(L, w.heads_kv, w.n)
+    for l in range(L):
+        i64 = pre.idx[l].long()
+        for t_in, t_out in ((inp["k"][l], dec.K[cur][l]), (inp["v"][l], dec.V[cur][l])):
+            assert torch.equal(torch.gather(t_in, 1, i64[:, :, None].expand(-1, -1, w.head_dim)),
+                               t_out[:, :k])
+        assert torch.equal(torch.gather(E0[l], 1, i64), dec.E[cur][l, :, :k])
+        assert torch.equal(dec.K[cur][l][:, k:], new["k"][l]) and torch.equal(dec.V[cur][l][:, k:], new["v"][l])
+    Kcur = [t.clone() for t in dec.K[cur]]
+    Ecur = dec.E[cur].clone()
+    dec.run(new)
+    torch.cuda.synchronize()
+    nxt = dec.cur
+    r = np.random.default_rng(11)
+    rows = torch.from_numpy(np.sort(r.choice(period, 24, replace=False))).to(dev)
+    H_ref = infokv.topk_entropy(host_f64(new["logits"].index_select(0, rows)), w.topk_entropy)
+    assert_rel(dec.H[rows].cpu().numpy(), H_ref, 1e-3, what="H sample")
+    hf = host_f64(new["h_final"].index_select(0, rows))
+    for l in range(0, L, 7):
+        D_ref = infokv.repr_distance(host_f64(new["h"][l].index_select(0, rows)), hf, w.tau)
+        assert_rel(dec.D[l][rows].cpu().numpy(), D_ref, 1e-3, what="D sample")
+    l, g, G = 13, 5, w.group
+    A_ref = infokv.window_attention(host_f64(new["q_win"][l][g * G:(g + 1) * G]), host_f64(Kcur[l][g:g + 1]))
+    assert_rel(dec.A[l, g].cpu().numpy(), A_ref[0], 1e-3, what="A (one layer, one KV head)")
+    np.testing.assert_allclose(dec.S.sum(dim=2).cpu().numpy(), 1.0, atol=1e-3)
+    # the period appended the new tokens' E = D * H after the kept slots' E
+    E_app = Ecur.clone()
+    E_app[:, :, k:] = dec.D[:, None, :] * dec.H[None, None, :]
+    S = dec.S.cpu().numpy()
+    for l in range(L):
+        check_topk_property(S[l], dec.idx[l].cpu().numpy(), k, win)
+        i64 = dec.idx[l].long()
+        assert torch.equal(torch.gather(Kcur[l], 1, i64[:, :, None].expand(-1, -1, w.head_dim)),
+                           dec.K[nxt][l][:, :k])
+        assert torch.equal(torch.gather(E_app[l], 1, i64), dec.E[nxt][l, :, :k])
+    del inp, new, pre, dec
+    torch.cuda.empty_cache()
+
+
+def check_topk_property(S_gpu, idx, k, w):
+    """idx is the window plus the top k - w of S over the body (ties to the lower
+    index), ascending, on the GPU's own float32 scores."""
+    Hkv, n = S_gpu.shape
+    nb = n - w
+    for g in range(Hkv):
+        ii = np.asarray(idx[g])
+        assert np.all(np.diff(ii) > 0)
+        assert ii[-w:].tolist() == list(range(nb, n))
+        body = ii[ii < nb]
+        assert body.size == k - w
+        kept = np.zeros(nb, dtype=bool)
+        kept[body] = True
+        s = S_gpu[g, :nb]
+        lo, hi = s[kept].min(), s[~kept].max()
+        assert lo >= hi
+        if lo == hi:
+            assert np.nonzero(kept & (s == lo))[0].max() < np.nonzero(~kept & (s == lo))[0].min()
