@@ -12,6 +12,8 @@ The oracle is plain numpy in float64, written from the pages' definitions:
                   bound;
   * ``selkv``     SelKV's VATP + GQA-union selection, bucket routing, soft
                   cosine gate, gated merge and log-ratio compensation;
+  * ``recas``     RECAS's active-set decoding (sparse score, top-K_t active
+                  set, attention over it);
   * ``precision`` exact bf16 <-> float64 conversions.
 
 Pins (closed forms, invariants, library special cases, brute force) live in
@@ -20,4 +22,4 @@ are pinned only through those invariants and the shared code; the readings the
 pages leave open (group union, gated ratio, merge target) are choices no page
 number confirms.
 """
-from . import infokv, precision, selkv  # noqa: F401
+from . import infokv, precision, recas, selkv  # noqa: F401
