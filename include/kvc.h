@@ -282,6 +282,42 @@ int kvc_decode_attn(const void* const* q, const void* const* K, const void* cons
                     int Hq, int Hkv, int64_t len, int d, float scale, float* o_out,
                     float* lse_out, void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * Active-set scores of one decode step ([RECAS] section 2.C, dynamic sparse
+ * decoding attention: a query-aware sparse score over the retained cache, whose
+ * top K_t entries form the active set attended this step):
+ *   score_out[l, g, j] = max over the query heads h of group g of
+ *                        scale * <q[l][h, :], K[l][g, j, :]>  +  beta * utility[l][g, j]
+ * The page adds a utility score to the query-key compatibility without fixing
+ * its inputs, so the utility row is the caller's (NULL: compatibility only).
+ * The active set is kvc_select_topk(score_out, K_t, w = 0).
+ *   q          host array of L device pointers, each [Hq, d] of dtype.
+ *   K          host array of L device pointers, each [Hkv, len, d] of dtype.
+ *   utility    host array of L device pointers, each float32 [Hkv, len], or NULL.
+ *   score_out  device float32 [L, Hkv, len].
+ *   Hq / Hkv <= 8; L * Hkv <= 65535; d <= 256.
+ */
+int kvc_active_scores(const void* const* q, const void* const* K, int dtype,
+                      const float* const* utility, float beta, int L, int Hq, int Hkv,
+                      int64_t len, int d, float scale, float* score_out, void* stream);
+
+/*
+ * Decode attention over an active set ([RECAS] section 2.C: only the active
+ * entries take part in this step's attention; the others stay in the cache):
+ * kvc_decode_attn with the softmax and the output taken over the rows
+ * active[l][g, 0 .. k_active) of each KV head's cache (any order; a row listed
+ * twice counts twice).  With every row listed it is kvc_decode_attn.
+ *   active     host array of L device pointers, each int32 [Hkv, k_active],
+ *              every entry in [0, len) (not checked on the device).
+ *   1 <= k_active <= len; other arguments, the workspace size
+ *   (kvc_decode_attn_workspace_size(L, Hq, len, d)) and errors as kvc_decode_attn.
+ */
+int kvc_decode_attn_active(const void* const* q, const void* const* K, const void* const* V,
+                           int dtype, const float* const* logR, float alpha_bias,
+                           const int32_t* const* active, int64_t k_active, int L, int Hq,
+                           int Hkv, int64_t len, int d, float scale, float* o_out,
+                           float* lse_out, void* ws, size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

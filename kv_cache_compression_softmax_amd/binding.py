@@ -46,6 +46,10 @@ _SIGNATURES = {
     "kvc_fuse_scores_slots_workspace_size": ([_i32, _i32, _i64], _sz),
     "kvc_fuse_scores_slots": ([_vp, _vp, _i32, _i32, _i64, _f32, _vp, _vp, _vp, _sz, _vp], _i32),
     "kvc_append_entropy_scores": ([_vp, _vp, _i32, _i32, _i64, _vp, _i64, _i64, _vp], _i32),
+    "kvc_active_scores": ([_vp, _vp, _i32, _vp, _f32, _i32, _i32, _i32, _i64, _i32, _f32, _vp, _vp],
+                          _i32),
+    "kvc_decode_attn_active": ([_vp, _vp, _vp, _i32, _vp, _f32, _vp, _i64, _i32, _i32, _i32, _i64,
+                                _i32, _f32, _vp, _vp, _vp, _sz, _vp], _i32),
     "kvc_decode_attn_workspace_size": ([_i32, _i32, _i64, _i32], _sz),
     "kvc_decode_attn": ([_vp, _vp, _vp, _i32, _vp, _f32, _i32, _i32, _i32, _i64, _i32, _f32, _vp,
                          _vp, _vp, _sz, _vp], _i32),
@@ -333,5 +337,47 @@ def kvc_decode_attn(q, K, V, logR, alpha_bias: float, scale: float, o_out: torch
     _check("kvc_decode_attn", lib().kvc_decode_attn(
         qp, kp, vp, _dtype(K[0]), lp[0] if lp else None, alpha_bias, L, Hq, Hkv, length, d, scale,
         _ptr(o_out, torch.float32), _ptr(lse_out, torch.float32) if lse_out is not None else None,
+        _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+    return o_out, lse_out
+
+
+def kvc_active_scores(q, K, scale: float, score_out: torch.Tensor, utility=None, beta: float = 0.0,
+                      stream=None):
+    """score_out [L, Hkv, len] = max over each group's heads of scale*<q, k> (+ beta*utility)."""
+    L = len(K)
+    Hq, d = q[0].shape
+    Hkv, length, _ = K[0].shape
+    dt = K[0].dtype
+    qp, a1 = _ptrs(q, dt)
+    kp, a2 = _ptrs(K, dt)
+    up = _ptrs(utility, torch.float32)
+    _check("kvc_active_scores", lib().kvc_active_scores(
+        qp, kp, _dtype(K[0]), up[0] if up else None, beta, L, Hq, Hkv, length, d, scale,
+        _ptr(score_out, torch.float32), _stream(stream)))
+    return score_out
+
+
+def kvc_decode_attn_active(q, K, V, logR, alpha_bias: float, active, scale: float,
+                           o_out: torch.Tensor, lse_out: torch.Tensor | None = None, ws=None,
+                           stream=None):
+    """Decode attention over the rows active[l][g, :] of each KV head's cache."""
+    L = len(K)
+    Hq, d = q[0].shape
+    Hkv, length, _ = K[0].shape
+    k_active = active[0].shape[1]
+    for a in active:
+        if tuple(a.shape) != (Hkv, k_active):
+            raise ValueError("active index lists must all be [Hkv, k_active]")
+    dt = K[0].dtype
+    ws = _ws(kvc_decode_attn_workspace_size(L, Hq, length, d), K[0].device, ws)
+    qp, a1 = _ptrs(q, dt)
+    kp, a2 = _ptrs(K, dt)
+    vp, a3 = _ptrs(V, dt)
+    ip, a4 = _ptrs(active, torch.int32)
+    lp = _ptrs(logR, torch.float32)
+    _check("kvc_decode_attn_active", lib().kvc_decode_attn_active(
+        qp, kp, vp, _dtype(K[0]), lp[0] if lp else None, alpha_bias, ip, k_active, L, Hq, Hkv,
+        length, d, scale, _ptr(o_out, torch.float32),
+        _ptr(lse_out, torch.float32) if lse_out is not None else None,
         _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
     return o_out, lse_out

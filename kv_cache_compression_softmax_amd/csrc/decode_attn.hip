@@ -68,7 +68,12 @@ template <> struct DE<float> {
   }
 };
 
-struct DecTables { ConstPtrs q, K, V, logR; };
+// ix: per layer an int32 [Hkv, npos] list of cache rows to attend over (the
+// active set), or null for rows 0..len-1 (then npos = len)
+__device__ __forceinline__ float elem_f32(uint16_t b) { return bf16_to_f32(b); }
+__device__ __forceinline__ float elem_f32(float f) { return f; }
+
+struct DecTables { ConstPtrs q, K, V, logR, ix; int64_t npos; };
 
 // partial layout: [lc, Hq, nchunk] x (m, l, -, -, o[d]), 16-byte aligned rows
 template <typename T, int LG, int G>
@@ -89,6 +94,7 @@ decode_partial(DecTables t, int Hq, int Hkv, int64_t len, int d, float scale, fl
   const T* K = (const T*)t.K.p[l] + (int64_t)g * len * d;
   const T* V = (const T*)t.V.p[l] + (int64_t)g * len * d;
   const float* lr = t.logR.p[l] ? (const float*)t.logR.p[l] + (int64_t)g * len : nullptr;
+  const int32_t* ix = t.ix.p[l] ? (const int32_t*)t.ix.p[l] + (int64_t)g * t.npos : nullptr;
 
   float qv[G][W];
 #pragma unroll
@@ -101,8 +107,9 @@ decode_partial(DecTables t, int Hq, int Hkv, int64_t len, int d, float scale, fl
 #pragma unroll
     for (int e = 0; e < W; ++e) o[h][e] = 0.f;
   }
-  const int64_t j0 = (int64_t)ch * CK, j1 = min(len, j0 + CK);
-  for (int64_t j = j0 + grp; j < j1; j += NG) {
+  const int64_t j0 = (int64_t)ch * CK, j1 = min(t.npos, j0 + CK);
+  for (int64_t jp = j0 + grp; jp < j1; jp += NG) {
+    const int64_t j = ix ? (int64_t)ix[jp] : jp;
     float kx[W], vx[W];
     DE<T>::unpack(*reinterpret_cast<const uint4*>(K + j * d + c * W), kx);
     DE<T>::unpack(*reinterpret_cast<const uint4*>(V + j * d + c * W), vx);
@@ -178,11 +185,14 @@ struct DecTile {
   float lr;
 };
 
-template <int D, bool BIAS>
+// jb, jlast are positions; with IDX the cache row of position p is ix[p]
+template <int D, bool BIAS, bool IDX>
 __device__ __forceinline__ void dec_load(DecTile<D>& t, const uint16_t* K, const uint16_t* V,
-                                         const float* lr, int64_t jb, int64_t jlast, int lane) {
+                                         const float* lr, const int32_t* ix, int64_t jb,
+                                         int64_t jlast, int lane) {
   constexpr int VL = DecTile<D>::VL, KPI = 64 / VL;
-  const int64_t kk = min(jb + (lane & 15), jlast);
+  const int64_t kp = min(jb + (lane & 15), jlast);
+  const int64_t kk = IDX ? (int64_t)ix[kp] : kp;
   const uint16_t* kr = K + kk * D + 8 * (lane >> 4);
 #pragma unroll
   for (int s = 0; s < DecTile<D>::KB; ++s) {
@@ -191,7 +201,8 @@ __device__ __forceinline__ void dec_load(DecTile<D>& t, const uint16_t* K, const
   }
 #pragma unroll
   for (int i = 0; i < DecTile<D>::VI; ++i) {
-    const int64_t kv = min(jb + i * KPI + lane / VL, jlast);
+    const int64_t vp = min(jb + i * KPI + lane / VL, jlast);
+    const int64_t kv = IDX ? (int64_t)ix[vp] : vp;
     t.v[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(V + kv * D + 8 * (lane % VL)));
   }
   t.lr = BIAS ? lr[kk] : 0.f;
@@ -208,7 +219,7 @@ __device__ __forceinline__ float row16_max(float v) {
   return v;
 }
 
-template <int D, bool BIAS>
+template <int D, bool BIAS, bool IDX>
 __global__ void __launch_bounds__(NT)
 decode_mfma(DecTables t, int Hq, int Hkv, int G, int64_t len, float sl2, float bl2, int nchunk,
             int64_t ckm, int64_t nw, float* __restrict__ part) {
@@ -225,6 +236,7 @@ decode_mfma(DecTables t, int Hq, int Hkv, int G, int64_t len, float sl2, float b
   const uint16_t* K = (const uint16_t*)t.K.p[l] + (int64_t)g * len * D;
   const uint16_t* V = (const uint16_t*)t.V.p[l] + (int64_t)g * len * D;
   const float* lr = BIAS ? (const float*)t.logR.p[l] + (int64_t)g * len : nullptr;
+  const int32_t* ix = IDX ? (const int32_t*)t.ix.p[l] + (int64_t)g * t.npos : nullptr;
 
   // A operand: row c = lane % 16 holds query head c % 4 (zero if that head is >= G)
   bf16x8 qa[KB];
@@ -239,7 +251,7 @@ decode_mfma(DecTables t, int Hq, int Hkv, int G, int64_t len, float sl2, float b
       qa[s] = __builtin_bit_cast(bf16x8, x);
     }
   }
-  const int64_t j0 = (int64_t)ch * ckm, j1 = min(len, j0 + ckm), jlast = j1 - 1;
+  const int64_t j0 = (int64_t)ch * ckm, j1 = min(t.npos, j0 + ckm), jlast = j1 - 1;
   const int ntile = (int)((j1 - j0 + 15) / 16);
   float m[4], ls[4], o[4][8];
 #pragma unroll
@@ -315,7 +327,7 @@ decode_mfma(DecTables t, int Hq, int Hkv, int G, int64_t len, float sl2, float b
   const int64_t jl = j0 + (int64_t)(ntile - 1) * 16;      // the last tile
   DecTile<D> ts[kSets];
 #pragma unroll
-  for (int u = 0; u + 1 < kSets; ++u) dec_load<D, BIAS>(ts[u], K, V, lr, min(j0 + 16 * u, jl), jlast, lane);
+  for (int u = 0; u + 1 < kSets; ++u) dec_load<D, BIAS, IDX>(ts[u], K, V, lr, ix, min(j0 + 16 * u, jl), jlast, lane);
   for (int ti = 0; ti < ntile; ti += kSets) {
     const int64_t jb = j0 + (int64_t)ti * 16;
 #pragma unroll
@@ -323,7 +335,7 @@ decode_mfma(DecTables t, int Hq, int Hkv, int G, int64_t len, float sl2, float b
       // the scheduling barrier keeps each refill below the last use of the set it
       // overwrites (otherwise the sets are renamed and copied, with a wait per copy)
       __builtin_amdgcn_sched_barrier(0);
-      dec_load<D, BIAS>(ts[(u + kSets - 1) % kSets], K, V, lr, min(jb + 16 * (u + kSets - 1), jl), jlast, lane);
+      dec_load<D, BIAS, IDX>(ts[(u + kSets - 1) % kSets], K, V, lr, ix, min(jb + 16 * (u + kSets - 1), jl), jlast, lane);
       asm volatile("" ::: "memory");
       tile(ts[u], jb + 16 * u);
     }
@@ -350,6 +362,98 @@ decode_mfma(DecTables t, int Hq, int Hkv, int G, int64_t len, float sl2, float b
       *reinterpret_cast<float4*>(p + 8 + 8 * lane) = make_float4(o[e][4], o[e][5], o[e][6], o[e][7]);
     }
   }
+}
+
+// ---- active set of a decode step ([RECAS] section 2.C) -------------------------
+// score[l, g, j] = max over the group's query heads of scale * <q_h, k_j>
+//                  (+ beta * u[l][g, j] when a utility row is given)
+// One wave per chunk of keys, 16-key tiles of K in the MFMA B layout (as in
+// decode_mfma, without V), logits on v_mfma_f32_16x16x32_bf16.
+template <int D>
+__global__ void __launch_bounds__(NT)
+active_scores_mfma(DecTables t, int Hkv, int G, int64_t len, float scale, float beta,
+                   int nchunk, int64_t ckm, int64_t nw, float* __restrict__ score) {
+  constexpr int KB = D / 32;
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t wid = (int64_t)blockIdx.x * (NT / 64) + wv;
+  if (wid >= nw) return;
+  const int ch = (int)(wid % nchunk);
+  const int g = (int)((wid / nchunk) % Hkv);
+  const int l = (int)(wid / ((int64_t)nchunk * Hkv));
+  const uint16_t* q = (const uint16_t*)t.q.p[l];
+  const uint16_t* K = (const uint16_t*)t.K.p[l] + (int64_t)g * len * D;
+  const float* u = (const float*)t.logR.p[l];          // utility rows, or null
+  if (u) u += (int64_t)g * len;
+  float* out = score + ((int64_t)l * Hkv + g) * len;
+  bf16x8 qa[KB];
+  {
+    const int h = (lane & 15) & 3;
+    const unsigned keep = h < G ? ~0u : 0u;
+    const uint16_t* qr = q + (int64_t)(g * G + (h < G ? h : 0)) * D + 8 * (lane >> 4);
+#pragma unroll
+    for (int s2 = 0; s2 < KB; ++s2) {
+      u32x4 x = *reinterpret_cast<const u32x4*>(qr + 32 * s2);
+      x &= keep;
+      qa[s2] = __builtin_bit_cast(bf16x8, x);
+    }
+  }
+  const int64_t j0 = (int64_t)ch * ckm, j1 = min(len, j0 + ckm), jlast = j1 - 1;
+  const int ntile = (int)((j1 - j0 + 15) / 16);
+  auto load = [&](bf16x8 (&kt)[KB], int64_t jb) __attribute__((always_inline)) {
+    const int64_t kk = min(jb + (lane & 15), jlast);
+    const uint16_t* kr = K + kk * D + 8 * (lane >> 4);
+#pragma unroll
+    for (int s2 = 0; s2 < KB; ++s2)
+      kt[s2] = __builtin_bit_cast(bf16x8, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kr + 32 * s2)));
+  };
+  auto tile = [&](const bf16x8 (&kt)[KB], int64_t jb) __attribute__((always_inline)) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s2 = 0; s2 < KB; ++s2) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[s2], kt[s2], acc, 0, 0, 0);
+    float m = acc[0];
+#pragma unroll
+    for (int e = 1; e < 4; ++e) m = e < G ? fmaxf(m, acc[e]) : m;
+    const int64_t j = jb + (lane & 15);
+    if (lane < 16 && j <= jlast) out[j] = m * scale + (u ? beta * u[j] : 0.f);
+  };
+  // two register sets in turn; a tile past the chunk's end is clamped and not stored
+  const int64_t jl = j0 + (int64_t)(ntile - 1) * 16;
+  bf16x8 ka[KB], kb[KB];
+  load(ka, j0);
+  for (int ti = 0; ti < ntile; ti += 2) {
+    const int64_t jb = j0 + (int64_t)ti * 16;
+    __builtin_amdgcn_sched_barrier(0);
+    load(kb, min(jb + 16, jl));
+    asm volatile("" ::: "memory");
+    tile(ka, jb);
+    __builtin_amdgcn_sched_barrier(0);
+    load(ka, min(jb + 32, jl));
+    asm volatile("" ::: "memory");
+    if (jb + 16 <= jlast) tile(kb, jb + 16);
+  }
+}
+
+// General path (float32, other d, G up to 8): one thread per key.
+template <typename T>
+__global__ void __launch_bounds__(NT)
+active_scores_any(DecTables t, int Hkv, int G, int64_t len, int d, float scale, float beta,
+                  float* __restrict__ score) {
+  const int64_t row = blockIdx.y;                      // (layer, KV head)
+  const int l = (int)(row / Hkv), g = (int)(row % Hkv);
+  const int64_t j = (int64_t)blockIdx.x * NT + threadIdx.x;
+  if (j >= len) return;
+  const T* q = (const T*)t.q.p[l];
+  const T* k = (const T*)t.K.p[l] + ((int64_t)g * len + j) * d;
+  float m = -INFINITY;
+  for (int h = 0; h < G; ++h) {
+    const T* qh = q + (int64_t)(g * G + h) * d;
+    float acc = 0.f;
+    for (int e = 0; e < d; ++e) acc += elem_f32(qh[e]) * elem_f32(k[e]);
+    m = fmaxf(m, acc);
+  }
+  const float* u = (const float*)t.logR.p[l];
+  score[row * len + j] = m * scale + (u ? beta * u[(int64_t)g * len + j] : 0.f);
 }
 
 __global__ void decode_combine(const float* __restrict__ part, int nchunk, int d, int64_t nhead,
@@ -433,52 +537,63 @@ extern "C" size_t kvc_decode_attn_workspace_size(int L, int Hq, int64_t len, int
   return max(launch_bytes(lc), rest ? launch_bytes(rest) : (size_t)0) + 256;
 }
 
-extern "C" int kvc_decode_attn(const void* const* q, const void* const* K, const void* const* V,
-                               int dtype, const float* const* logR, float alpha_bias, int L, int Hq,
-                               int Hkv, int64_t len, int d, float scale, float* o_out, float* lse_out,
-                               void* ws, size_t ws_bytes, void* stream) {
+namespace {
+
+int decode_impl(const char* fn, const void* const* q, const void* const* K, const void* const* V,
+                int dtype, const float* const* logR, float alpha_bias, const int32_t* const* ix,
+                int64_t npos, int L, int Hq, int Hkv, int64_t len, int d, float scale, float* o_out,
+                float* lse_out, void* ws, size_t ws_bytes, void* stream) {
   clear_error();
-  if (!dtype_ok(dtype)) return KVC_FAIL(KVC_ERR_DTYPE, "kvc_decode_attn: dtype %d", dtype);
-  KVC_REQUIRE(L >= 1 && L <= KVC_MAX_LAYERS, "kvc_decode_attn: need 1 <= L <= %d", KVC_MAX_LAYERS);
-  KVC_REQUIRE(Hkv >= 1 && Hq >= Hkv && Hq % Hkv == 0, "kvc_decode_attn: need Hq %% Hkv == 0");
-  KVC_REQUIRE(Hq / Hkv <= MAXG, "kvc_decode_attn: more than %d query heads per KV head", MAXG);
-  KVC_REQUIRE(len >= 1 && len <= 0x7fffffffLL, "kvc_decode_attn: need 1 <= len < 2^31");
-  KVC_REQUIRE(q && K && V && o_out, "kvc_decode_attn: null pointer");
+  if (!dtype_ok(dtype)) return KVC_FAIL(KVC_ERR_DTYPE, "%s: dtype %d", fn, dtype);
+  KVC_REQUIRE(L >= 1 && L <= KVC_MAX_LAYERS, "%s: need 1 <= L <= %d", fn, KVC_MAX_LAYERS);
+  KVC_REQUIRE(Hkv >= 1 && Hq >= Hkv && Hq % Hkv == 0, "%s: need Hq %% Hkv == 0", fn);
+  KVC_REQUIRE(Hq / Hkv <= MAXG, "%s: more than %d query heads per KV head", fn, MAXG);
+  KVC_REQUIRE(len >= 1 && len <= 0x7fffffffLL, "%s: need 1 <= len < 2^31", fn);
+  KVC_REQUIRE(q && K && V && o_out, "%s: null pointer", fn);
   const int rb = d * dtype_size(dtype);
   KVC_REQUIRE(d <= 256 && rb % 16 == 0 && (rb / 16 == 4 || rb / 16 == 8 || rb / 16 == 16 || rb / 16 == 32),
-              "kvc_decode_attn: need d * elsize in {64, 128, 256, 512} bytes and d <= 256");
+              "%s: need d * elsize in {64, 128, 256, 512} bytes and d <= 256", fn);
   const int LG = rb / 16;
   for (int l = 0; l < L; ++l) {
-    KVC_REQUIRE(q[l] && K[l] && V[l], "kvc_decode_attn: null pointer in layer %d", l);
+    KVC_REQUIRE(q[l] && K[l] && V[l], "%s: null pointer in layer %d", fn, l);
     KVC_REQUIRE((uintptr_t)q[l] % 16 == 0 && (uintptr_t)K[l] % 16 == 0 && (uintptr_t)V[l] % 16 == 0,
-                "kvc_decode_attn: layer %d tensors not 16-byte aligned", l);
-    KVC_REQUIRE(!logR || logR[l], "kvc_decode_attn: logR[%d] is null", l);
+                "%s: layer %d tensors not 16-byte aligned", fn, l);
+    KVC_REQUIRE(!logR || logR[l], "%s: logR[%d] is null", fn, l);
+    KVC_REQUIRE(!ix || ix[l], "%s: active index list of layer %d is null", fn, l);
   }
+  KVC_REQUIRE(npos >= 1 && npos <= len, "%s: need 1 <= positions <= len", fn);
   const size_t need = kvc_decode_attn_workspace_size(L, Hq, len, d);
   if (!ws || ws_bytes < need)
-    return KVC_FAIL(KVC_ERR_WORKSPACE, "kvc_decode_attn: workspace needs %zu bytes", need);
+    return KVC_FAIL(KVC_ERR_WORKSPACE, "%s: workspace needs %zu bytes", fn, need);
   float* part = (float*)(((uintptr_t)ws + 255) & ~(uintptr_t)255);
   hipStream_t s = as_stream(stream);
   const int G = Hq / Hkv;
   const bool mfma = dtype == KVC_BF16 && G <= 4 && (d == 64 || d == 128);
-  const int nchunk_g = (int)((len + CK - 1) / CK);
+  const int nchunk_g = (int)((npos + CK - 1) / CK);
   for (int l0 = 0; l0 < L; l0 += kLayersPerLaunch) {
     const int lc = min(kLayersPerLaunch, L - l0);
     DecTables t{};
     for (int i = 0; i < lc; ++i) {
       t.q.p[i] = q[l0 + i]; t.K.p[i] = K[l0 + i]; t.V.p[i] = V[l0 + i];
       t.logR.p[i] = logR ? logR[l0 + i] : nullptr;
+      t.ix.p[i] = ix ? ix[l0 + i] : nullptr;
     }
+    t.npos = npos;
     int nchunk = nchunk_g;
     if (mfma) {
-      const int64_t ckm = mfma_chunk_len(len, mfma_chunks(lc, Hkv, len));
-      nchunk = (int)((len + ckm - 1) / ckm);
+      const int64_t ckm = mfma_chunk_len(npos, mfma_chunks(lc, Hkv, npos));
+      nchunk = (int)((npos + ckm - 1) / ckm);
       const int64_t nw = (int64_t)lc * Hkv * nchunk;
       const dim3 grid((unsigned)((nw + NT / 64 - 1) / (NT / 64)));
       const float sl2 = scale * LOG2E, bl2 = alpha_bias * LOG2E;
-#define KVC_M(DD, BB) hipLaunchKernelGGL((decode_mfma<DD, BB>), grid, dim3(NT), 0, s, t, Hq, Hkv, G, len, sl2, bl2, nchunk, ckm, nw, part)
-      if (d == 128) { if (logR) KVC_M(128, true); else KVC_M(128, false); }
-      else { if (logR) KVC_M(64, true); else KVC_M(64, false); }
+#define KVC_M(DD, BB, II) hipLaunchKernelGGL((decode_mfma<DD, BB, II>), grid, dim3(NT), 0, s, t, Hq, Hkv, G, len, sl2, bl2, nchunk, ckm, nw, part)
+      if (ix) {
+        if (d == 128) { if (logR) KVC_M(128, true, true); else KVC_M(128, false, true); }
+        else { if (logR) KVC_M(64, true, true); else KVC_M(64, false, true); }
+      } else {
+        if (d == 128) { if (logR) KVC_M(128, true, false); else KVC_M(128, false, false); }
+        else { if (logR) KVC_M(64, true, false); else KVC_M(64, false, false); }
+      }
 #undef KVC_M
     } else {
       const dim3 grid((unsigned)((int64_t)lc * Hkv * nchunk));
@@ -489,5 +604,75 @@ extern "C" int kvc_decode_attn(const void* const* q, const void* const* K, const
     hipLaunchKernelGGL(decode_combine, dim3((unsigned)nhead), dim3(128), 0, s, (const float*)part, nchunk,
                        d, nhead, o_out + (int64_t)l0 * Hq * d, lse_out ? lse_out + (int64_t)l0 * Hq : nullptr);
   }
-  return launch_status("kvc_decode_attn");
+  return launch_status(fn);
+}
+
+}  // namespace
+
+extern "C" int kvc_decode_attn(const void* const* q, const void* const* K, const void* const* V,
+                               int dtype, const float* const* logR, float alpha_bias, int L, int Hq,
+                               int Hkv, int64_t len, int d, float scale, float* o_out, float* lse_out,
+                               void* ws, size_t ws_bytes, void* stream) {
+  return decode_impl("kvc_decode_attn", q, K, V, dtype, logR, alpha_bias, nullptr, len, L, Hq, Hkv,
+                     len, d, scale, o_out, lse_out, ws, ws_bytes, stream);
+}
+
+extern "C" int kvc_decode_attn_active(const void* const* q, const void* const* K,
+                                      const void* const* V, int dtype, const float* const* logR,
+                                      float alpha_bias, const int32_t* const* active,
+                                      int64_t k_active, int L, int Hq, int Hkv, int64_t len, int d,
+                                      float scale, float* o_out, float* lse_out, void* ws,
+                                      size_t ws_bytes, void* stream) {
+  if (!active) {
+    clear_error();
+    return KVC_FAIL(KVC_ERR_ARG, "kvc_decode_attn_active: null active index list");
+  }
+  return decode_impl("kvc_decode_attn_active", q, K, V, dtype, logR, alpha_bias, active, k_active,
+                     L, Hq, Hkv, len, d, scale, o_out, lse_out, ws, ws_bytes, stream);
+}
+
+
+extern "C" int kvc_active_scores(const void* const* q, const void* const* K, int dtype,
+                                 const float* const* utility, float beta, int L, int Hq, int Hkv,
+                                 int64_t len, int d, float scale, float* score_out, void* stream) {
+  clear_error();
+  if (!dtype_ok(dtype)) return KVC_FAIL(KVC_ERR_DTYPE, "kvc_active_scores: dtype %d", dtype);
+  KVC_REQUIRE(L >= 1 && L <= KVC_MAX_LAYERS, "kvc_active_scores: need 1 <= L <= %d", KVC_MAX_LAYERS);
+  KVC_REQUIRE(Hkv >= 1 && Hq >= Hkv && Hq % Hkv == 0, "kvc_active_scores: need Hq %% Hkv == 0");
+  KVC_REQUIRE(Hq / Hkv <= MAXG, "kvc_active_scores: more than %d query heads per KV head", MAXG);
+  KVC_REQUIRE(len >= 1 && len <= 0x7fffffffLL && d >= 1 && d <= 256,
+              "kvc_active_scores: need 1 <= len < 2^31 and 1 <= d <= 256");
+  KVC_REQUIRE(q && K && score_out, "kvc_active_scores: null pointer");
+  KVC_REQUIRE((int64_t)L * Hkv <= 65535, "kvc_active_scores: L * Hkv > 65535");
+  const int G = Hq / Hkv;
+  const bool mfma = dtype == KVC_BF16 && G <= 4 && (d == 64 || d == 128);
+  for (int l = 0; l < L; ++l) {
+    KVC_REQUIRE(q[l] && K[l], "kvc_active_scores: null pointer in layer %d", l);
+    KVC_REQUIRE(!utility || utility[l], "kvc_active_scores: utility[%d] is null", l);
+    KVC_REQUIRE(!mfma || ((uintptr_t)q[l] % 16 == 0 && (uintptr_t)K[l] % 16 == 0),
+                "kvc_active_scores: layer %d tensors not 16-byte aligned", l);
+  }
+  hipStream_t s = as_stream(stream);
+  for (int l0 = 0; l0 < L; l0 += kLayersPerLaunch) {
+    const int lc = min(kLayersPerLaunch, L - l0);
+    DecTables t{};
+    for (int i = 0; i < lc; ++i) {
+      t.q.p[i] = q[l0 + i]; t.K.p[i] = K[l0 + i];
+      t.logR.p[i] = utility ? utility[l0 + i] : nullptr;
+    }
+    float* out = score_out + (int64_t)l0 * Hkv * len;
+    if (mfma) {
+      const int64_t ckm = mfma_chunk_len(len, mfma_chunks(lc, Hkv, len));
+      const int nchunk = (int)((len + ckm - 1) / ckm);
+      const int64_t nw = (int64_t)lc * Hkv * nchunk;
+      const dim3 grid((unsigned)((nw + NT / 64 - 1) / (NT / 64)));
+      if (d == 128) hipLaunchKernelGGL(active_scores_mfma<128>, grid, dim3(NT), 0, s, t, Hkv, G, len, scale, beta, nchunk, ckm, nw, out);
+      else hipLaunchKernelGGL(active_scores_mfma<64>, grid, dim3(NT), 0, s, t, Hkv, G, len, scale, beta, nchunk, ckm, nw, out);
+    } else {
+      const dim3 grid((unsigned)((len + NT - 1) / NT), (unsigned)(lc * Hkv));
+      if (dtype == KVC_BF16) hipLaunchKernelGGL(active_scores_any<uint16_t>, grid, dim3(NT), 0, s, t, Hkv, G, len, d, scale, beta, out);
+      else hipLaunchKernelGGL(active_scores_any<float>, grid, dim3(NT), 0, s, t, Hkv, G, len, d, scale, beta, out);
+    }
+  }
+  return launch_status("kvc_active_scores");
 }
