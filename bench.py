@@ -410,7 +410,8 @@ def main():
         # row a12's decode check (compensated decode over the compacted cache and
         # plain decode over the full cache, one query per head and layer), timed
         # apart: it checks the compressed cache rather than producing it
-        plan.decode_check(inp)
+        act_frac = 0.293        # the active share of the retained cache [RECAS] reports
+        plan.decode_check(inp, active_fraction=act_frac)
         torch.cuda.synchronize()
         dmarks = []
 
@@ -420,7 +421,7 @@ def main():
             dmarks.append((name, ev))
 
         for _ in range(args.steps):
-            plan.decode_check(inp, mark=dmark)
+            plan.decode_check(inp, mark=dmark, active_fraction=act_frac)
         torch.cuda.synchronize()
         dper = {}
         for (n0, e0), (n1, e1) in zip(dmarks[:-1], dmarks[1:]):
@@ -430,8 +431,14 @@ def main():
         L, Hq, Hkv, d = w.layers, w.heads_q, w.heads_kv, w.head_dim
         m = plan.m[0]
         # K and V rows read once, ln R once (compacted), the query and the output
+        kt = max(1, int(math.floor(act_frac * m)))
         dbytes = {"decode_compacted": L * Hkv * m * (2 * d * e + 4) + L * Hq * d * (e + 4),
-                  "decode_full": L * Hkv * w.n * 2 * d * e + L * Hq * d * (e + 4)}
+                  "decode_full": L * Hkv * w.n * 2 * d * e + L * Hq * d * (e + 4),
+                  # K and ln R read, the score row written; the score row read and the
+                  # active list written; the active rows' K, V and ln R and the list read
+                  "active_scores": L * Hkv * m * (d * e + 4 + 4) + L * Hq * d * e,
+                  "active_select": L * Hkv * m * 4 + L * Hkv * kt * 4,
+                  "decode_active": L * Hkv * kt * (2 * d * e + 4 + 4) + L * Hq * d * (e + 4)}
         dec = {}
         for k, v in dper.items():
             t = sum(v) / len(v)
@@ -439,6 +446,9 @@ def main():
                       "GBps": round(dbytes[k] / (t * 1e-3) / 1e9, 1),
                       "frac_hbm": round(dbytes[k] / (t * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
                       "traffic": measured_traffic(w.name, k)}
+        dec["active_set"] = {"fraction": act_frac, "k_active": kt,
+                             "ms_step": round(sum(dec[k]["ms"] for k in
+                                                  ("active_scores", "active_select", "decode_active")), 4)}
         dec["timed"] = "separately, after the steps; not in ms_per_step"
         out["decode_check"] = dec
     if period:

@@ -42,6 +42,9 @@ constexpr int NT = 256;
 constexpr int CK = 1024;          // keys per workgroup (decode_partial)
 constexpr int kWaveTarget = 1024;  // decode_mfma waves per launch: MI355X's 256 CUs x 4 SIMDs
 constexpr int kSets = 2;           // decode_mfma register sets (tiles) per wave
+constexpr int kActiveWaves = 2048; // waves of decode_mfma over an active row list
+constexpr int kScoreWaves = 2048;  // waves of active_scores_mfma
+constexpr int kScoreSets = 2;      // active_scores_mfma register sets (tiles) per wave
 constexpr int MAXG = 8;           // query heads per KV head
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
@@ -417,20 +420,21 @@ active_scores_mfma(DecTables t, int Hkv, int G, int64_t len, float scale, float 
     const int64_t j = jb + (lane & 15);
     if (lane < 16 && j <= jlast) out[j] = m * scale + (u ? beta * u[j] : 0.f);
   };
-  // two register sets in turn; a tile past the chunk's end is clamped and not stored
+  // a ring of kScoreSets register sets, kScoreSets - 1 tiles' loads in flight; loads
+  // past the chunk's last tile are clamped to it, and a tile past the end is not stored
   const int64_t jl = j0 + (int64_t)(ntile - 1) * 16;
-  bf16x8 ka[KB], kb[KB];
-  load(ka, j0);
-  for (int ti = 0; ti < ntile; ti += 2) {
+  bf16x8 kt[kScoreSets][KB];
+#pragma unroll
+  for (int v = 0; v + 1 < kScoreSets; ++v) load(kt[v], min(j0 + 16 * v, jl));
+  for (int ti = 0; ti < ntile; ti += kScoreSets) {
     const int64_t jb = j0 + (int64_t)ti * 16;
-    __builtin_amdgcn_sched_barrier(0);
-    load(kb, min(jb + 16, jl));
-    asm volatile("" ::: "memory");
-    tile(ka, jb);
-    __builtin_amdgcn_sched_barrier(0);
-    load(ka, min(jb + 32, jl));
-    asm volatile("" ::: "memory");
-    if (jb + 16 <= jlast) tile(kb, jb + 16);
+#pragma unroll
+    for (int v = 0; v < kScoreSets; ++v) {
+      __builtin_amdgcn_sched_barrier(0);
+      load(kt[(v + kScoreSets - 1) % kScoreSets], min(jb + 16 * (v + kScoreSets - 1), jl));
+      asm volatile("" ::: "memory");
+      if (jb + 16 * v <= jlast) tile(kt[v], jb + 16 * v);
+    }
   }
 }
 
@@ -482,8 +486,8 @@ __global__ void decode_combine(const float* __restrict__ part, int nchunk, int d
 // decode_mfma's chunks per (layer, KV head): about kWaveTarget waves in all,
 // at least 32 keys each.  The chunk length is then ceil(len / nchunk) rounded up
 // to whole rings of kSets tiles.
-int64_t mfma_chunks(int lc, int Hkv, int64_t len) {
-  const int64_t per = (kWaveTarget + (int64_t)lc * Hkv - 1) / ((int64_t)lc * Hkv);
+int64_t mfma_chunks(int lc, int Hkv, int64_t len, int target = kWaveTarget) {
+  const int64_t per = (target + (int64_t)lc * Hkv - 1) / ((int64_t)lc * Hkv);
   return max((int64_t)1, min(per, (len + 31) / 32));
 }
 int64_t mfma_chunk_len(int64_t len, int64_t nchunk) {
@@ -529,7 +533,8 @@ extern "C" size_t kvc_decode_attn_workspace_size(int L, int Hq, int64_t len, int
   // partials of one launch (at most kLayersPerLaunch layers), for either kernel and
   // any Hkv >= 1; the last launch of L layers may cover fewer layers
   auto launch_bytes = [&](int lc) {
-    const int64_t nchunk = max((len + CK - 1) / CK, mfma_chunks(lc, 1, len));
+    const int64_t nchunk = max((len + CK - 1) / CK,
+                               mfma_chunks(lc, 1, len, max(kWaveTarget, kActiveWaves)));
     return (size_t)lc * Hq * nchunk * (d + 4) * sizeof(float);
   };
   const int lc = L < kLayersPerLaunch ? L : kLayersPerLaunch;
@@ -581,7 +586,7 @@ int decode_impl(const char* fn, const void* const* q, const void* const* K, cons
     t.npos = npos;
     int nchunk = nchunk_g;
     if (mfma) {
-      const int64_t ckm = mfma_chunk_len(npos, mfma_chunks(lc, Hkv, npos));
+      const int64_t ckm = mfma_chunk_len(npos, mfma_chunks(lc, Hkv, npos, ix ? kActiveWaves : kWaveTarget));
       nchunk = (int)((npos + ckm - 1) / ckm);
       const int64_t nw = (int64_t)lc * Hkv * nchunk;
       const dim3 grid((unsigned)((nw + NT / 64 - 1) / (NT / 64)));
@@ -662,7 +667,7 @@ extern "C" int kvc_active_scores(const void* const* q, const void* const* K, int
     }
     float* out = score_out + (int64_t)l0 * Hkv * len;
     if (mfma) {
-      const int64_t ckm = mfma_chunk_len(len, mfma_chunks(lc, Hkv, len));
+      const int64_t ckm = mfma_chunk_len(len, mfma_chunks(lc, Hkv, len, kScoreWaves));
       const int nchunk = (int)((len + ckm - 1) / ckm);
       const int64_t nw = (int64_t)lc * Hkv * nchunk;
       const dim3 grid((unsigned)((nw + NT / 64 - 1) / (NT / 64)));

@@ -262,11 +262,17 @@ class SelKVPlan:
                          torch.empty(max(1, nbytes), dtype=torch.uint8, device=dev))
         return self._dec
 
-    def decode_check(self, inp: dict, stream=None, mark=None):
+    def decode_check(self, inp: dict, stream=None, mark=None, active_fraction: float = 0.0):
         """Compensated decode over the compacted cache and plain decode over the
         full cache, one query per head and layer: (o', lse', o, lse).  The output
         buffers are the plan's own (allocated on the first call) and are
-        overwritten by the next call."""
+        overwritten by the next call.
+
+        With ``active_fraction`` > 0 it also runs RECAS's active-set step over
+        the compacted cache ([RECAS] section 2.C): sparse scores (the compensated
+        logit, max over the group's heads: compatibility plus alpha * ln R as
+        the utility), the top floor(fraction * m) entries per KV head, attention
+        over them; the outputs go to ``self.o_active``, ``self.lse_active``."""
         w = self.w
         mark = mark or (lambda name: None)
         q = [inp["q_dec"][l] for l in range(w.layers)]
@@ -277,4 +283,21 @@ class SelKVPlan:
         mark("decode_compacted")
         B.kvc_decode_attn(q, inp["k"], inp["v"], None, 0.0, self.scale, o_f, l_f, ws=ws, stream=stream)
         mark("decode_full")
+        if active_fraction > 0:
+            L, m = w.layers, self.m[0]
+            kt = max(1, int(math.floor(active_fraction * m)))
+            if getattr(self, "_act", None) is None or self._act[0] != kt:
+                dev = self.U.device
+                self._act = (kt, torch.empty(L, w.heads_kv, m, dtype=torch.float32, device=dev),
+                             [torch.empty(w.heads_kv, kt, dtype=torch.int32, device=dev) for _ in range(L)])
+                self.o_active = torch.empty_like(o_c)
+                self.lse_active = torch.empty_like(l_c)
+            _, sc, act = self._act
+            B.kvc_active_scores(q, self.Kc, self.scale, sc, self.logR, w.alpha_bias, stream=stream)
+            mark("active_scores")
+            B.kvc_select_topk(sc, [kt] * L, 0, act, stream=stream)
+            mark("active_select")
+            B.kvc_decode_attn_active(q, self.Kc, self.Vc, self.logR, w.alpha_bias, act, self.scale,
+                                     self.o_active, self.lse_active, ws=ws, stream=stream)
+            mark("decode_active")
         return o_c, l_c, o_f, l_f
