@@ -70,6 +70,8 @@ KERNEL_SOURCES = {
     "select_topk": ["select_topk.hip"], "compact": ["compact.hip"],
     "vatp_union": ["selkv.hip"], "merge_gated": ["selkv.hip"],
     "decode_compacted": ["decode_attn.hip"], "decode_full": ["decode_attn.hip"],
+    "active_scores": ["decode_attn.hip"], "active_select": ["select_topk.hip"],
+    "decode_active": ["decode_attn.hip"],
 }
 
 
