@@ -453,30 +453,47 @@ win_f32_stats(ConstPtrs qs, ConstPtrs ks, Geo g, float scale_log2, float* __rest
   if (threadIdx.x == 0) c[id] = M + log2f(S);
 }
 
-__global__ void __launch_bounds__(NTF)
+// One thread per key: the key row is read once (into registers when d is one of
+// the compiled sizes), then dotted with every window row of the group held in LDS.
+// Blocks of NTA threads, so that short caches still spread over many CUs.
+constexpr int NTA = 64;
+
+template <int D>
+__global__ void __launch_bounds__(NTA)
 win_f32_accum(ConstPtrs qs, ConstPtrs ks, Geo g, float scale_log2, const float* __restrict__ c,
               int per_head, float* __restrict__ A) {
   extern __shared__ float qall[];              // [R, d]
   const int R = g.G * g.w;
-  const int64_t nblk = (g.n + NTF - 1) / NTF;
+  const int d = D > 0 ? D : g.d;
+  const int64_t nblk = (g.n + NTA - 1) / NTA;
   const int64_t id = blockIdx.x;
   const int kvh = (int)((id / nblk) % g.Hkv);
   const int l = (int)(id / (nblk * g.Hkv));
-  const int64_t j = (id % nblk) * NTF + threadIdx.x;
-  const float* q = (const float*)qs.p[l] + (int64_t)kvh * g.G * g.w * g.d;
-  for (int e = threadIdx.x; e < R * g.d; e += NTF) qall[e] = q[e];
+  const int64_t j = (id % nblk) * NTA + threadIdx.x;
+  const float* q = (const float*)qs.p[l] + (int64_t)kvh * g.G * g.w * d;
+  for (int e = threadIdx.x; e < R * d; e += NTA) qall[e] = q[e];
   __syncthreads();
   if (j >= g.n) return;
-  const float* kr = (const float*)ks.p[l] + ((int64_t)kvh * g.n + j) * g.d;
+  const float* kr = (const float*)ks.p[l] + ((int64_t)kvh * g.n + j) * d;
   const float* cr = c + ((int64_t)l * g.Hkv + kvh) * R;
+  float kreg[D > 0 ? D : 1];
+  if constexpr (D > 0) {
+#pragma unroll
+    for (int e = 0; e < D; ++e) kreg[e] = kr[e];
+  }
   float total = 0.f;
   for (int h = 0; h < g.G; ++h) {
     float hs = 0.f;
     for (int rr = 0; rr < g.w; ++rr) {
       if (j > g.n - g.w + rr) continue;
-      const float* qr = qall + (h * g.w + rr) * g.d;
+      const float* qr = qall + (h * g.w + rr) * d;
       float dot = 0.f;
-      for (int e = 0; e < g.d; ++e) dot += qr[e] * kr[e];
+      if constexpr (D > 0) {
+#pragma unroll
+        for (int e = 0; e < D; ++e) dot += qr[e] * kreg[e];
+      } else {
+        for (int e = 0; e < d; ++e) dot += qr[e] * kr[e];
+      }
       hs += exp2f(dot * scale_log2 - cr[h * g.w + rr]);
     }
     if (per_head) A[((int64_t)l * g.Hq + kvh * g.G + h) * g.n + j] = hs / (float)g.w;
@@ -647,10 +664,19 @@ extern "C" int kvc_score_window_attn(const void* const* q_win, const void* const
       const int R = g.G * w;
       hipLaunchKernelGGL(win_f32_stats, dim3((unsigned)((int64_t)lc * Hkv * R)), dim3(NTF), 0, s,
                          qt, kt, g, sl2, cfin);
-      const int64_t nblk = (n + NTF - 1) / NTF;
-      hipLaunchKernelGGL(win_f32_accum, dim3((unsigned)(lc * Hkv * nblk)), dim3(NTF),
-                         (size_t)R * d * sizeof(float), s, qt, kt, g, sl2, (const float*)cfin,
-                         per_query_head, A);
+      const int64_t nblk = (n + NTA - 1) / NTA;
+      const dim3 ga((unsigned)(lc * Hkv * nblk));
+      const size_t lds = (size_t)R * d * sizeof(float);
+#define KVC_A(DD) hipLaunchKernelGGL((win_f32_accum<DD>), ga, dim3(NTA), lds, s, qt, kt, g, sl2, \
+                                     (const float*)cfin, per_query_head, A)
+      switch (d) {
+        case 16: KVC_A(16); break;
+        case 32: KVC_A(32); break;
+        case 64: KVC_A(64); break;
+        case 128: KVC_A(128); break;
+        default: KVC_A(0); break;
+      }
+#undef KVC_A
     }
   }
   return launch_status("kvc_score_window_attn");
