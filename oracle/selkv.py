@@ -23,6 +23,10 @@ Readings taken where the page is silent or ambiguous (listed in the design doc):
     weight A_t.
   * The compensation ratio is gated: R_t = (A_t + sum g_e A_e) / A_t, one per
     KV head, shared by the group's query heads.
+  * RoPE re-positioning (step 6, off for long contexts on the page) turns each
+    kept key from its original position to its slot's position, with the
+    half-split pairing (element i with element i + d/2) and a caller-given
+    base; the page names neither.
 """
 from __future__ import annotations
 
@@ -152,3 +156,27 @@ def compensated_decode(q: np.ndarray, K_c: np.ndarray, Vp: np.ndarray,
     """Decode over the compacted cache with the alpha * ln R logit bias
     ([SelKV] section 2, attention compensation).  Returns (o', lse)."""
     return decode_attention(q, K_c, Vp, lnR, alpha_bias, scale)
+
+
+def rope_apply(x: np.ndarray, pos: np.ndarray, base: float) -> np.ndarray:
+    """Rotary position embedding of rows x [..., n, d] at positions pos [..., n]
+    (the half-split pairing: element i turns with element i + d/2 by the angle
+    pos * base^(-2i/d)).  float64."""
+    x = np.asarray(x, dtype=np.float64)
+    d = x.shape[-1]
+    h = d // 2
+    inv = base ** (-2.0 * np.arange(h) / d)
+    ang = np.asarray(pos, dtype=np.float64)[..., None] * inv
+    c, s = np.cos(ang), np.sin(ang)
+    a, b = x[..., :h], x[..., h:]
+    return np.concatenate([a * c - b * s, a * s + b * c], axis=-1)
+
+
+def rope_reposition(K_c: np.ndarray, pos_old: np.ndarray, new_pos0: int, base: float) -> np.ndarray:
+    """[SelKV] section 2, pipeline step 6 (RoPE re-positioning): the kept keys,
+    embedded at their original positions pos_old [Hkv, m], are re-embedded at
+    the contiguous positions new_pos0, new_pos0 + 1, ...: each row turns by
+    (new - old) times the pair's frequency.  float64 [Hkv, m, d]."""
+    m = np.asarray(pos_old).shape[-1]
+    delta = (new_pos0 + np.arange(m))[None, :] - np.asarray(pos_old, dtype=np.int64)
+    return rope_apply(K_c, delta, base)
