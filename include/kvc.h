@@ -264,6 +264,23 @@ int kvc_merge_gated(const void* const* K, const void* const* V, int dtype,
                     void* stream);
 
 /*
+ * RoPE re-positioning of the kept keys ([SelKV] section 2, pipeline overview,
+ * step 6; the page turns it off for long contexts): key row j of each head,
+ * carrying the rotary embedding of position pos_old[l][g, j], is re-embedded at
+ * position new_pos0 + j, in place.  Element i pairs with element i + d/2 and
+ * turns by (new_pos0 + j - pos_old[l][g, j]) * base^(-2i/d) radians (the page
+ * gives neither the pairing nor the base).  The angle is reduced in float64;
+ * bf16 results are rounded to nearest even.
+ *   K          host array of L device pointers, each [Hkv, m, d] of dtype.
+ *   pos_old    host array of L device pointers, each int32 [Hkv, m] (for a
+ *              compacted cache: the kept indices).
+ *   d even; base > 1; 0 <= new_pos0 < 2^31.
+ */
+int kvc_rope_reposition(void* const* K, int dtype, const int32_t* const* pos_old,
+                        int64_t new_pos0, double base, int L, int Hkv, int64_t m, int d,
+                        void* stream);
+
+/*
  * Decode attention of one query per head over a (compacted) cache, with the
  * optional compensation bias ([SelKV] section 2, attention compensation; used
  * with [RECAS] section 2.B's bound as a check):

@@ -50,6 +50,7 @@ _SIGNATURES = {
                           _i32),
     "kvc_decode_attn_active": ([_vp, _vp, _vp, _i32, _vp, _f32, _vp, _i64, _i32, _i32, _i32, _i64,
                                 _i32, _f32, _vp, _vp, _vp, _sz, _vp], _i32),
+    "kvc_rope_reposition": ([_vp, _i32, _vp, _i64, _f64, _i32, _i32, _i64, _i32, _vp], _i32),
     "kvc_decode_attn_workspace_size": ([_i32, _i32, _i64, _i32], _sz),
     "kvc_decode_attn": ([_vp, _vp, _vp, _i32, _vp, _f32, _i32, _i32, _i32, _i64, _i32, _f32, _vp,
                          _vp, _vp, _sz, _vp], _i32),
@@ -381,3 +382,17 @@ def kvc_decode_attn_active(q, K, V, logR, alpha_bias: float, active, scale: floa
         _ptr(lse_out, torch.float32) if lse_out is not None else None,
         _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
     return o_out, lse_out
+
+
+def kvc_rope_reposition(K, pos_old, new_pos0: int, base: float, stream=None):
+    """In place: row j of K[l][g] re-embedded from position pos_old[l][g, j] to new_pos0 + j."""
+    L = len(K)
+    Hkv, m, d = K[0].shape
+    for p in pos_old:
+        if tuple(p.shape) != (Hkv, m):
+            raise ValueError("pos_old[l] must be [Hkv, m]")
+    kp, a1 = _ptrs(K, K[0].dtype)
+    pp, a2 = _ptrs(pos_old, torch.int32)
+    _check("kvc_rope_reposition", lib().kvc_rope_reposition(
+        kp, _dtype(K[0]), pp, new_pos0, base, L, Hkv, m, d, _stream(stream)))
+    return K
