@@ -453,6 +453,24 @@ def main():
                                                   ("active_scores", "active_select", "decode_active")), 4)}
         dec["timed"] = "separately, after the steps; not in ms_per_step"
         out["decode_check"] = dec
+        # SelKV pipeline step 6 (off for long contexts on the page): the compacted
+        # keys re-embedded at contiguous positions, in place, timed on its own
+        from kv_cache_compression_softmax_amd import binding as B
+        r0 = torch.cuda.Event(enable_timing=True)
+        r1 = torch.cuda.Event(enable_timing=True)
+        B.kvc_rope_reposition(plan.Kc, plan.idx, 0, 500000.0)
+        r0.record(stream)
+        for _ in range(args.steps):
+            B.kvc_rope_reposition(plan.Kc, plan.idx, 0, 500000.0)
+        r1.record(stream)
+        torch.cuda.synchronize()
+        t = r0.elapsed_time(r1) / args.steps
+        rb = 2 * L * Hkv * m * d * e + L * Hkv * m * 4
+        out["rope_reposition"] = {"ms": round(t, 4), "alg_bytes": rb,
+                                  "GBps": round(rb / (t * 1e-3) / 1e9, 1),
+                                  "frac_hbm": round(rb / (t * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                                  "base": 500000.0,
+                                  "timed": "separately, after the decode check; not in ms_per_step"}
     if period:
         out["decode_period"] = {"period": period, "slots_per_step": n_step,
                                 "note": "value counts the slots re-scored and compacted per period "

@@ -9,8 +9,8 @@
 // so it is formed and reduced to [-pi, pi] in float64; the rotation itself runs
 // in float32 and bf16 results are rounded to nearest even.
 //
-// One thread per (row, pair): a wave covers the pairs of one row (d = 128), so
-// a row's two halves are each read and written as one contiguous segment.
+// A wave takes one row at a time (lane i: pairs i, i + 64, ...), so a row's two
+// halves are each read and written as one contiguous segment.
 #include "common.h"
 
 namespace kvc {
@@ -26,29 +26,64 @@ template <> __device__ __forceinline__ float ld_el<float>(const float* p) { retu
 __device__ __forceinline__ void st_el(uint16_t* p, float v) { *p = f32_to_bf16_rne(v); }
 __device__ __forceinline__ void st_el(float* p, float v) { *p = v; }
 
+constexpr int FR = 4;          // pair frequencies per lane kept in registers (d <= 512)
+constexpr int RPB = 8;         // blocks per (layer, KV head)
+constexpr int RW = 8;          // rows per wave step when d <= 128
+
+// One wave per row at a time, looping over the rows of its (layer, KV head); lane
+// i turns pairs i, i + 64, ...  The shift new - old is the same for the whole row
+// (wave-uniform), and each lane's frequencies are computed once per launch.
 template <typename T>
 __global__ void __launch_bounds__(NT)
-rope_kernel(RopeTables t, int lc, int Hkv, int64_t m, int d, int64_t new0, double log2_base) {
+rope_kernel(RopeTables t, int Hkv, int64_t m, int d, int64_t new0, double log2_base) {
+  const int lg = blockIdx.y;                    // (layer, KV head)
+  const int l = lg / Hkv, g = lg % Hkv;
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int h = d / 2;
-  const int64_t id = (int64_t)blockIdx.x * NT + threadIdx.x;
-  const int64_t rows = (int64_t)lc * Hkv * m;
-  if (id >= rows * h) return;
-  const int i = (int)(id % h);
-  const int64_t row = id / h;                   // (layer, KV head, slot)
-  const int64_t j = row % m;
-  const int64_t lg = row / m;
-  const int l = (int)(lg / Hkv), g = (int)(lg % Hkv);
   const int32_t* pos = (const int32_t*)t.pos.p[l] + (int64_t)g * m;
-  T* k = (T*)t.K.p[l] + ((int64_t)g * m + j) * d;
-  const double freq = exp2(-2.0 * (double)i / (double)d * log2_base);
-  const double ang = (double)(new0 + j - (int64_t)pos[j]) * freq;
+  T* kg = (T*)t.K.p[l] + (int64_t)g * m * d;
+  const double inv_two_pi = 0.15915494309189533576888376337251;
   const double two_pi = 6.283185307179586476925286766559;
-  const float r = (float)(ang - two_pi * rint(ang / two_pi));
-  float sn, cs;
-  sincosf(r, &sn, &cs);
-  const float a = ld_el<T>(k + i), b = ld_el<T>(k + i + h);
-  st_el(k + i, a * cs - b * sn);
-  st_el(k + i + h, a * sn + b * cs);
+  double fr[FR];
+#pragma unroll
+  for (int c = 0; c < FR; ++c) fr[c] = exp2(-2.0 * (double)(lane + 64 * c) / (double)d * log2_base);
+  auto turn = [&](int64_t delta, int i, int c, float a, float b, T* k) __attribute__((always_inline)) {
+    const double f = c < FR ? fr[c < FR ? c : 0] : exp2(-2.0 * (double)i / (double)d * log2_base);
+    const double ang = (double)delta * f;
+    const float r = (float)fma(-two_pi, rint(ang * inv_two_pi), ang);
+    float sn, cs;
+    sincosf(r, &sn, &cs);
+    st_el(k + i, a * cs - b * sn);
+    st_el(k + i + h, a * sn + b * cs);
+  };
+  const int64_t nw = (int64_t)gridDim.x * (NT / 64);
+  int64_t j = (int64_t)blockIdx.x * (NT / 64) + wv;
+  if (h <= 64) {
+    // RW rows per step, all their loads issued before any is used
+    for (; j < m; j += RW * nw) {
+      float a[RW], b[RW];
+      int64_t dl[RW];
+#pragma unroll
+      for (int u = 0; u < RW; ++u) {
+        const int64_t ju = min(j + u * nw, m - 1);          // clamped: loaded, not stored
+        dl[u] = new0 + ju - (int64_t)pos[ju];
+        const T* k = kg + ju * d;
+        const int i = lane < h ? lane : 0;
+        a[u] = ld_el<T>(k + i);
+        b[u] = ld_el<T>(k + i + h);
+      }
+#pragma unroll
+      for (int u = 0; u < RW; ++u)
+        if (j + u * nw < m && lane < h) turn(dl[u], lane, 0, a[u], b[u], kg + (j + u * nw) * d);
+    }
+  } else {
+    for (; j < m; j += nw) {
+      const int64_t delta = new0 + j - (int64_t)pos[j];
+      T* k = kg + j * d;
+      for (int i = lane, c = 0; i < h; i += 64, ++c) turn(delta, i, c, ld_el<T>(k + i), ld_el<T>(k + i + h), k);
+    }
+  }
 }
 
 }  // namespace
@@ -75,11 +110,10 @@ extern "C" int kvc_rope_reposition(void* const* K, int dtype, const int32_t* con
     const int lc = min(kLayersPerLaunch, L - l0);
     RopeTables t{};
     for (int i = 0; i < lc; ++i) { t.K.p[i] = K[l0 + i]; t.pos.p[i] = pos_old[l0 + i]; }
-    const int64_t total = (int64_t)lc * Hkv * m * (d / 2);
-    KVC_REQUIRE((total + NT - 1) / NT <= 0x7fffffffLL, "kvc_rope_reposition: too many rows");
-    const dim3 grid((unsigned)((total + NT - 1) / NT));
-    if (dtype == KVC_BF16) hipLaunchKernelGGL(rope_kernel<uint16_t>, grid, dim3(NT), 0, s, t, lc, Hkv, m, d, new_pos0, lb);
-    else hipLaunchKernelGGL(rope_kernel<float>, grid, dim3(NT), 0, s, t, lc, Hkv, m, d, new_pos0, lb);
+    KVC_REQUIRE((int64_t)lc * Hkv <= 65535, "kvc_rope_reposition: L * Hkv > 65535");
+    const dim3 grid((unsigned)RPB, (unsigned)(lc * Hkv));
+    if (dtype == KVC_BF16) hipLaunchKernelGGL(rope_kernel<uint16_t>, grid, dim3(NT), 0, s, t, Hkv, m, d, new_pos0, lb);
+    else hipLaunchKernelGGL(rope_kernel<float>, grid, dim3(NT), 0, s, t, Hkv, m, d, new_pos0, lb);
   }
   return launch_status("kvc_rope_reposition");
 }
