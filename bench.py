@@ -71,7 +71,7 @@ KERNEL_SOURCES = {
     "vatp_union": ["selkv.hip"], "merge_gated": ["selkv.hip"],
     "decode_compacted": ["decode_attn.hip"], "decode_full": ["decode_attn.hip"],
     "active_scores": ["decode_attn.hip"], "active_select": ["select_topk.hip"],
-    "decode_active": ["decode_attn.hip"],
+    "decode_active": ["decode_attn.hip"], "rope_reposition": ["rope.hip"],
 }
 
 
@@ -470,6 +470,7 @@ def main():
                                   "GBps": round(rb / (t * 1e-3) / 1e9, 1),
                                   "frac_hbm": round(rb / (t * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
                                   "base": 500000.0,
+                                  "traffic": measured_traffic(w.name, "rope_reposition"),
                                   "timed": "separately, after the decode check; not in ms_per_step"}
     if period:
         out["decode_period"] = {"period": period, "slots_per_step": n_step,
