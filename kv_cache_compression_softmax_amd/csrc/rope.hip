@@ -26,13 +26,12 @@ template <> __device__ __forceinline__ float ld_el<float>(const float* p) { retu
 __device__ __forceinline__ void st_el(uint16_t* p, float v) { *p = f32_to_bf16_rne(v); }
 __device__ __forceinline__ void st_el(float* p, float v) { *p = v; }
 
-constexpr int FR = 4;          // pair frequencies per lane kept in registers (d <= 512)
 constexpr int RPB = 8;         // blocks per (layer, KV head)
 constexpr int RW = 8;          // rows per wave step when d <= 128
 
 // One wave per row at a time, looping over the rows of its (layer, KV head); lane
 // i turns pairs i, i + 64, ...  The shift new - old is the same for the whole row
-// (wave-uniform), and each lane's frequencies are computed once per launch.
+// (wave-uniform); for d <= 128 each lane's one frequency is computed once.
 template <typename T>
 __global__ void __launch_bounds__(NT)
 rope_kernel(RopeTables t, int Hkv, int64_t m, int d, int64_t new0, double log2_base) {
@@ -45,11 +44,11 @@ rope_kernel(RopeTables t, int Hkv, int64_t m, int d, int64_t new0, double log2_b
   T* kg = (T*)t.K.p[l] + (int64_t)g * m * d;
   const double inv_two_pi = 0.15915494309189533576888376337251;
   const double two_pi = 6.283185307179586476925286766559;
-  double fr[FR];
-#pragma unroll
-  for (int c = 0; c < FR; ++c) fr[c] = exp2(-2.0 * (double)(lane + 64 * c) / (double)d * log2_base);
-  auto turn = [&](int64_t delta, int i, int c, float a, float b, T* k) __attribute__((always_inline)) {
-    const double f = c < FR ? fr[c < FR ? c : 0] : exp2(-2.0 * (double)i / (double)d * log2_base);
+  // frequency of pair i: base^(-2i/d)
+  auto freq = [&](int i) __attribute__((always_inline)) {
+    return exp2(-2.0 * (double)i / (double)d * log2_base);
+  };
+  auto turn = [&](int64_t delta, int i, double f, float a, float b, T* k) __attribute__((always_inline)) {
     const double ang = (double)delta * f;
     const float r = (float)fma(-two_pi, rint(ang * inv_two_pi), ang);
     float sn, cs;
@@ -60,7 +59,9 @@ rope_kernel(RopeTables t, int Hkv, int64_t m, int d, int64_t new0, double log2_b
   const int64_t nw = (int64_t)gridDim.x * (NT / 64);
   int64_t j = (int64_t)blockIdx.x * (NT / 64) + wv;
   if (h <= 64) {
-    // RW rows per step, all their loads issued before any is used
+    // lane i owns pair i of every row; RW rows per step, all their loads issued
+    // before any is used
+    const double f = freq(lane < h ? lane : 0);
     for (; j < m; j += RW * nw) {
       float a[RW], b[RW];
       int64_t dl[RW];
@@ -75,13 +76,13 @@ rope_kernel(RopeTables t, int Hkv, int64_t m, int d, int64_t new0, double log2_b
       }
 #pragma unroll
       for (int u = 0; u < RW; ++u)
-        if (j + u * nw < m && lane < h) turn(dl[u], lane, 0, a[u], b[u], kg + (j + u * nw) * d);
+        if (j + u * nw < m && lane < h) turn(dl[u], lane, f, a[u], b[u], kg + (j + u * nw) * d);
     }
   } else {
     for (; j < m; j += nw) {
       const int64_t delta = new0 + j - (int64_t)pos[j];
       T* k = kg + j * d;
-      for (int i = lane, c = 0; i < h; i += 64, ++c) turn(delta, i, c, ld_el<T>(k + i), ld_el<T>(k + i + h), k);
+      for (int i = lane; i < h; i += 64) turn(delta, i, freq(i), ld_el<T>(k + i), ld_el<T>(k + i + h), k);
     }
   }
 }
