@@ -9,8 +9,11 @@
 // so it is formed and reduced to [-pi, pi] in float64; the rotation itself runs
 // in float32 and bf16 results are rounded to nearest even.
 //
-// A wave takes one row at a time (lane i: pairs i, i + 64, ...), so a row's two
-// halves are each read and written as one contiguous segment.
+// For d = 4 .. 128 (a power of two) a lane turns two neighbouring pairs with
+// one 2-element load per half, and a wave covers 128/(d/2) rows per step, eight
+// steps' loads in flight; other shapes take one row per wave, one pair per lane
+// at a time.  Either way a row's halves are read and written as contiguous
+// segments.
 #include "common.h"
 
 namespace kvc {
@@ -19,6 +22,16 @@ namespace {
 constexpr int NT = 256;
 
 struct RopeTables { MutPtrs K; ConstPtrs pos; };
+
+// two consecutive elements, loaded as one
+template <typename T> struct P2T;
+template <> struct P2T<uint16_t> { using type = uint32_t; };
+template <> struct P2T<float> { using type = float2; };
+template <typename T> using P2 = typename P2T<T>::type;
+__device__ __forceinline__ float p2_lo(uint32_t v) { return bf16_lo(v); }
+__device__ __forceinline__ float p2_hi(uint32_t v) { return bf16_hi(v); }
+__device__ __forceinline__ float p2_lo(float2 v) { return v.x; }
+__device__ __forceinline__ float p2_hi(float2 v) { return v.y; }
 
 template <typename T> __device__ __forceinline__ float ld_el(const T* p);
 template <> __device__ __forceinline__ float ld_el<uint16_t>(const uint16_t* p) { return bf16_to_f32(*p); }
@@ -34,7 +47,7 @@ constexpr int RW = 8;          // rows per wave step when d <= 128
 // (wave-uniform); for d <= 128 each lane's one frequency is computed once.
 template <typename T>
 __global__ void __launch_bounds__(NT)
-rope_kernel(RopeTables t, int Hkv, int64_t m, int d, int64_t new0, double log2_base) {
+rope_kernel(RopeTables t, int Hkv, int64_t m, int d, int64_t new0, double log2_base, int paired) {
   const int lg = blockIdx.y;                    // (layer, KV head)
   const int l = lg / Hkv, g = lg % Hkv;
   const int lane = threadIdx.x & 63;
@@ -58,25 +71,35 @@ rope_kernel(RopeTables t, int Hkv, int64_t m, int d, int64_t new0, double log2_b
   };
   const int64_t nw = (int64_t)gridDim.x * (NT / 64);
   int64_t j = (int64_t)blockIdx.x * (NT / 64) + wv;
-  if (h <= 64) {
-    // lane i owns pair i of every row; RW rows per step, all their loads issued
-    // before any is used
-    const double f = freq(lane < h ? lane : 0);
-    for (; j < m; j += RW * nw) {
-      float a[RW], b[RW];
+  if (paired) {                                 // h a power of two <= 64, rows 8-byte aligned
+    // two pairs per lane (elements 2q, 2q + 1 of each half, one 2-element load
+    // per half), 128 / h rows per wave step; RW steps' loads issued before any
+    // is used
+    const int lpr = h / 2;                       // lanes per row
+    const int rpw = 64 / lpr;                    // rows per wave step
+    const int sub = lane / lpr, q = 2 * (lane % lpr);
+    const double f0 = freq(q), f1 = freq(q + 1);
+    const int64_t stride = nw * rpw;             // rows between a wave's steps
+    for (j = ((int64_t)blockIdx.x * (NT / 64) + wv) * rpw + sub; j < m; j += RW * stride) {
+      P2<T> a[RW], b[RW];
       int64_t dl[RW];
 #pragma unroll
       for (int u = 0; u < RW; ++u) {
-        const int64_t ju = min(j + u * nw, m - 1);          // clamped: loaded, not stored
+        const int64_t ju = min(j + u * stride, m - 1);      // clamped: loaded, not stored
         dl[u] = new0 + ju - (int64_t)pos[ju];
         const T* k = kg + ju * d;
-        const int i = lane < h ? lane : 0;
-        a[u] = ld_el<T>(k + i);
-        b[u] = ld_el<T>(k + i + h);
+        a[u] = *reinterpret_cast<const P2<T>*>(k + q);
+        b[u] = *reinterpret_cast<const P2<T>*>(k + q + h);
       }
 #pragma unroll
-      for (int u = 0; u < RW; ++u)
-        if (j + u * nw < m && lane < h) turn(dl[u], lane, f, a[u], b[u], kg + (j + u * nw) * d);
+      for (int u = 0; u < RW; ++u) {
+        const int64_t ju = j + u * stride;
+        if (ju < m) {
+          T* k = kg + ju * d;
+          turn(dl[u], q, f0, p2_lo(a[u]), p2_lo(b[u]), k);
+          turn(dl[u], q + 1, f1, p2_hi(a[u]), p2_hi(b[u]), k);
+        }
+      }
     }
   } else {
     for (; j < m; j += nw) {
@@ -107,14 +130,19 @@ extern "C" int kvc_rope_reposition(void* const* K, int dtype, const int32_t* con
     KVC_REQUIRE(K[l] && pos_old[l], "kvc_rope_reposition: null pointer in layer %d", l);
   hipStream_t s = as_stream(stream);
   const double lb = log2(base);
+  // two pairs per lane with 2-element loads: h = d/2 a power of two up to 64 (so
+  // the lanes of a row divide the wave), every row 8-byte aligned
+  const int h = d / 2;
+  int paired = h >= 2 && h <= 64 && (h & (h - 1)) == 0;
+  for (int l = 0; l < L; ++l) paired = paired && (uintptr_t)K[l] % 8 == 0;
   for (int l0 = 0; l0 < L; l0 += kLayersPerLaunch) {
     const int lc = min(kLayersPerLaunch, L - l0);
     RopeTables t{};
     for (int i = 0; i < lc; ++i) { t.K.p[i] = K[l0 + i]; t.pos.p[i] = pos_old[l0 + i]; }
     KVC_REQUIRE((int64_t)lc * Hkv <= 65535, "kvc_rope_reposition: L * Hkv > 65535");
     const dim3 grid((unsigned)RPB, (unsigned)(lc * Hkv));
-    if (dtype == KVC_BF16) hipLaunchKernelGGL(rope_kernel<uint16_t>, grid, dim3(NT), 0, s, t, Hkv, m, d, new_pos0, lb);
-    else hipLaunchKernelGGL(rope_kernel<float>, grid, dim3(NT), 0, s, t, Hkv, m, d, new_pos0, lb);
+    if (dtype == KVC_BF16) hipLaunchKernelGGL(rope_kernel<uint16_t>, grid, dim3(NT), 0, s, t, Hkv, m, d, new_pos0, lb, paired);
+    else hipLaunchKernelGGL(rope_kernel<float>, grid, dim3(NT), 0, s, t, Hkv, m, d, new_pos0, lb, paired);
   }
   return launch_status("kvc_rope_reposition");
 }

@@ -24,7 +24,8 @@ def dev():
 @pytest.mark.parametrize("Hkv,m,d,dtype,base,new0", [
     (8, 3000, 128, torch.bfloat16, 500000.0, 0), (2, 700, 64, torch.bfloat16, 10000.0, 17),
     (4, 129, 2, torch.float32, 10000.0, 3), (3, 1000, 128, torch.float32, 1e6, 0),
-    (1, 1, 128, torch.bfloat16, 10000.0, 0)], ids=str)
+    (1, 1, 128, torch.bfloat16, 10000.0, 0), (2, 333, 4, torch.bfloat16, 10000.0, 5),
+    (2, 200, 6, torch.float32, 10000.0, 0), (1, 50, 512, torch.bfloat16, 10000.0, 1)], ids=str)
 def test_rope_reposition(dev, Hkv, m, d, dtype, base, new0):
     from kv_cache_compression_softmax_amd import binding as B
     announce("rope", Hkv, m, d, dtype, base, new0)
