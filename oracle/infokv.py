@@ -13,7 +13,7 @@ and returns float64 unless stated otherwise.  Each step is the plain definition;
 library primitives (sort, partition, matmul) are used as steps, nothing is
 blocked, fused or reordered.
 
-Readings taken where the page is silent or garbled (listed again in the design doc):
+Readings taken where the page is silent or garbled:
   * A comes from layer l's own window queries and keys (the Technical-detail
     section speaks of each layer; the Method section's "last layer" is read as
     a garble).

@@ -9,7 +9,7 @@ section 2.C (dynamic sparse decoding attention: a query-aware sparse score over
 the retained cache, the top K_t entries form the active set, and only they take
 part in the step's attention).
 
-Readings taken where the page is silent (listed in the design doc):
+Readings taken where the page is silent:
   * The sparse score of a cached entry is the query-key compatibility, scaled
     by 1/sqrt(d), plus a utility term.  The page fuses three utility signals
     without fixing their inputs, so the utility row is an input (zero by

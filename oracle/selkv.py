@@ -7,7 +7,7 @@ Merge-or-Drop and Attention Compensation", gist.science paper 2607.16213;
 section 2 (방법론 / Method): "Soft cosine gate", "Attention compensation" and
 the six-step "Pipeline overview".
 
-Readings taken where the page is silent or ambiguous (listed in the design doc):
+Readings taken where the page is silent or ambiguous:
   * The importance score is VATP: window-averaged attention of a query head
     times the l2 norm of the token's value vector.
   * GQA union: U[g, j] = max over the group's query heads of VATP[h, j]; keep
