@@ -98,6 +98,32 @@ def test_validation_before_launch(lib):
     assert lib.kvc_decode_attn(pa, pa, pa, 1, None, ctypes.c_float(0), 1, 16, 1, 64, 128, ctypes.c_float(0.1), fake, None, fake, 1 << 20, None) == -1
 
 
+def test_validation_before_launch_decode_side(lib):
+    fake = ctypes.c_void_p(0x1000)     # never dereferenced: every call below fails validation
+    arr = (ctypes.c_void_p * 1)(0x1000)
+    pa = ctypes.cast(arr, ctypes.c_void_p)
+    kk = (ctypes.c_int64 * 1)(8)
+    # compact into a head stride: out_rows below k_keep, or below 1
+    assert lib.kvc_compact_into(pa, None, 1, 1, 2, 64, 128, pa, kk, 7, pa, None, None) == -1
+    assert "out_rows" in err(lib)
+    assert lib.kvc_compact_into(pa, None, 1, 1, 2, 64, 128, pa, kk, 0, pa, None, None) == -1
+    # slot fusion: alpha outside [0, 1]; workspace missing
+    assert lib.kvc_fuse_scores_slots(fake, fake, 1, 2, 64, 1.5, fake, None, fake, 1 << 20, None) == -1
+    assert lib.kvc_fuse_scores_slots(fake, fake, 1, 2, 64, 0.9, fake, None, None, 0, None) == -3
+    # entropy-score append past the slot capacity
+    assert lib.kvc_append_entropy_scores(fake, fake, 1, 2, 100, fake, 150, 51, None) == -1
+    # active scores: Hq not a multiple of Hkv
+    assert lib.kvc_active_scores(pa, pa, 1, None, 0.0, 1, 6, 4, 64, 128, 0.1, fake, None) == -1
+    # active decode: no list, or more positions than rows
+    assert lib.kvc_decode_attn_active(pa, pa, pa, 1, None, 0.0, None, 8, 1, 8, 2, 64, 128, 0.1,
+                                      fake, None, fake, 1 << 20, None) == -1
+    assert lib.kvc_decode_attn_active(pa, pa, pa, 1, None, 0.0, pa, 65, 1, 8, 2, 64, 128, 0.1,
+                                      fake, None, fake, 1 << 20, None) == -1
+    # RoPE re-positioning: odd d, base <= 1
+    assert lib.kvc_rope_reposition(pa, 1, pa, 0, 10000.0, 1, 2, 64, 127, None) == -1
+    assert lib.kvc_rope_reposition(pa, 1, pa, 0, 1.0, 1, 2, 64, 128, None) == -1
+
+
 def test_uniform_budget_matches_oracle():
     from kv_cache_compression_softmax_amd import binding
     from oracle import infokv
