@@ -42,7 +42,6 @@ constexpr int NT = 256;
 constexpr int CK = 1024;          // keys per workgroup (decode_partial)
 constexpr int kWaveTarget = 1024;  // decode_mfma waves per launch: MI355X's 256 CUs x 4 SIMDs
 constexpr int kSets = 2;           // decode_mfma register sets (tiles) per wave
-constexpr int kActiveWaves = 2048; // waves of decode_mfma over an active row list
 constexpr int kScoreWaves = 2048;  // waves of active_scores_mfma
 constexpr int kScoreSets = 2;      // active_scores_mfma register sets (tiles) per wave
 constexpr int MAXG = 8;           // query heads per KV head
@@ -188,27 +187,42 @@ struct DecTile {
   float lr;
 };
 
-// jb, jlast are positions; with IDX the cache row of position p is ix[p]
-template <int D, bool BIAS, bool IDX>
-__device__ __forceinline__ void dec_load(DecTile<D>& t, const uint16_t* K, const uint16_t* V,
-                                         const float* lr, const int32_t* ix, int64_t jb,
-                                         int64_t jlast, int lane) {
+// The cache rows one tile reads: lane l's K row (key l % 16) and its V rows.
+// jb, jlast are positions; with IDX the row of position p is ix[p] (loaded),
+// otherwise p itself.
+template <int D>
+struct DecRows {
+  int32_t k;
+  int32_t v[DecTile<D>::VI];
+};
+
+template <int D, bool IDX>
+__device__ __forceinline__ void dec_rows(DecRows<D>& r, const int32_t* ix, int64_t jb, int64_t jlast,
+                                         int lane) {
   constexpr int VL = DecTile<D>::VL, KPI = 64 / VL;
   const int64_t kp = min(jb + (lane & 15), jlast);
-  const int64_t kk = IDX ? (int64_t)ix[kp] : kp;
-  const uint16_t* kr = K + kk * D + 8 * (lane >> 4);
+  r.k = IDX ? ix[kp] : (int32_t)kp;
+#pragma unroll
+  for (int i = 0; i < DecTile<D>::VI; ++i) {
+    const int64_t vp = min(jb + i * KPI + lane / VL, jlast);
+    r.v[i] = IDX ? ix[vp] : (int32_t)vp;
+  }
+}
+
+template <int D, bool BIAS>
+__device__ __forceinline__ void dec_load(DecTile<D>& t, const uint16_t* K, const uint16_t* V,
+                                         const float* lr, const DecRows<D>& r, int lane) {
+  constexpr int VL = DecTile<D>::VL;
+  const uint16_t* kr = K + (int64_t)r.k * D + 8 * (lane >> 4);
 #pragma unroll
   for (int s = 0; s < DecTile<D>::KB; ++s) {
     const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kr + 32 * s));
     t.k[s] = __builtin_bit_cast(bf16x8, x);
   }
 #pragma unroll
-  for (int i = 0; i < DecTile<D>::VI; ++i) {
-    const int64_t vp = min(jb + i * KPI + lane / VL, jlast);
-    const int64_t kv = IDX ? (int64_t)ix[vp] : vp;
-    t.v[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(V + kv * D + 8 * (lane % VL)));
-  }
-  t.lr = BIAS ? lr[kk] : 0.f;
+  for (int i = 0; i < DecTile<D>::VI; ++i)
+    t.v[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(V + (int64_t)r.v[i] * D + 8 * (lane % VL)));
+  t.lr = BIAS ? lr[r.k] : 0.f;
 }
 
 // partial layout as decode_partial: [lc, Hq, nchunk] x (m, l, -, -, o[d]), m in natural
@@ -327,10 +341,17 @@ decode_mfma(DecTables t, int Hq, int Hkv, int G, int64_t len, float sl2, float b
   // tiles from a ring of kSets register sets, kSets - 1 tiles' loads always in
   // flight.  Loads past the chunk's last tile are clamped to it (a re-read of rows
   // just fetched); a tile past the end is fully masked and changes nothing.
+  // The rows of tile T + kSets are found (with IDX: their indices loaded) while
+  // tile T is computed, one step before that tile's K/V loads are issued: the
+  // wait for the indices then does not include the K/V loads in flight, which
+  // complete in order behind them.
   const int64_t jl = j0 + (int64_t)(ntile - 1) * 16;      // the last tile
   DecTile<D> ts[kSets];
+  DecRows<D> rs[kSets];
 #pragma unroll
-  for (int u = 0; u + 1 < kSets; ++u) dec_load<D, BIAS, IDX>(ts[u], K, V, lr, ix, min(j0 + 16 * u, jl), jlast, lane);
+  for (int u = 0; u < kSets; ++u) dec_rows<D, IDX>(rs[u], ix, min(j0 + 16 * u, jl), jlast, lane);
+#pragma unroll
+  for (int u = 0; u + 1 < kSets; ++u) dec_load<D, BIAS>(ts[u], K, V, lr, rs[u], lane);
   for (int ti = 0; ti < ntile; ti += kSets) {
     const int64_t jb = j0 + (int64_t)ti * 16;
 #pragma unroll
@@ -338,7 +359,8 @@ decode_mfma(DecTables t, int Hq, int Hkv, int G, int64_t len, float sl2, float b
       // the scheduling barrier keeps each refill below the last use of the set it
       // overwrites (otherwise the sets are renamed and copied, with a wait per copy)
       __builtin_amdgcn_sched_barrier(0);
-      dec_load<D, BIAS, IDX>(ts[(u + kSets - 1) % kSets], K, V, lr, ix, min(jb + 16 * (u + kSets - 1), jl), jlast, lane);
+      dec_rows<D, IDX>(rs[u], ix, min(jb + 16 * (u + kSets), jl), jlast, lane);
+      dec_load<D, BIAS>(ts[(u + kSets - 1) % kSets], K, V, lr, rs[(u + kSets - 1) % kSets], lane);
       asm volatile("" ::: "memory");
       tile(ts[u], jb + 16 * u);
     }
@@ -533,8 +555,7 @@ extern "C" size_t kvc_decode_attn_workspace_size(int L, int Hq, int64_t len, int
   // partials of one launch (at most kLayersPerLaunch layers), for either kernel and
   // any Hkv >= 1; the last launch of L layers may cover fewer layers
   auto launch_bytes = [&](int lc) {
-    const int64_t nchunk = max((len + CK - 1) / CK,
-                               mfma_chunks(lc, 1, len, max(kWaveTarget, kActiveWaves)));
+    const int64_t nchunk = max((len + CK - 1) / CK, mfma_chunks(lc, 1, len));
     return (size_t)lc * Hq * nchunk * (d + 4) * sizeof(float);
   };
   const int lc = L < kLayersPerLaunch ? L : kLayersPerLaunch;
@@ -586,7 +607,7 @@ int decode_impl(const char* fn, const void* const* q, const void* const* K, cons
     t.npos = npos;
     int nchunk = nchunk_g;
     if (mfma) {
-      const int64_t ckm = mfma_chunk_len(npos, mfma_chunks(lc, Hkv, npos, ix ? kActiveWaves : kWaveTarget));
+      const int64_t ckm = mfma_chunk_len(npos, mfma_chunks(lc, Hkv, npos));
       nchunk = (int)((npos + ckm - 1) / ckm);
       const int64_t nw = (int64_t)lc * Hkv * nchunk;
       const dim3 grid((unsigned)((nw + NT / 64 - 1) / (NT / 64)));
