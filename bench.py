@@ -139,6 +139,25 @@ def window_flops(w):
     return 2 * 2 * w.layers * w.heads_q * w.window * w.n * w.head_dim
 
 
+def host_cores():
+    """Threads the oracle's BLAS pool uses, and the host CPU's model name."""
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:
+        cores = 1
+    cpu = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return cores, cpu
+
+
 def cpu_baseline(w, inp, budget_s=15.0):
     """The oracle, as it stands, on a bounded sample of the same workload: whole
     chunks of the step are run until about `budget_s` seconds of CPU work are
@@ -148,11 +167,7 @@ def cpu_baseline(w, inp, budget_s=15.0):
     import torch
     from oracle import infokv, precision, selkv
 
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-    except Exception:
-        cores = 1
+    cores, cpu = host_cores()
 
     def f64(t):
         t = t.detach().cpu().contiguous()
@@ -223,7 +238,7 @@ def cpu_baseline(w, inp, budget_s=15.0):
         sample = (f"oracle run for {time.perf_counter() - t_start:.1f} s: the SelKV layer "
                   f"(attention, union, select, route, gate, merge) on all {n} tokens of {layers} "
                   f"of {L} layers, scaled by layers to the whole step")
-    return {"value": n / total, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+    return {"value": n / total, "unit": "tokens/s", "cores": cores, "cpu": cpu, "kind": "oracle",
             "sample": sample, "sample_s": round(time.perf_counter() - t_start, 2),
             "est_step_s": total}
 
@@ -236,11 +251,7 @@ def cpu_baseline_period(w, plan, new, period, budget_s=15.0):
     import torch
     from oracle import infokv, precision
 
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-    except Exception:
-        cores = 1
+    cores, cpu = host_cores()
 
     def f64(t):
         t = t.detach().cpu().contiguous()
@@ -285,7 +296,7 @@ def cpu_baseline_period(w, plan, new, period, budget_s=15.0):
               f"representation distance on {rows} of {period} new token rows, re-compression of "
               f"{layers} of {L} layers (all KV heads); each part scaled by rows or layers to the "
               f"whole period")
-    return {"value": plan.cap / total, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+    return {"value": plan.cap / total, "unit": "tokens/s", "cores": cores, "cpu": cpu, "kind": "oracle",
             "sample": sample, "sample_s": round(time.perf_counter() - t_start, 2),
             "est_step_s": total}
 
