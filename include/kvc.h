@@ -197,7 +197,9 @@ int kvc_select_topk(const float* S, int L, int Hkv, int64_t n, const int64_t* k_
  * Bit-exact copy.
  *   K, V       host arrays of L device pointers, each [Hkv, n, d] of dtype.
  *   idx        host array of L device pointers, each int32 [Hkv, k_keep[l]],
- *              every entry in [0, n) (not checked on the device).
+ *              every entry in [0, n).  An entry outside it is clamped to n - 1
+ *              on the device: a wrong row is copied, nothing is read out of
+ *              bounds, and no error is reported.
  *   k_keep     host int64 [L].
  *   K_out, V_out  host arrays of L device pointers, each [Hkv, k_keep[l], d].
  *   V and V_out may both be NULL (keys only).
@@ -325,7 +327,9 @@ int kvc_active_scores(const void* const* q, const void* const* K, int dtype,
  * active[l][g, 0 .. k_active) of each KV head's cache (any order; a row listed
  * twice counts twice).  With every row listed it is kvc_decode_attn.
  *   active     host array of L device pointers, each int32 [Hkv, k_active],
- *              every entry in [0, len) (not checked on the device).
+ *              every entry in [0, len).  An entry outside it is clamped to
+ *              len - 1 on the device: a wrong row takes part, nothing is read
+ *              out of bounds, and no error is reported.
  *   1 <= k_active <= len; other arguments, the workspace size
  *   (kvc_decode_attn_workspace_size(L, Hq, len, d)) and errors as kvc_decode_attn.
  */

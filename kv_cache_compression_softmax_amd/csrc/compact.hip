@@ -25,6 +25,12 @@ struct Tables {
   I64s blk0;                    // first block of each layer
 };
 
+// A kept index outside [0, n) is clamped to n - 1: a bad list gives wrong rows,
+// never a read outside the head's rows.
+__device__ __forceinline__ int64_t row_in(int32_t i, int64_t n) {
+  return min((int64_t)(uint32_t)i, n - 1);
+}
+
 // MODE: 0 any row size (2-byte words), 1 rows of 16-byte multiples, 2 four-byte rows
 template <int MODE>
 __global__ void __launch_bounds__(NT)
@@ -48,7 +54,7 @@ compact_kernel(Tables t, int lc, int Hkv, int64_t n, int rowbytes) {
     const int r = threadIdx.x / lpr, c = threadIdx.x % lpr;
     if (r >= rpi) return;
     for (int64_t j = j0 + r; j < min(k, j0 + ROWS); j += rpi) {
-      const int64_t src = idx[j];
+      const int64_t src = row_in(idx[j], n);
       const uint4 kv = *reinterpret_cast<const uint4*>(K + src * rowbytes + c * 16);
       uint4 vv;
       if (V) vv = *reinterpret_cast<const uint4*>(V + src * rowbytes + c * 16);
@@ -59,14 +65,14 @@ compact_kernel(Tables t, int lc, int Hkv, int64_t n, int rowbytes) {
     // one 4-byte row per thread (per-slot float32 scores)
     const int64_t j = j0 + threadIdx.x;
     if (threadIdx.x < ROWS && j < k) {
-      const int64_t src = idx[j];
+      const int64_t src = row_in(idx[j], n);
       *reinterpret_cast<uint32_t*>(Ko + j * 4) = *reinterpret_cast<const uint32_t*>(K + src * 4);
       if (V) *reinterpret_cast<uint32_t*>(Vo + j * 4) = *reinterpret_cast<const uint32_t*>(V + src * 4);
     }
   } else {
     const int half = rowbytes / 2;                 // 2-byte words per row
     for (int64_t j = j0; j < min(k, j0 + ROWS); ++j) {
-      const int64_t src = idx[j];
+      const int64_t src = row_in(idx[j], n);
       for (int c = threadIdx.x; c < half; c += NT) {
         ((uint16_t*)(Ko + j * rowbytes))[c] = ((const uint16_t*)(K + src * rowbytes))[c];
         if (V) ((uint16_t*)(Vo + j * rowbytes))[c] = ((const uint16_t*)(V + src * rowbytes))[c];

@@ -111,7 +111,7 @@ decode_partial(DecTables t, int Hq, int Hkv, int64_t len, int d, float scale, fl
   }
   const int64_t j0 = (int64_t)ch * CK, j1 = min(t.npos, j0 + CK);
   for (int64_t jp = j0 + grp; jp < j1; jp += NG) {
-    const int64_t j = ix ? (int64_t)ix[jp] : jp;
+    const int64_t j = ix ? min((int64_t)(uint32_t)ix[jp], len - 1) : jp;   // listed rows clamped into [0, len)
     float kx[W], vx[W];
     DE<T>::unpack(*reinterpret_cast<const uint4*>(K + j * d + c * W), kx);
     DE<T>::unpack(*reinterpret_cast<const uint4*>(V + j * d + c * W), vx);
@@ -209,11 +209,14 @@ __device__ __forceinline__ void dec_rows(DecRows<D>& r, const int32_t* ix, int64
   }
 }
 
+// Rows are clamped to rmax = len - 1 where they are used (a no-op for positions;
+// for a listed row, a bad entry reads a wrong row, never one outside the head).
 template <int D, bool BIAS>
 __device__ __forceinline__ void dec_load(DecTile<D>& t, const uint16_t* K, const uint16_t* V,
-                                         const float* lr, const DecRows<D>& r, int lane) {
+                                         const float* lr, const DecRows<D>& r, uint32_t rmax, int lane) {
   constexpr int VL = DecTile<D>::VL;
-  const uint16_t* kr = K + (int64_t)r.k * D + 8 * (lane >> 4);
+  const uint32_t rk = min((uint32_t)r.k, rmax);
+  const uint16_t* kr = K + (int64_t)rk * D + 8 * (lane >> 4);
 #pragma unroll
   for (int s = 0; s < DecTile<D>::KB; ++s) {
     const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kr + 32 * s));
@@ -221,8 +224,9 @@ __device__ __forceinline__ void dec_load(DecTile<D>& t, const uint16_t* K, const
   }
 #pragma unroll
   for (int i = 0; i < DecTile<D>::VI; ++i)
-    t.v[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(V + (int64_t)r.v[i] * D + 8 * (lane % VL)));
-  t.lr = BIAS ? lr[r.k] : 0.f;
+    t.v[i] = __builtin_nontemporal_load(
+        reinterpret_cast<const u32x4*>(V + (int64_t)min((uint32_t)r.v[i], rmax) * D + 8 * (lane % VL)));
+  t.lr = BIAS ? lr[rk] : 0.f;
 }
 
 // partial layout as decode_partial: [lc, Hq, nchunk] x (m, l, -, -, o[d]), m in natural
@@ -269,6 +273,7 @@ decode_mfma(DecTables t, int Hq, int Hkv, int G, int64_t len, float sl2, float b
     }
   }
   const int64_t j0 = (int64_t)ch * ckm, j1 = min(t.npos, j0 + ckm), jlast = j1 - 1;
+  const uint32_t rmax = (uint32_t)(len - 1);
   const int ntile = (int)((j1 - j0 + 15) / 16);
   float m[4], ls[4], o[4][8];
 #pragma unroll
@@ -351,7 +356,7 @@ decode_mfma(DecTables t, int Hq, int Hkv, int G, int64_t len, float sl2, float b
 #pragma unroll
   for (int u = 0; u < kSets; ++u) dec_rows<D, IDX>(rs[u], ix, min(j0 + 16 * u, jl), jlast, lane);
 #pragma unroll
-  for (int u = 0; u + 1 < kSets; ++u) dec_load<D, BIAS>(ts[u], K, V, lr, rs[u], lane);
+  for (int u = 0; u + 1 < kSets; ++u) dec_load<D, BIAS>(ts[u], K, V, lr, rs[u], rmax, lane);
   for (int ti = 0; ti < ntile; ti += kSets) {
     const int64_t jb = j0 + (int64_t)ti * 16;
 #pragma unroll
@@ -360,7 +365,7 @@ decode_mfma(DecTables t, int Hq, int Hkv, int G, int64_t len, float sl2, float b
       // overwrites (otherwise the sets are renamed and copied, with a wait per copy)
       __builtin_amdgcn_sched_barrier(0);
       dec_rows<D, IDX>(rs[u], ix, min(jb + 16 * (u + kSets), jl), jlast, lane);
-      dec_load<D, BIAS>(ts[(u + kSets - 1) % kSets], K, V, lr, rs[(u + kSets - 1) % kSets], lane);
+      dec_load<D, BIAS>(ts[(u + kSets - 1) % kSets], K, V, lr, rs[(u + kSets - 1) % kSets], rmax, lane);
       asm volatile("" ::: "memory");
       tile(ts[u], jb + 16 * u);
     }

@@ -13,9 +13,13 @@
 //      k - w - cgt keys == T in index order.  Output positions come from a block
 //      scan of (count > T, count == T) per thread, so the indices come out
 //      ascending and the result is exact and deterministic.
-// The score row (at most a few hundred KB) is re-read from L2 by each pass; each
-// thread keeps several loads in flight, and the histograms are per wave with
-// wave-aggregated increments where lanes crowd into one bin.
+// Each thread keeps several loads in flight; with rows a multiple of 4 floats long
+// they are 16-byte loads, since a lone workgroup per CU is bound by the bytes it
+// has in flight, not by the histogram work.  When [0, n - w) fits in LDS beside
+// the histograms, the first pass copies it there and the other four passes read
+// it from LDS, so the row comes from memory once; otherwise every pass re-reads
+// it.  The histograms are per wave, with wave-aggregated increments where lanes
+// crowd into one bin.
 #include "common.h"
 
 namespace kvc {
@@ -48,8 +52,12 @@ __device__ __forceinline__ void hist_add(int* hist, bool valid, int bin) {
   }
 }
 
+// VEC: 16-byte loads (n % 4 == 0, S 16-byte aligned).  CACHE: [0, n - w) is held in
+// dynamic LDS, as float4, from the first pass on.
+template <bool VEC, bool CACHE>
 __global__ void __launch_bounds__(NT)
 select_kernel(const float* __restrict__ S, int Hkv, int64_t n, I64s kk, int w, MutPtrs idx) {
+  extern __shared__ float4 rc[];
   __shared__ int hist[NW][256];                   // one histogram per wave
   __shared__ int scan[NT / 64];
   __shared__ int pick[2];
@@ -78,16 +86,46 @@ select_kernel(const float* __restrict__ S, int Hkv, int64_t n, I64s kk, int w, M
     const uint32_t hi_mask = (p == 3) ? 0u : (uint32_t)(~0ull << (shift + 8));
     for (int i = tid; i < NW * 256; i += NT) (&hist[0][0])[i] = 0;
     __syncthreads();
+    auto count = [&](uint32_t key, bool in) __attribute__((always_inline)) {
+      hist_add(hist[wv], in && (key & hi_mask) == (prefix & hi_mask), (int)((key >> shift) & 255));
+    };
+    if constexpr (VEC) {
+      // vectors [0, nv) of 4 scores; the last may reach past nb but not past n
+      const int64_t nv = (nb + 3) / 4;
+      const float4* row4 = reinterpret_cast<const float4*>(row);
+      const bool lds = CACHE && p != 3;
 #pragma unroll 1
-    for (int64_t i0 = 0; i0 < nb; i0 += (int64_t)NT * HU) {
-      float v[HU];                                // HU loads in flight per thread
+      for (int64_t i0 = 0; i0 < nv; i0 += (int64_t)NT * HU) {
+        float4 v[HU];                             // HU 16-byte loads in flight per thread
+        if (lds) {
 #pragma unroll
-      for (int u = 0; u < HU; ++u) v[u] = row[min(i0 + (int64_t)u * NT + tid, nb - 1)];
+          for (int u = 0; u < HU; ++u) v[u] = rc[min(i0 + (int64_t)u * NT + tid, nv - 1)];
+        } else {
 #pragma unroll
-      for (int u = 0; u < HU; ++u) {
-        const uint32_t key = f32_key(v[u]);
-        const bool ok = i0 + (int64_t)u * NT + tid < nb && (key & hi_mask) == (prefix & hi_mask);
-        hist_add(hist[wv], ok, (int)((key >> shift) & 255));
+          for (int u = 0; u < HU; ++u) v[u] = row4[min(i0 + (int64_t)u * NT + tid, nv - 1)];
+          if (CACHE) {
+#pragma unroll
+            for (int u = 0; u < HU; ++u)
+              if (i0 + (int64_t)u * NT + tid < nv) rc[i0 + (int64_t)u * NT + tid] = v[u];
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < HU; ++u) {
+          const int64_t e0 = 4 * (i0 + (int64_t)u * NT + tid);
+          count(f32_key(v[u].x), e0 < nb);
+          count(f32_key(v[u].y), e0 + 1 < nb);
+          count(f32_key(v[u].z), e0 + 2 < nb);
+          count(f32_key(v[u].w), e0 + 3 < nb);
+        }
+      }
+    } else {
+#pragma unroll 1
+      for (int64_t i0 = 0; i0 < nb; i0 += (int64_t)NT * HU) {
+        float v[HU];                              // HU loads in flight per thread
+#pragma unroll
+        for (int u = 0; u < HU; ++u) v[u] = row[min(i0 + (int64_t)u * NT + tid, nb - 1)];
+#pragma unroll
+        for (int u = 0; u < HU; ++u) count(f32_key(v[u]), i0 + (int64_t)u * NT + tid < nb);
       }
     }
     __syncthreads();
@@ -111,10 +149,17 @@ select_kernel(const float* __restrict__ S, int Hkv, int64_t n, I64s kk, int w, M
   // before this chunk's block scan
   int64_t run_gt = 0, run_eq = 0;
   float cur[EPT];
+  static_assert(EPT == 4, "one float4 per thread and chunk");
   auto fetch = [&](int64_t c0, float (&v)[EPT]) __attribute__((always_inline)) {
     const int64_t i0 = c0 + (int64_t)tid * EPT;
+    if constexpr (VEC) {
+      const int64_t vi = min(i0 / 4, (nb - 1) / 4);
+      const float4 f = CACHE ? rc[vi] : reinterpret_cast<const float4*>(row)[vi];
+      v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
+    } else {
 #pragma unroll
-    for (int e = 0; e < EPT; ++e) v[e] = row[min(i0 + e, nb - 1)];
+      for (int e = 0; e < EPT; ++e) v[e] = row[min(i0 + e, nb - 1)];
+    }
   };
   fetch(0, cur);
 #pragma unroll 1
@@ -165,13 +210,32 @@ extern "C" int kvc_select_topk(const float* S, int L, int Hkv, int64_t n, const 
     KVC_REQUIRE(idx_out[l], "kvc_select_topk: idx_out[%d] is null", l);
   }
   hipStream_t s = as_stream(stream);
+  // 16-byte loads need 16-byte rows; the LDS copy of [0, n - w) must fit beside
+  // the kernel's own LDS
+  const bool vec = n % 4 == 0 && (uintptr_t)S % 16 == 0;
+  const size_t cache = (size_t)((n - w + 3) / 4) * sizeof(float4);
+  bool use_cache = false;
+  if (vec && n > w) {
+    int dev = 0, max_lds = 0;
+    const void* kern = reinterpret_cast<const void*>(&select_kernel<true, true>);
+    hipFuncAttributes fa{};
+    use_cache = hipGetDevice(&dev) == hipSuccess &&
+                hipDeviceGetAttribute(&max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) == hipSuccess &&
+                hipFuncGetAttributes(&fa, kern) == hipSuccess &&
+                fa.sharedSizeBytes + cache <= (size_t)max_lds &&
+                hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)cache) == hipSuccess;
+    if (!use_cache) (void)hipGetLastError();      // a refused query only selects the other path
+  }
   for (int l0 = 0; l0 < L; l0 += kLayersPerLaunch) {
     const int lc = min(kLayersPerLaunch, L - l0);
     I64s kk{};
     MutPtrs ip{};
     for (int i = 0; i < lc; ++i) { kk.v[i] = k_keep[l0 + i]; ip.p[i] = idx_out[l0 + i]; }
-    hipLaunchKernelGGL(select_kernel, dim3((unsigned)(lc * Hkv)), dim3(NT), 0, s,
-                       S + (int64_t)l0 * Hkv * n, Hkv, n, kk, w, ip);
+    const dim3 grid((unsigned)(lc * Hkv));
+    const float* Sl = S + (int64_t)l0 * Hkv * n;
+    if (use_cache) hipLaunchKernelGGL((select_kernel<true, true>), grid, dim3(NT), cache, s, Sl, Hkv, n, kk, w, ip);
+    else if (vec) hipLaunchKernelGGL((select_kernel<true, false>), grid, dim3(NT), 0, s, Sl, Hkv, n, kk, w, ip);
+    else hipLaunchKernelGGL((select_kernel<false, false>), grid, dim3(NT), 0, s, Sl, Hkv, n, kk, w, ip);
   }
   return launch_status("kvc_select_topk");
 }

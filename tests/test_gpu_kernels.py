@@ -290,6 +290,11 @@ SELECT_CASES = [
     (1, 4, 4000, 10, 32, 0),         # budget smaller than the window
     (1, 4, 999, 300, 0, 3),          # no window
     (1, 2, 102400, 25600, 32, 0),    # SelKV length
+    (1, 2, 102400, 25600, 32, 4),    # SelKV length with ties: 16-byte loads, row re-read
+    (2, 8, 4096, 834, 31, 5),        # ties; n - w not a multiple of 4 (row held in LDS)
+    (1, 4, 32768, 6553, 32, 0),      # InfoKV length (row held in LDS)
+    (1, 2, 36844, 9000, 0, 2),       # the longest row LDS holds beside the histograms
+    (1, 2, 36848, 9000, 0, 2),       # one vector longer: re-read from memory
     (2, 1, 50, 1, 0, 1),             # one token, all tied
 ]
 
