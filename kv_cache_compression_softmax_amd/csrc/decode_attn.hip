@@ -43,7 +43,7 @@ constexpr int CK = 1024;          // keys per workgroup (decode_partial)
 constexpr int kWaveTarget = 1024;  // decode_mfma waves per launch: MI355X's 256 CUs x 4 SIMDs
 constexpr int kSets = 2;           // decode_mfma register sets (tiles) per wave
 constexpr int kScoreWaves = 2048;  // waves of active_scores_mfma
-constexpr int kScoreSets = 2;      // active_scores_mfma register sets (tiles) per wave
+constexpr int kScoreSets = 4;      // active_scores_mfma register sets (tiles) per wave
 constexpr int MAXG = 8;           // query heads per KV head
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
@@ -398,8 +398,10 @@ decode_mfma(DecTables t, int Hq, int Hkv, int G, int64_t len, float sl2, float b
 // score[l, g, j] = max over the group's query heads of scale * <q_h, k_j>
 //                  (+ beta * u[l][g, j] when a utility row is given)
 // One wave per chunk of keys, 16-key tiles of K in the MFMA B layout (as in
-// decode_mfma, without V), logits on v_mfma_f32_16x16x32_bf16.
-template <int D>
+// decode_mfma, without V), logits on v_mfma_f32_16x16x32_bf16.  UT: a utility row
+// is given; its value for a key is loaded with the key's tile (a load issued at
+// the store would make the in-order wait include the next tile's K loads).
+template <int D, bool UT>
 __global__ void __launch_bounds__(NT)
 active_scores_mfma(DecTables t, int Hkv, int G, int64_t len, float scale, float beta,
                    int nchunk, int64_t ckm, int64_t nw, float* __restrict__ score) {
@@ -430,14 +432,15 @@ active_scores_mfma(DecTables t, int Hkv, int G, int64_t len, float scale, float 
   }
   const int64_t j0 = (int64_t)ch * ckm, j1 = min(len, j0 + ckm), jlast = j1 - 1;
   const int ntile = (int)((j1 - j0 + 15) / 16);
-  auto load = [&](bf16x8 (&kt)[KB], int64_t jb) __attribute__((always_inline)) {
+  auto load = [&](bf16x8 (&kt)[KB], float& uv, int64_t jb) __attribute__((always_inline)) {
     const int64_t kk = min(jb + (lane & 15), jlast);
     const uint16_t* kr = K + kk * D + 8 * (lane >> 4);
 #pragma unroll
     for (int s2 = 0; s2 < KB; ++s2)
       kt[s2] = __builtin_bit_cast(bf16x8, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kr + 32 * s2)));
+    if constexpr (UT) uv = __builtin_nontemporal_load(u + kk);
   };
-  auto tile = [&](const bf16x8 (&kt)[KB], int64_t jb) __attribute__((always_inline)) {
+  auto tile = [&](const bf16x8 (&kt)[KB], float uv, int64_t jb) __attribute__((always_inline)) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s2 = 0; s2 < KB; ++s2) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[s2], kt[s2], acc, 0, 0, 0);
@@ -445,22 +448,24 @@ active_scores_mfma(DecTables t, int Hkv, int G, int64_t len, float scale, float 
 #pragma unroll
     for (int e = 1; e < 4; ++e) m = e < G ? fmaxf(m, acc[e]) : m;
     const int64_t j = jb + (lane & 15);
-    if (lane < 16 && j <= jlast) out[j] = m * scale + (u ? beta * u[j] : 0.f);
+    if (lane < 16 && j <= jlast) out[j] = m * scale + (UT ? beta * uv : 0.f);
   };
   // a ring of kScoreSets register sets, kScoreSets - 1 tiles' loads in flight; loads
   // past the chunk's last tile are clamped to it, and a tile past the end is not stored
   const int64_t jl = j0 + (int64_t)(ntile - 1) * 16;
   bf16x8 kt[kScoreSets][KB];
+  float ut[kScoreSets] = {};
 #pragma unroll
-  for (int v = 0; v + 1 < kScoreSets; ++v) load(kt[v], min(j0 + 16 * v, jl));
+  for (int v = 0; v + 1 < kScoreSets; ++v) load(kt[v], ut[v], min(j0 + 16 * v, jl));
   for (int ti = 0; ti < ntile; ti += kScoreSets) {
     const int64_t jb = j0 + (int64_t)ti * 16;
 #pragma unroll
     for (int v = 0; v < kScoreSets; ++v) {
       __builtin_amdgcn_sched_barrier(0);
-      load(kt[(v + kScoreSets - 1) % kScoreSets], min(jb + 16 * (v + kScoreSets - 1), jl));
+      load(kt[(v + kScoreSets - 1) % kScoreSets], ut[(v + kScoreSets - 1) % kScoreSets],
+           min(jb + 16 * (v + kScoreSets - 1), jl));
       asm volatile("" ::: "memory");
-      if (jb + 16 * v <= jlast) tile(kt[v], jb + 16 * v);
+      if (jb + 16 * v <= jlast) tile(kt[v], ut[v], jb + 16 * v);
     }
   }
 }
@@ -697,8 +702,11 @@ extern "C" int kvc_active_scores(const void* const* q, const void* const* K, int
       const int nchunk = (int)((len + ckm - 1) / ckm);
       const int64_t nw = (int64_t)lc * Hkv * nchunk;
       const dim3 grid((unsigned)((nw + NT / 64 - 1) / (NT / 64)));
-      if (d == 128) hipLaunchKernelGGL(active_scores_mfma<128>, grid, dim3(NT), 0, s, t, Hkv, G, len, scale, beta, nchunk, ckm, nw, out);
-      else hipLaunchKernelGGL(active_scores_mfma<64>, grid, dim3(NT), 0, s, t, Hkv, G, len, scale, beta, nchunk, ckm, nw, out);
+#define KVC_AS(DD, UU) hipLaunchKernelGGL((active_scores_mfma<DD, UU>), grid, dim3(NT), 0, s, t, Hkv, G, len, \
+                                         scale, beta, nchunk, ckm, nw, out)
+      if (d == 128) { if (utility) KVC_AS(128, true); else KVC_AS(128, false); }
+      else { if (utility) KVC_AS(64, true); else KVC_AS(64, false); }
+#undef KVC_AS
     } else {
       const dim3 grid((unsigned)((len + NT - 1) / NT), (unsigned)(lc * Hkv));
       if (dtype == KVC_BF16) hipLaunchKernelGGL(active_scores_any<uint16_t>, grid, dim3(NT), 0, s, t, Hkv, G, len, d, scale, beta, out);
