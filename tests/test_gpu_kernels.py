@@ -322,9 +322,10 @@ def test_select_and_compact(dev, case):
         np.testing.assert_array_equal(host_bits(Vc[l]), vr)
 
 
-def test_select_ragged_budgets_and_compact_f32(dev):
-    L, Hkv, n, w, d = 5, 3, 777, 8, 64
-    ks = [8, 100, 777, 9, 400]
+@pytest.mark.parametrize("n", [777, 1000], ids=["rows-not-x4", "rows-x4"])
+def test_select_ragged_budgets_and_compact_f32(dev, n):
+    L, Hkv, w, d = 5, 3, 8, 64
+    ks = [8, 100, n, 9, 400]
     announce("select ragged", ks)
     S = synth.random_scores((L, Hkv, n), dev, seed=3, tie_levels=7)
     idx = [torch.empty(Hkv, k, dtype=torch.int32, device=dev) for k in ks]
