@@ -32,13 +32,6 @@ __device__ __forceinline__ int64_t row_in(int32_t i, int64_t n) {
   return min((int64_t)(uint32_t)i, n - 1);
 }
 
-// 16-byte store marked non-temporal: the gathered rows are not read again soon
-// (and each source row is read once, so the loads use ld_stream)
-__device__ __forceinline__ void st_stream(void* p, uint4 v) {
-  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-  __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4*>(p));
-}
-
 // MODE: 0 any row size (2-byte words), 1 rows of 16-byte multiples, 2 four-byte rows
 template <int MODE>
 __global__ void __launch_bounds__(NT)

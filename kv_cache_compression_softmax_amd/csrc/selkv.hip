@@ -404,11 +404,11 @@ merge_kernel(MergeTables t, int lc, const float* Ag, int Hkv, int64_t n, int d,
   auto kload = [&](int q) __attribute__((always_inline)) {
     const int s = min(q * RPP + rg, nk - 1);
     const int64_t src = __shfl(kid, s, 64);
-    return *reinterpret_cast<const uint4*>(Kg + src * d + c * W);
+    return ld_stream(Kg + src * d + c * W);      // kept K rows are read once
   };
   auto kstore = [&](int q, const uint4& v) __attribute__((always_inline)) {
     const int s = min(q * RPP + rg, nk - 1);     // clamped lanes rewrite the last row
-    *reinterpret_cast<uint4*>(Ko + (lo + s) * d + c * W) = v;
+    st_stream(Ko + (lo + s) * d + c * W, v);
   };
   const uint4 k0 = kload(0), k1 = kload(1), k2 = kload(2), k3 = kload(3);
 
@@ -435,8 +435,7 @@ merge_kernel(MergeTables t, int lc, const float* Ag, int Hkv, int64_t n, int d,
   for (int s0 = 4 * RPP; s0 < nk; s0 += RPP) {
     const int s = min(s0 + rg, nk - 1);
     const int64_t src = __shfl(kid, s, 64);
-    *reinterpret_cast<uint4*>(Ko + (lo + s) * d + c * W) =
-        *reinterpret_cast<const uint4*>(Kg + src * d + c * W);
+    st_stream(Ko + (lo + s) * d + c * W, ld_stream(Kg + src * d + c * W));
   }
 
   // the target's V row is one of the bucket rows already in registers: pass
@@ -473,7 +472,7 @@ merge_kernel(MergeTables t, int lc, const float* Ag, int Hkv, int64_t n, int d,
     if ((rowmask >> r) & 1ull) {                 // kept: copy its V (the target is merged below)
       if (e != tt) {
         const int64_t slot = lo + __builtin_popcountll(rowmask & ((1ull << r) - 1ull));
-        *reinterpret_cast<uint4*>(Vo + slot * d + c * W) = raw[p];
+        st_stream(Vo + slot * d + c * W, raw[p]);
         if (c == 0) lR[slot] = 0.f;
       }
       continue;
@@ -507,9 +506,9 @@ merge_kernel(MergeTables t, int lc, const float* Ag, int Hkv, int64_t n, int d,
 #pragma unroll
       for (int i = 0; i < W; ++i) out[i] = (At * vt[i] + num[i]) * inv;
       lr = log1pf(den / At);
-      *reinterpret_cast<uint4*>(Vo + ts * d + c * W) = El<T>::pack(out);
+      st_stream(Vo + ts * d + c * W, El<T>::pack(out));
     } else {
-      *reinterpret_cast<uint4*>(Vo + ts * d + c * W) = tv;
+      st_stream(Vo + ts * d + c * W, tv);
     }
     if (c == 0) lR[ts] = lr;
   }
