@@ -239,6 +239,7 @@ WIN_CASES = [
     (1, 4, 2, 40, 33, 128, torch.bfloat16),         # window nearly the whole sequence
     (1, 2, 1, 31, 31, 64, torch.bfloat16),          # w = n < 32
     (1, 6, 2, 150, 20, 32, torch.float32),          # float32 path, G = 3
+    (34, 4, 2, 300, 16, 64, torch.bfloat16),        # more layers than one launch holds
 ]
 
 
@@ -259,7 +260,7 @@ def test_window_attention(dev, case, per_head):
 
 
 # ----------------------------------------------------------------- fuse
-@pytest.mark.parametrize("L,Hkv,n", [(1, 2, 512), (3, 8, 20001), (2, 4, 70000)])
+@pytest.mark.parametrize("L,Hkv,n", [(1, 2, 512), (3, 8, 20001), (2, 4, 70000), (34, 2, 300)])
 def test_fuse_scores(dev, L, Hkv, n):
     announce("fuse", L, Hkv, n)
     g = torch.Generator(device=dev)
@@ -296,6 +297,7 @@ SELECT_CASES = [
     (1, 2, 36844, 9000, 0, 2),       # the longest row LDS holds beside the histograms
     (1, 2, 36848, 9000, 0, 2),       # one vector longer: re-read from memory
     (2, 1, 50, 1, 0, 1),             # one token, all tied
+    (34, 2, 300, 64, 16, 0),         # more layers than one launch holds
 ]
 
 
@@ -361,6 +363,7 @@ SELKV_CASES = [
     (1, 4, 2, 2048, 32, 128, 40, 64),        # 40 kept: no search round, most buckets empty
     (1, 4, 2, 1000, 16, 64, 990, 64),        # nearly all kept: long kept runs, few merges
     (1, 8, 2, 3001, 32, 128, 1500, 32),      # bucket 32, ragged last bucket
+    (34, 4, 2, 300, 16, 64, 100, 32),        # more layers than one launch holds
 ]
 
 
@@ -459,8 +462,7 @@ DECODE_CASES = [(32, 8, 3000, 128, True, torch.bfloat16), (4, 2, 100, 64, False,
 
 
 @pytest.mark.parametrize("Hq,Hkv,length,d,bias,dtype", DECODE_CASES)
-def test_decode_attention(dev, Hq, Hkv, length, d, bias, dtype):
-    L = 2
+def test_decode_attention(dev, Hq, Hkv, length, d, bias, dtype, L=2):
     announce("decode", Hq, Hkv, length, d, bias, dtype)
     q = [gen((Hq, d), 300 + l, dev, dtype) for l in range(L)]
     K = [gen((Hkv, length, d), 320 + l, dev, dtype) for l in range(L)]
@@ -479,6 +481,11 @@ def test_decode_attention(dev, Hq, Hkv, length, d, bias, dtype):
         # lse is a log: its error is relative for the normaliser itself, so an
         # absolute 1e-4 applies where |lse| < 1 (a single key: lse = its logit)
         assert_rel(lse[l].cpu().numpy(), rl, 1e-4, floor=1.0, what="lse")
+
+
+def test_decode_attention_layer_groups(dev):
+    """34 layers: two launches of at most 32 layers' pointers each."""
+    test_decode_attention(dev, 4, 2, 100, 64, True, torch.bfloat16, L=34)
 
 
 # ----------------------------------------------------------------- random sweep

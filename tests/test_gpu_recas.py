@@ -46,9 +46,8 @@ CASES = [(32, 8, 3000, 128, torch.bfloat16, True), (8, 2, 700, 64, torch.bfloat1
 
 
 @pytest.mark.parametrize("Hq,Hkv,n,d,dtype,util", CASES, ids=str)
-def test_active_scores(dev, Hq, Hkv, n, d, dtype, util):
-    announce("active scores", Hq, Hkv, n, d, dtype, util)
-    L = 2
+def test_active_scores(dev, Hq, Hkv, n, d, dtype, util, L=2):
+    announce("active scores", Hq, Hkv, n, d, dtype, util, L)
     q = [gen((Hq, d), 500 + l, dev, dtype) for l in range(L)]
     K = [gen((Hkv, n, d), 520 + l, dev, dtype) for l in range(L)]
     u = [gen((Hkv, n), 540 + l, dev, torch.float32) for l in range(L)] if util else None
@@ -67,9 +66,8 @@ DEC_CASES = [(32, 8, 2000, 128, torch.bfloat16, 600, True), (8, 2, 700, 64, torc
 
 
 @pytest.mark.parametrize("Hq,Hkv,n,d,dtype,k,bias", DEC_CASES, ids=str)
-def test_decode_over_random_active_lists(dev, Hq, Hkv, n, d, dtype, k, bias):
-    announce("decode active", Hq, Hkv, n, d, dtype, k, bias)
-    L = 2
+def test_decode_over_random_active_lists(dev, Hq, Hkv, n, d, dtype, k, bias, L=2):
+    announce("decode active", Hq, Hkv, n, d, dtype, k, bias, L)
     q = [gen((Hq, d), 600 + l, dev, dtype) for l in range(L)]
     K = [gen((Hkv, n, d), 620 + l, dev, dtype) for l in range(L)]
     V = [gen((Hkv, n, d), 640 + l, dev, dtype) for l in range(L)]
@@ -87,6 +85,12 @@ def test_decode_over_random_active_lists(dev, Hq, Hkv, n, d, dtype, k, bias):
                                      host_f64(lr[l]) if bias else None, 0.9 if bias else 0.0)
         assert np.max(np.abs(o[l].cpu().numpy() - ro)) <= 1e-3
         assert_rel(lse[l].cpu().numpy(), rl, 1e-4, floor=1.0, what="lse")
+
+
+def test_layer_groups(dev):
+    """34 layers: two launches of at most 32 layers' pointers each."""
+    test_active_scores(dev, 4, 2, 200, 64, torch.bfloat16, True, L=34)
+    test_decode_over_random_active_lists(dev, 4, 2, 200, 64, torch.bfloat16, 50, True, L=34)
 
 
 @pytest.mark.parametrize("Hq,Hkv,n,d,frac", [(32, 8, 6400, 128, 0.293), (8, 2, 1000, 64, 0.5)], ids=str)

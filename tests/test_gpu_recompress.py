@@ -35,7 +35,7 @@ def B():
     return binding
 
 
-@pytest.mark.parametrize("L,Hkv,n", [(1, 1, 1), (2, 4, 777), (3, 8, 20001)])
+@pytest.mark.parametrize("L,Hkv,n", [(1, 1, 1), (2, 4, 777), (3, 8, 20001), (34, 2, 300)])
 def test_fuse_scores_slots(dev, L, Hkv, n):
     announce("fuse slots", L, Hkv, n)
     g = torch.Generator(device=dev); g.manual_seed(n)
@@ -51,9 +51,10 @@ def test_fuse_scores_slots(dev, L, Hkv, n):
         assert_rel([Ebar[l].item()], [Eb], 1e-3, floor=1e-3, what="Ebar")
 
 
-def test_append_entropy_scores(dev):
-    announce("append entropy scores")
-    L, Hkv, t, cap, off = 3, 5, 1000, 1400, 333
+@pytest.mark.parametrize("L", [3, 34])
+def test_append_entropy_scores(dev, L):
+    announce("append entropy scores", L)
+    Hkv, t, cap, off = 5, 1000, 1400, 333
     g = torch.Generator(device=dev); g.manual_seed(5)
     D = torch.rand(L, t, generator=g, device=dev) + 1
     H = torch.rand(t, generator=g, device=dev) * 5
@@ -67,12 +68,12 @@ def test_append_entropy_scores(dev):
     assert (e[:, :, :off] == -7.0).all() and (e[:, :, off + t:] == -7.0).all()
 
 
-@pytest.mark.parametrize("dtype,d", [(torch.bfloat16, 128), (torch.bfloat16, 64), (torch.float32, 1),
-                                     (torch.float32, 3)])
-def test_compact_into(dev, dtype, d):
-    announce("compact into", dtype, d)
-    L, Hkv, n, out_rows = 2, 3, 1000, 700
-    ks = [300, 555]
+@pytest.mark.parametrize("dtype,d,L", [(torch.bfloat16, 128, 2), (torch.bfloat16, 64, 2), (torch.float32, 1, 2),
+                                       (torch.float32, 3, 2), (torch.bfloat16, 128, 34)])
+def test_compact_into(dev, dtype, d, L):
+    announce("compact into", dtype, d, L)
+    Hkv, n, out_rows = 3, 1000, 700
+    ks = [300, 555] * (L // 2)
     g = torch.Generator(device=dev); g.manual_seed(d)
     K = [torch.randn(Hkv, n, d, generator=g, device=dev).to(dtype) for _ in range(L)]
     V = [torch.randn(Hkv, n, d, generator=g, device=dev).to(dtype) for _ in range(L)]

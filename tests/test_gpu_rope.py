@@ -26,10 +26,9 @@ def dev():
     (4, 129, 2, torch.float32, 10000.0, 3), (3, 1000, 128, torch.float32, 1e6, 0),
     (1, 1, 128, torch.bfloat16, 10000.0, 0), (2, 333, 4, torch.bfloat16, 10000.0, 5),
     (2, 200, 6, torch.float32, 10000.0, 0), (1, 50, 512, torch.bfloat16, 10000.0, 1)], ids=str)
-def test_rope_reposition(dev, Hkv, m, d, dtype, base, new0):
+def test_rope_reposition(dev, Hkv, m, d, dtype, base, new0, L=2):
     from kv_cache_compression_softmax_amd import binding as B
-    announce("rope", Hkv, m, d, dtype, base, new0)
-    L = 2
+    announce("rope", Hkv, m, d, dtype, base, new0, L)
     g = torch.Generator(device=dev)
     g.manual_seed(m + d)
     K = [torch.randn(Hkv, m, d, generator=g, device=dev).to(dtype) for _ in range(L)]
@@ -47,3 +46,8 @@ def test_rope_reposition(dev, Hkv, m, d, dtype, base, new0):
         tol = (2.0 ** -8) * np.abs(ref) + 1e-5 * scale + 1e-6 if dtype == torch.bfloat16 else \
             1e-5 * scale + 1e-6
         assert np.all(np.abs(got - ref) <= tol), float(np.max(np.abs(got - ref) - tol))
+
+
+def test_rope_layer_groups(dev):
+    """34 layers: two launches of at most 32 layers' pointers each."""
+    test_rope_reposition(dev, 2, 100, 128, torch.bfloat16, 500000.0, 3, L=34)
