@@ -344,6 +344,27 @@ def test_select_ragged_budgets_and_compact_f32(dev, n):
         np.testing.assert_array_equal(host_bits(Kc[l]), kr)
 
 
+def test_select_unaligned_scores(dev):
+    """Scores 4 bytes past a 16-byte boundary take the 4-byte load path; the
+    kept indices must be the same as from an aligned copy."""
+    L, Hkv, n, k, w = 2, 3, 4000, 900, 32
+    announce("select unaligned", L, Hkv, n)
+    S = synth.random_scores((L, Hkv, n), dev, seed=11, tie_levels=3)
+    buf = torch.empty(L * Hkv * n + 4, device=dev)
+    Su = buf[1:1 + L * Hkv * n].view(L, Hkv, n)
+    Su.copy_(S)
+    assert Su.data_ptr() % 16 == 4
+    a = [torch.empty(Hkv, k, dtype=torch.int32, device=dev) for _ in range(L)]
+    b = [torch.empty_like(x) for x in a]
+    B().kvc_select_topk(S, [k] * L, w, a)
+    B().kvc_select_topk(Su, [k] * L, w, b)
+    torch.cuda.synchronize()
+    Sn = S.cpu().numpy()
+    for l in range(L):
+        np.testing.assert_array_equal(b[l].cpu().numpy(), a[l].cpu().numpy())
+        np.testing.assert_array_equal(a[l].cpu().numpy(), infokv.select_topk(Sn[l], k, w))
+
+
 def test_select_deterministic(dev):
     S = synth.random_scores((4, 8, 5000), dev, seed=9, tie_levels=4)
     a = [torch.empty(8, 1000, dtype=torch.int32, device=dev) for _ in range(4)]
