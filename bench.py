@@ -366,6 +366,11 @@ def main():
     torch.cuda.synchronize()
     total_ms = marks[0][2].elapsed_time(marks[-1][2])
     ms = total_ms / args.steps
+    # each step from its "start" mark to the next step's (the last one to the
+    # final mark): the median step beside the mean
+    starts = [ev for name, _, ev in marks if name == "start"] + [marks[-1][2]]
+    step_ms = sorted(starts[i].elapsed_time(starts[i + 1]) for i in range(len(starts) - 1))
+    median_ms = (step_ms[(len(step_ms) - 1) // 2] + step_ms[len(step_ms) // 2]) / 2
     # a step's duration: from the previous mark on the same stream to its own mark
     per, last = {}, {}
     for name, sid, ev in marks:
@@ -400,6 +405,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
+        "ms_per_step_median": round(median_ms, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
