@@ -60,6 +60,31 @@ add("ratio_two_parallel_routed", math.log(2.0),
     "R = (A_t + g1 A_1 + g2 A_2) / A_t with g = 1, A = (0.5, 0.25, 0.25)",
     SELKV + " section 2, attention compensation")
 
+# VATP with its GQA union: Hq = 4 query heads over Hkv = 2 groups (G = 2, head h
+# in group h // 2).  Token 0's value is (3, 4, 0, 0) in group 0 (l2 norm 5) and
+# (5, 12, 0, 0) in group 1 (l2 norm 13); the heads' attention on it is
+# 0.1, 0.2, 0.3, 0.4.  VATP = A * ||v|| = 0.5, 1.0, 3.9, 5.2 and the union takes
+# the largest of each group: U = (1.0, 5.2).
+add("vatp_norms_5_13_A_1234", {"vatp": [0.5, 1.0, 3.9, 5.2], "U": [1.0, 5.2]},
+    "VATP[h] = A[h] * ||v_{h // 2}||_2 with norms 5 (3-4-5) and 13 (5-12-13); U = max per group",
+    SELKV + " section 2, pipeline overview step 1 (VATP: attention times value norm) and"
+    " step 2 (union over the query heads of a KV head)")
+
+# Compensated decode: d = 4, scale 1/2, q = (2, 0, 0, 0) and two keys (10, 0, 0, 0)
+# give the logit 10 twice; ln R = (0, ln 3) with alpha = 1 adds ln 3 to key 1.
+# Normaliser e^10 + 3 e^10, so lse = 10 + ln 4 and o = v0/4 + 3 v1/4.
+add("decode_lse_two_keys_bias_ln3", 10.0 + math.log(4.0),
+    "logits 10 and 10 + ln 3: lse = ln(e^10 (1 + 3)) = 10 + ln 4",
+    SELKV + " section 2, attention compensation (alpha * ln R added to the logit)")
+
+# Rotary re-positioning with d = 4 (pairs (0, 2) and (1, 3)): pair i turns by
+# delta * base^(-2i/d); pair 1 by delta * base^(-1/2).  base 10000, delta 7:
+# 0.07 rad.
+add("rope_d4_pair1_angle_base1e4_delta7", 7.0 * 10000.0 ** -0.5,
+    "pair i = 1 of d = 4: angle = delta * base^(-2 * 1 / 4) = 7 / 100",
+    SELKV + " section 2, pipeline overview step 6 (RoPE re-positioning); the"
+    " frequency schedule base^(-2i/d) is the standard rotary one, the page gives none")
+
 here = os.path.dirname(os.path.abspath(__file__))
 with open(os.path.join(here, "closed_forms.json"), "w") as f:
     json.dump(forms, f, indent=1, sort_keys=True)

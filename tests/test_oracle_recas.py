@@ -7,10 +7,14 @@
   * The formal bound of section 2.B, ||o - o_active|| <= 2 * V_max * delta,
     where delta is the attention mass outside the active set, on random sets.
   * A large utility on chosen entries puts exactly them into the active set.
+  * Decode attention itself (the function the active step calls): lse by a
+    closed form and by scipy's logsumexp, o by torch's SDPA with the bias as
+    an additive mask.
 """
 import math
 
 import numpy as np
+import pytest
 
 from oracle import infokv, recas
 
@@ -71,3 +75,41 @@ def test_utility_selects_its_entries():
     u[0, [3, 17, 40]] = 1e6
     a = recas.active_set(recas.active_scores(q, K, u, 1.0).astype(np.float32), 3)
     assert a[0].tolist() == [3, 17, 40]
+
+
+def test_decode_lse_closed_form(golden):
+    # two keys with the logit 10; ln R = (0, ln 3) adds ln 3 to the second
+    q = np.array([[2.0, 0.0, 0.0, 0.0]])
+    K = np.array([[[10.0, 0.0, 0.0, 0.0], [10.0, 0.0, 0.0, 0.0]]])
+    V = np.array([[[4.0, 0.0, 0.0, 0.0], [0.0, 8.0, 0.0, 0.0]]])
+    lnR = np.array([[0.0, math.log(3.0)]])
+    o, lse = infokv.decode_attention(q, K, V, lnR, 1.0, scale=0.5)
+    assert abs(lse[0] - golden["decode_lse_two_keys_bias_ln3"]) < 1e-13
+    np.testing.assert_allclose(o[0], [1.0, 6.0, 0.0, 0.0], rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_decode_matches_library_logsumexp_and_sdpa(seed):
+    """lse against scipy's logsumexp of the biased logits, o against torch's
+    scaled_dot_product_attention (float64, CPU) with alpha * ln R as an additive
+    mask; both are library routines, not the oracle's own steps."""
+    import scipy.special
+    import torch
+    r = np.random.default_rng(seed)
+    Hq, Hkv, n, d = 8, 2, 90, 16
+    q = r.normal(size=(Hq, d)) * 3.0 + 2.0          # large logits: lse far from 0
+    K, V = r.normal(size=(Hkv, n, d)), r.normal(size=(Hkv, n, d))
+    lnR = r.random((Hkv, n)) * 2.0
+    alpha = 0.7
+    o, lse = infokv.decode_attention(q, K, V, lnR, alpha)
+    G = Hq // Hkv
+    sc = 1.0 / math.sqrt(d)
+    for h in range(Hq):
+        g = h // G
+        logits = (K[g] @ q[h]) * sc + alpha * lnR[g]
+        assert abs(lse[h] - scipy.special.logsumexp(logits)) <= 1e-12 * max(1.0, abs(lse[h]))
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(q[h])[None, None], torch.from_numpy(K[g])[None],
+            torch.from_numpy(V[g])[None], attn_mask=torch.from_numpy(alpha * lnR[g])[None, None])
+        np.testing.assert_allclose(o[h], ref[0, 0].numpy(), rtol=1e-12, atol=1e-13)
+    assert np.abs(lse).min() > 1.0

@@ -30,6 +30,15 @@ def test_slot_softmax_rows_match_scipy():
     assert Ebar == pytest.approx(E.mean(), rel=1e-14)
 
 
+def test_slot_softmax_is_per_head_under_far_apart_rows():
+    # head 1's scores sit 2000 below head 0's: each head's softmax is its own,
+    # so both rows still sum to one (a shared shift would underflow head 1)
+    E = np.stack([rng.normal(size=40), rng.normal(size=40) - 2000.0])
+    _, _, sigma = infokv.fuse_scores_slots(np.zeros((2, 40)), E, 0.5)
+    np.testing.assert_allclose(sigma.sum(axis=1), 1.0, rtol=1e-14)
+    np.testing.assert_allclose(sigma[1], scipy.special.softmax(E[1]), rtol=1e-12)
+
+
 def test_slot_fusion_equals_prefill_fusion_for_shared_slots():
     n = 64
     A = rng.random((4, n))

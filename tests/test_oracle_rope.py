@@ -2,9 +2,13 @@
 
   * d = 2: the single pair turns by (new - old) radians (frequency base^0 = 1),
     so (1, 0) goes to (cos, sin) of that angle.
+  * d = 4: pair 1 (elements 1 and 3) turns by (new - old) * base^(-1/2), a
+    closed form that fixes the frequency schedule base^(-2i/d) (a wrong
+    exponent such as base^(-i/d) turns it by another angle).
   * Re-positioning a key embedded at position p to position p' equals embedding
-    the raw key at p' (rotations compose): a wrong sign, a swapped pair half or
-    a wrong frequency exponent fails it.
+    the raw key at p' (rotations compose): a wrong sign or a swapped pair half
+    fails it.  It holds for any frequency family, so it does not fix the
+    schedule; the d = 4 closed form does.
   * Zero shift is the identity; every pair keeps its norm.
 """
 import math
@@ -22,6 +26,16 @@ def test_two_dims_closed_form():
     # slot 0: 2 - 5 = -3 rad; slot 1: 3 - 9 = -6 rad
     np.testing.assert_allclose(out[0, 0], [math.cos(-3), math.sin(-3)], rtol=0, atol=1e-15)
     np.testing.assert_allclose(out[0, 1], [-2 * math.sin(-6), 2 * math.cos(-6)], rtol=0, atol=1e-15)
+
+
+def test_four_dims_pair_one_frequency(golden):
+    # row 0 holds (0, 1, 0, 0): pair 1 is (element 1, element 3) = (1, 0);
+    # row 1 holds (1, 0, 0, 0): pair 0 turns by the whole shift (base^0 = 1)
+    K = np.array([[[0.0, 1.0, 0.0, 0.0], [1.0, 0.0, 0.0, 0.0]]])
+    out = selkv.rope_reposition(K, np.array([[3, 4]]), 10, 10000.0)     # shifts 7 and 7
+    ang = golden["rope_d4_pair1_angle_base1e4_delta7"]
+    np.testing.assert_allclose(out[0, 0], [0.0, math.cos(ang), 0.0, math.sin(ang)], rtol=0, atol=1e-15)
+    np.testing.assert_allclose(out[0, 1], [math.cos(7.0), 0.0, math.sin(7.0), 0.0], rtol=0, atol=1e-15)
 
 
 def test_reposition_equals_embedding_at_the_new_position():

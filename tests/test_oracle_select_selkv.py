@@ -81,6 +81,49 @@ def test_dropped_mass_bound_and_renormalised_output(seed):
     np.testing.assert_allclose(o, of, atol=1e-12)
 
 
+def test_dropped_mass_closed_form():
+    # two keys with equal logits (q orthogonal to both): p = (1/2, 1/2); token 1
+    # is evicted, so delta = 1/2.  Values (3, 4) and (0, 1): V_max = 5, o is
+    # their mean, o' = v0, and ||o - o'|| = ||(v1 - v0) / 2|| = sqrt(9 + 9) / 2.
+    q = np.array([[0.0, 0.0, 1.0]])
+    K = np.array([[[1.0, 0.0, 0.0], [0.0, 1.0, 0.0]]])
+    V = np.array([[[3.0, 4.0, 0.0], [0.0, 1.0, 0.0]]])
+    o, o2, delta, vmax = infokv.dropped_mass_bound(q, K, V, np.array([[0]]))
+    assert delta[0] == 0.5 and vmax[0] == 5.0
+    np.testing.assert_allclose(o[0], [1.5, 2.5, 0.0], rtol=0, atol=1e-15)
+    np.testing.assert_allclose(o2[0], [3.0, 4.0, 0.0], rtol=0, atol=1e-15)
+    assert abs(np.linalg.norm(o - o2) - math.sqrt(18.0) / 2) < 1e-14
+    assert np.linalg.norm(o - o2) <= 2 * vmax[0] * delta[0]
+
+
+def test_selkv_group_attention_is_the_group_mean_of_sdpa():
+    """A_g (routing target and merge weight) is the mean over the group's heads
+    of window attention, here rebuilt from torch's SDPA (float64, V = I); the
+    route and merge of ``selkv_layer`` are re-run on that A_g."""
+    import torch
+    Hq, Hkv, n, d, w, m, bucket = 6, 2, 96, 8, 8, 30, 16
+    q_win = rng.normal(size=(Hq, w, d)) * 2.0
+    K = rng.normal(size=(Hkv, n, d))
+    V = rng.normal(size=(Hkv, n, d))
+    out = selkv.selkv_layer(q_win, K, V, m, w, bucket)
+    G = Hq // Hkv
+    pos = n - w + np.arange(w)
+    mask = torch.from_numpy(np.arange(n)[None, :] <= pos[:, None])
+    eye = torch.eye(n, dtype=torch.float64)
+    A_h = np.stack([torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q_win[h])[None], torch.from_numpy(K[h // G])[None], eye[None],
+        attn_mask=mask[None])[0].numpy().mean(axis=0) for h in range(Hq)])
+    A_g = A_h.reshape(Hkv, G, n).mean(axis=1)
+    np.testing.assert_allclose(out["A_g"], A_g, rtol=1e-12, atol=1e-15)
+    assert np.abs(A_h.reshape(Hkv, G, n).max(axis=1) - A_g).max() > 1e-3   # mean != max here
+    for g in range(Hkv):
+        t = selkv.route(out["idx"][g], A_g[g], n, bucket)
+        np.testing.assert_array_equal(out["target"][g], t)
+        Vp, lnR, _ = selkv.merge_group(V[g], A_g[g], out["idx"][g], t)
+        np.testing.assert_allclose(out["Vp"][g], Vp, rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(out["lnR"][g], lnR, rtol=1e-12, atol=1e-14)
+
+
 def test_gate_closed_forms(golden):
     a = np.array([1.0, 0.0, 2.0, 0.0])
     b = np.array([0.0, 3.0, 0.0, -1.0])
@@ -117,6 +160,35 @@ def test_route_picks_highest_attention_lowest_index():
     assert t.tolist() == [1, -1, -1, -1, 7, 7, 7, -1]
     t = selkv.route(np.array([5]), A, 8, 4)     # bucket 0 has no kept token
     assert t.tolist() == [-1, -1, -1, -1, 5, -1, 5, 5]
+
+
+def test_vatp_union_closed_form(golden):
+    # token 0: group 0 value (3, 4, 0, 0), group 1 value (5, 12, 0, 0); token 1
+    # is a zero vector (norm 0, so VATP 0 whatever the attention)
+    V = np.zeros((2, 2, 4))
+    V[0, 0, :2] = [3.0, 4.0]
+    V[1, 0, :2] = [5.0, 12.0]
+    A_hq = np.array([[0.1, 0.9], [0.2, 0.8], [0.3, 0.7], [0.4, 0.6]])
+    vatp, U = selkv.vatp_union(A_hq, V)
+    want = golden["vatp_norms_5_13_A_1234"]
+    np.testing.assert_allclose(vatp[:, 0], want["vatp"], rtol=1e-15)
+    np.testing.assert_allclose(U[:, 0], want["U"], rtol=1e-15)
+    assert (vatp[:, 1] == 0).all() and (U[:, 1] == 0).all()
+
+
+def test_vatp_union_brute_force():
+    Hq, Hkv, n, d = 6, 3, 25, 5
+    A_hq = rng.random((Hq, n))
+    V = rng.normal(size=(Hkv, n, d)) * rng.random((Hkv, 1, 1)) * 4
+    vatp, U = selkv.vatp_union(A_hq, V)
+    G = Hq // Hkv
+    for g in range(Hkv):
+        for j in range(n):
+            norm = math.sqrt(sum(float(x) ** 2 for x in V[g, j]))
+            heads = [A_hq[h, j] * norm for h in range(g * G, (g + 1) * G)]
+            for h, val in zip(range(g * G, (g + 1) * G), heads):
+                assert abs(vatp[h, j] - val) <= 1e-14 * max(1.0, val)
+            assert abs(U[g, j] - max(heads)) <= 1e-14 * max(1.0, max(heads))
 
 
 def test_union_is_shared_threshold_superlevel_union():
