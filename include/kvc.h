@@ -100,6 +100,7 @@ int kvc_repr_distance(const void* const* h_layers, const void* h_final, int dtyp
  *   q_win      host array of L device pointers, each [Hq, w, d] of dtype.
  *   k          host array of L device pointers, each [Hkv, n, d] of dtype.
  *   A_out      device float32, shape above.  Every row of A sums to 1.
+ *   scale: finite and > 0 (1/sqrt(d) in the pages' attention).
  *   1 <= w <= n; Hq % Hkv == 0; bf16 needs d in {64, 128} and
  *   (Hq/Hkv) * ceil(w/32) <= 8; float32 needs d <= 256.
  *   ws         device workspace, kvc_score_window_attn_workspace_size() bytes.
@@ -293,7 +294,7 @@ int kvc_rope_reposition(void* const* K, int dtype, const int32_t* const* pos_old
  *   K, V       host arrays of L device pointers, each [Hkv, len, d] of dtype.
  *   logR       host array of L device pointers, each float32 [Hkv, len], or NULL.
  *   o_out      device float32 [L, Hq, d];  lse_out device float32 [L, Hq].
- *   len >= 1; d <= 256.
+ *   len >= 1; d <= 256; scale and alpha_bias finite.
  */
 size_t kvc_decode_attn_workspace_size(int L, int Hq, int64_t len, int d);
 int kvc_decode_attn(const void* const* q, const void* const* K, const void* const* V,
@@ -314,7 +315,7 @@ int kvc_decode_attn(const void* const* q, const void* const* K, const void* cons
  *   K          host array of L device pointers, each [Hkv, len, d] of dtype.
  *   utility    host array of L device pointers, each float32 [Hkv, len], or NULL.
  *   score_out  device float32 [L, Hkv, len].
- *   Hq / Hkv <= 8; L * Hkv <= 65535; d <= 256.
+ *   Hq / Hkv <= 8; L * Hkv <= 65535; d <= 256; scale finite and > 0; beta finite.
  */
 int kvc_active_scores(const void* const* q, const void* const* K, int dtype,
                       const float* const* utility, float beta, int L, int Hq, int Hkv,

@@ -33,6 +33,8 @@
 // bytes each); per key the G dot products are reduced inside the lane group,
 // then an online softmax keeps (max, sum, output) per head.  Lane groups, then
 // waves, are merged in a fixed order.
+#include <cmath>
+
 #include "common.h"
 
 namespace kvc {
@@ -586,6 +588,7 @@ int decode_impl(const char* fn, const void* const* q, const void* const* K, cons
   KVC_REQUIRE(Hq / Hkv <= MAXG, "%s: more than %d query heads per KV head", fn, MAXG);
   KVC_REQUIRE(len >= 1 && len <= 0x7fffffffLL, "%s: need 1 <= len < 2^31", fn);
   KVC_REQUIRE(q && K && V && o_out, "%s: null pointer", fn);
+  KVC_REQUIRE(std::isfinite(scale) && std::isfinite(alpha_bias), "%s: scale and alpha_bias must be finite", fn);
   const int rb = d * dtype_size(dtype);
   KVC_REQUIRE(d <= 256 && rb % 16 == 0 && (rb / 16 == 4 || rb / 16 == 8 || rb / 16 == 16 || rb / 16 == 32),
               "%s: need d * elsize in {64, 128, 256, 512} bytes and d <= 256", fn);
@@ -679,6 +682,10 @@ extern "C" int kvc_active_scores(const void* const* q, const void* const* K, int
   KVC_REQUIRE(len >= 1 && len <= 0x7fffffffLL && d >= 1 && d <= 256,
               "kvc_active_scores: need 1 <= len < 2^31 and 1 <= d <= 256");
   KVC_REQUIRE(q && K && score_out, "kvc_active_scores: null pointer");
+  // The group maximum is taken over raw dot products and scaled afterwards,
+  // which equals the maximum of the scaled ones only for scale > 0.
+  KVC_REQUIRE(scale > 0.f && std::isfinite(scale) && std::isfinite(beta),
+              "kvc_active_scores: need a finite scale > 0 and a finite beta");
   KVC_REQUIRE((int64_t)L * Hkv <= 65535, "kvc_active_scores: L * Hkv > 65535");
   const int G = Hq / Hkv;
   const bool mfma = dtype == KVC_BF16 && G <= 4 && (d == 64 || d == 128);

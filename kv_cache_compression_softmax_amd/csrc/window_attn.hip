@@ -27,6 +27,7 @@
 // instruction touches 32 cache lines, not 64 (measured 5.9 vs 4.6 TB/s for a
 // plain K stream).  Q is staged once per workgroup in LDS in fragment order, one
 // ds_read_b128 per fragment.
+#include <cmath>
 #include <type_traits>
 
 #include "common.h"
@@ -604,6 +605,9 @@ extern "C" int kvc_score_window_attn(const void* const* q_win, const void* const
   KVC_REQUIRE(n >= 1 && w >= 1 && w <= n, "kvc_score_window_attn: need 1 <= w <= n");
   KVC_REQUIRE(n <= 0x7fffffffLL, "kvc_score_window_attn: n > 2^31-1");
   KVC_REQUIRE(per_query_head == 0 || per_query_head == 1, "kvc_score_window_attn: per_query_head");
+  // The passes keep running maxima of the raw dot products and scale them
+  // afterwards, which is the maximum of the scaled logits only for scale > 0.
+  KVC_REQUIRE(scale > 0.f && std::isfinite(scale), "kvc_score_window_attn: need a finite scale > 0");
   KVC_REQUIRE(q_win && k && A_out, "kvc_score_window_attn: null pointer");
   for (int l = 0; l < L; ++l)
     KVC_REQUIRE(q_win[l] && k[l], "kvc_score_window_attn: null pointer in layer %d", l);

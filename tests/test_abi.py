@@ -82,6 +82,10 @@ def test_validation_before_launch(lib):
     assert lib.kvc_score_window_attn(pa, pa, 1, 1, 4, 2, 64, 65, 128, ctypes.c_float(0.1), 0, fake, fake, 1 << 30, None) == -1
     assert lib.kvc_score_window_attn(pa, pa, 1, 1, 4, 2, 64, 8, 128, ctypes.c_float(0.1), 0, fake, None, 0, None) == -3
     assert lib.kvc_score_window_attn(pa, pa, 1, 1, 4, 2, 64, 8, 96, ctypes.c_float(0.1), 0, fake, fake, 1 << 30, None) == -1
+    # window attention: the scale must be finite and positive
+    for bad in (0.0, -0.1, float("inf"), float("nan")):
+        assert lib.kvc_score_window_attn(pa, pa, 1, 1, 4, 2, 64, 8, 128, ctypes.c_float(bad), 0, fake, fake, 1 << 30, None) == -1
+        assert "scale" in err(lib)
     # select: k_keep outside [1, n]
     kk = (ctypes.c_int64 * 1)(65)
     assert lib.kvc_select_topk(fake, 1, 2, 64, kk, 8, pa, None) == -1
@@ -114,6 +118,14 @@ def test_validation_before_launch_decode_side(lib):
     assert lib.kvc_append_entropy_scores(fake, fake, 1, 2, 100, fake, 150, 51, None) == -1
     # active scores: Hq not a multiple of Hkv
     assert lib.kvc_active_scores(pa, pa, 1, None, 0.0, 1, 6, 4, 64, 128, 0.1, fake, None) == -1
+    # active scores: the scale must be finite and positive
+    assert lib.kvc_active_scores(pa, pa, 1, None, 0.0, 1, 8, 2, 64, 128, -0.1, fake, None) == -1
+    assert "scale" in err(lib)
+    # decode: a non-finite scale or bias
+    assert lib.kvc_decode_attn(pa, pa, pa, 1, None, ctypes.c_float(float("nan")), 1, 8, 2, 64, 128,
+                               ctypes.c_float(0.1), fake, None, fake, 1 << 20, None) == -1
+    assert lib.kvc_decode_attn(pa, pa, pa, 1, None, ctypes.c_float(0), 1, 8, 2, 64, 128,
+                               ctypes.c_float(float("inf")), fake, None, fake, 1 << 20, None) == -1
     # active decode: no list, or more positions than rows
     assert lib.kvc_decode_attn_active(pa, pa, pa, 1, None, 0.0, None, 8, 1, 8, 2, 64, 128, 0.1,
                                       fake, None, fake, 1 << 20, None) == -1
