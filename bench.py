@@ -139,166 +139,180 @@ def window_flops(w):
     return 2 * 2 * w.layers * w.heads_q * w.window * w.n * w.head_dim
 
 
-def host_cores():
-    """Threads the oracle's BLAS pool uses, and the host CPU's model name."""
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-    except Exception:
-        cores = 1
-    cpu = "unknown"
+def host_cpu():
+    """The host CPU's model name."""
     try:
         with open("/proc/cpuinfo") as f:
             for line in f:
                 if line.startswith("model name"):
-                    cpu = line.split(":", 1)[1].strip()
-                    break
+                    return line.split(":", 1)[1].strip()
     except OSError:
         pass
-    return cores, cpu
+    return "unknown"
+
+
+def _host(t):
+    """Host copy of a device tensor: bf16 as its uint16 bit pattern."""
+    import numpy as np
+    import torch
+    t = t.detach().cpu().contiguous()
+    return t.view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16 else t.numpy()
+
+
+def _to_f64(a):
+    import numpy as np
+    from oracle import precision
+    return precision.bf16_bits_to_f64(a) if a.dtype == np.uint16 else a.astype(np.float64)
+
+
+def _rounds(fn, pieces, threads, deadline):
+    """Runs pieces `threads` at a time on the oracle's thread pool until all are
+    done or `deadline` passes; returns (results, pieces done, wall seconds)."""
+    from oracle import parallel
+    out, done, t0 = [], 0, time.perf_counter()
+    while done < len(pieces) and (done == 0 or time.perf_counter() < deadline):
+        batch = pieces[done:done + threads]
+        out += parallel.map_pieces(fn, batch, threads)
+        done += len(batch)
+    return out, done, time.perf_counter() - t0
 
 
 def cpu_baseline(w, inp, budget_s=15.0):
-    """The oracle, as it stands, on a bounded sample of the same workload: whole
-    chunks of the step are run until about `budget_s` seconds of CPU work are
-    spent, and each component's time is scaled by the share of the step its
-    chunks covered."""
+    """The oracle, as it stands, on a bounded sample of the same workload, run
+    on a pool of host threads (one piece per thread: a chunk of logits rows, a
+    chunk of hidden-state rows over every layer, or one layer's attention,
+    fusion, selection and gather).  Pieces run until about `budget_s` seconds
+    are spent; each leg's wall time is scaled by the share of the step its
+    pieces covered."""
     import numpy as np
-    import torch
-    from oracle import infokv, precision, selkv
+    from oracle import infokv, parallel, selkv
 
-    cores, cpu = host_cores()
-
-    def f64(t):
-        t = t.detach().cpu().contiguous()
-        if t.dtype == torch.bfloat16:
-            return precision.bf16_bits_to_f64(t.view(torch.int16).numpy().view(np.uint16))
-        return t.numpy().astype(np.float64)
-
+    T = parallel.host_threads()
     L, n = w.layers, w.n
     t_start = time.perf_counter()
     if w.method == "infokv":
-        # a chunk: 256 more logits rows, the same rows of every layer's hidden
-        # states, and one more layer's window attention, fuse, select and gather
         kk = infokv.uniform_budget(w.keep_fraction, n) if not w.adaptive_fraction else \
             w.adaptive_total() // L
-        rows_step = 256
-        t_h = t_d = t_l = 0.0
-        rows = layers = 0
-        while time.perf_counter() - t_start < budget_s and (rows < n or layers < L):
-            if rows < n:
-                r0, r1 = rows, min(n, rows + rows_step)
-                lg = f64(inp["logits"][r0:r1])
-                t0 = time.perf_counter()
-                H = infokv.topk_entropy(lg, w.topk_entropy)
-                t_h += time.perf_counter() - t0
-                del lg
-                hf = f64(inp["h_final"][r0:r1])
-                hl = [f64(inp["h"][l][r0:r1]) for l in range(L)]
-                t0 = time.perf_counter()
-                Ds = [infokv.repr_distance(hl[l], hf, w.tau) for l in range(L)]
-                t_d += time.perf_counter() - t0
-                del hl, hf
-                rows = r1
-            if layers < L:
-                lay = layers
-                q, k = f64(inp["q_win"][lay]), f64(inp["k"][lay])
-                kb = inp["k"][lay].cpu().view(torch.int16).numpy()
-                vb = inp["v"][lay].cpu().view(torch.int16).numpy()
-                # D and H over the whole row set are not all computed yet: the
-                # sampled rows' values are tiled to length n (only the time of
-                # fuse and select matters here, and neither depends on values)
-                Dn, Hn = np.resize(Ds[lay % len(Ds)], n), np.resize(H, n)
-                t0 = time.perf_counter()
-                A = infokv.window_attention(q, k)
-                S, _, _, _ = infokv.fuse_scores(A, Dn, Hn, w.alpha_fuse)
-                idx = infokv.select_topk(S.astype(np.float32), kk, w.window)
-                infokv.compact(kb, vb, idx)
-                t_l += time.perf_counter() - t0
-                del q, k, kb, vb
-                layers += 1
-        total = t_h * n / rows + t_d * n / rows + t_l * L / layers
-        sample = (f"oracle run for {time.perf_counter() - t_start:.1f} s: top-k entropy and "
-                  f"representation distance on {rows} of {n} token rows (all {L} layers), window "
-                  f"attention + fuse + select + gather on {layers} of {L} layers; each part "
-                  f"scaled by rows or layers to the whole step")
+        chunks = parallel.row_chunks(n, 256)
+        # host copies of the inputs (not timed): bf16 bit patterns, decoded per piece
+        logits = _host(inp["logits"])
+        hf, hl = _host(inp["h_final"]), [_host(h) for h in inp["h"]]
+        q = [_host(x) for x in inp["q_win"]]
+        kb, vb = [_host(x) for x in inp["k"]], [_host(x) for x in inp["v"]]
+        t_copy = time.perf_counter() - t_start
+        deadline = time.perf_counter() + budget_s / 3
+
+        def ent(c):
+            return infokv.topk_entropy(_to_f64(logits[c[0]:c[1]]), w.topk_entropy)
+
+        Hs, rows_h, t_h = _rounds(ent, chunks, T, deadline)
+        deadline = time.perf_counter() + budget_s / 3
+
+        def dist(c):
+            b = _to_f64(hf[c[0]:c[1]])
+            return [infokv.repr_distance(_to_f64(hl[l][c[0]:c[1]]), b, w.tau) for l in range(L)]
+
+        Ds, rows_d, t_d = _rounds(dist, chunks, T, deadline)
+        # the layers' fusion needs H and D of all n tokens: the computed rows are
+        # tiled to length n (fusion and selection take the same time on any values)
+        H = np.resize(np.concatenate(Hs), n)
+        D = [np.resize(np.concatenate([c[l] for c in Ds]), n) for l in range(L)]
+        deadline = time.perf_counter() + budget_s / 3
+
+        def layer(l):
+            A = infokv.window_attention(_to_f64(q[l]), _to_f64(kb[l]))
+            S, _, _, _ = infokv.fuse_scores(A, D[l], H, w.alpha_fuse)
+            idx = infokv.select_topk(S.astype(np.float32), kk, w.window)
+            infokv.compact(kb[l], vb[l], idx)
+
+        _, layers, t_l = _rounds(layer, list(range(L)), T, deadline)
+        rh, rd = chunks[rows_h - 1][1], chunks[rows_d - 1][1]
+        total = t_h * n / rh + t_d * n / rd + t_l * L / layers
+        threads = {"topk_entropy": min(T, rows_h), "repr_distance": min(T, rows_d),
+                   "attention_fuse_select_gather": min(T, layers)}
+        sample = (f"oracle on {T} host threads for {time.perf_counter() - t_start - t_copy:.1f} s: "
+                  f"top-k entropy on {rh} of {n} token rows, representation distance on {rd} of "
+                  f"{n} token rows (all {L} layers), window attention + fuse + select + gather on "
+                  f"{layers} of {L} layers; each leg's wall time scaled by rows or layers to the "
+                  f"whole step")
     else:
-        # a chunk: one whole layer (attention, union, select, route, gate, merge)
-        t_l = 0.0
-        layers = 0
-        while layers < L and (layers == 0 or time.perf_counter() - t_start < budget_s):
-            lay = layers
-            q, k, v = f64(inp["q_win"][lay]), f64(inp["k"][lay]), f64(inp["v"][lay])
-            t0 = time.perf_counter()
-            selkv.selkv_layer(q, k, v, int(w.keep_fraction * n), w.window, w.bucket)
-            t_l += time.perf_counter() - t0
-            del q, k, v
-            layers += 1
+        qb = [_host(x) for x in inp["q_win"]]
+        kb, vb = [_host(x) for x in inp["k"]], [_host(x) for x in inp["v"]]
+        t_copy = time.perf_counter() - t_start
+        deadline = time.perf_counter() + budget_s
+
+        def layer(l):
+            selkv.selkv_layer(_to_f64(qb[l]), _to_f64(kb[l]), _to_f64(vb[l]),
+                              int(w.keep_fraction * n), w.window, w.bucket)
+
+        _, layers, t_l = _rounds(layer, list(range(L)), T, deadline)
         total = t_l * L / layers
-        sample = (f"oracle run for {time.perf_counter() - t_start:.1f} s: the SelKV layer "
-                  f"(attention, union, select, route, gate, merge) on all {n} tokens of {layers} "
-                  f"of {L} layers, scaled by layers to the whole step")
-    return {"value": n / total, "unit": "tokens/s", "cores": cores, "cpu": cpu, "kind": "oracle",
-            "sample": sample, "sample_s": round(time.perf_counter() - t_start, 2),
-            "est_step_s": total}
+        threads = {"selkv_layer": min(T, layers)}
+        sample = (f"oracle on {T} host threads for {time.perf_counter() - t_start - t_copy:.1f} s: "
+                  f"the SelKV layer (attention, union, select, route, gate, merge) on all {n} "
+                  f"tokens of {layers} of {L} layers, one layer per thread, scaled by layers to "
+                  f"the whole step (route and merge loop in Python, which holds the interpreter "
+                  f"lock, so their threads overlap only partly)")
+    return {"value": n / total, "unit": "tokens/s", "cores": max(threads.values()), "threads": threads,
+            "cpu": host_cpu(), "kind": "oracle", "sample": sample,
+            "sample_s": round(time.perf_counter() - t_start - t_copy, 2), "est_step_s": total}
 
 
 def cpu_baseline_period(w, plan, new, period, budget_s=15.0):
-    """The oracle on a bounded sample of one decode period: the new tokens' H
-    and D on row chunks, and the re-compression (attention, slot fusion,
-    select, gather) of whole layers, each part scaled to the whole period."""
+    """The oracle on a bounded sample of one decode period, on a pool of host
+    threads: the new tokens' H and D on row chunks, and the re-compression
+    (attention, slot fusion, select, gather) of whole layers, each leg's wall
+    time scaled to the whole period."""
     import numpy as np
-    import torch
-    from oracle import infokv, precision
+    from oracle import infokv, parallel
 
-    cores, cpu = host_cores()
-
-    def f64(t):
-        t = t.detach().cpu().contiguous()
-        if t.dtype == torch.bfloat16:
-            return precision.bf16_bits_to_f64(t.view(torch.int16).numpy().view(np.uint16))
-        return t.numpy().astype(np.float64)
-
+    T = parallel.host_threads()
     L, G = w.layers, w.group
-    t_start = time.perf_counter()
-    rows = layers = 0
-    t_h = t_d = t_l = 0.0
     k = plan.k
-    while time.perf_counter() - t_start < budget_s and (rows < period or layers < L):
-        if rows < period:
-            r0, r1 = rows, min(period, rows + 128)
-            lg = f64(new["logits"][r0:r1])
-            t0 = time.perf_counter()
-            H = infokv.topk_entropy(lg, w.topk_entropy)
-            t_h += time.perf_counter() - t0
-            hf = f64(new["h_final"][r0:r1])
-            hl = [f64(new["h"][l][r0:r1]) for l in range(L)]
-            t0 = time.perf_counter()
-            Ds = [infokv.repr_distance(hl[l], hf, w.tau) for l in range(L)]
-            t_d += time.perf_counter() - t0
-            rows = r1
-        if layers < L:
-            lay = layers
-            q = f64(new["q_win"][lay])
-            Kf = f64(plan.K[plan.cur][lay])
-            Vb = plan.V[plan.cur][lay].cpu()
-            Vb = Vb.view(torch.int16).numpy().view(np.uint16) if Vb.dtype == torch.bfloat16 else Vb.numpy()
-            E = plan.E[plan.cur][lay].cpu().numpy().astype(np.float64)
-            Dn, Hn = np.resize(Ds[lay % len(Ds)], period), np.resize(H, period)
-            t0 = time.perf_counter()
-            for g in range(w.heads_kv):
-                infokv.recompress_period(q[g * G:(g + 1) * G], Kf[g:g + 1], Vb[g:g + 1],
-                                         E[g:g + 1, :k], Dn, Hn, w.alpha_fuse, k, w.window)
-            t_l += time.perf_counter() - t0
-            layers += 1
-    total = t_h * period / rows + t_d * period / rows + t_l * L / layers
-    sample = (f"oracle run for {time.perf_counter() - t_start:.1f} s: top-k entropy and "
-              f"representation distance on {rows} of {period} new token rows, re-compression of "
-              f"{layers} of {L} layers (all KV heads); each part scaled by rows or layers to the "
-              f"whole period")
-    return {"value": plan.cap / total, "unit": "tokens/s", "cores": cores, "cpu": cpu, "kind": "oracle",
-            "sample": sample, "sample_s": round(time.perf_counter() - t_start, 2),
-            "est_step_s": total}
+    t_start = time.perf_counter()
+    chunks = parallel.row_chunks(period, 128)
+    logits = _host(new["logits"])
+    hf, hl = _host(new["h_final"]), [_host(h) for h in new["h"]]
+    q = [_host(x) for x in new["q_win"]]
+    Kc = [_host(x) for x in plan.K[plan.cur]]
+    Vc = [_host(x) for x in plan.V[plan.cur]]
+    Ec = [x.cpu().numpy().astype(np.float64) for x in plan.E[plan.cur]]
+    t_copy = time.perf_counter() - t_start
+    deadline = time.perf_counter() + budget_s / 3
+
+    def ent(c):
+        return infokv.topk_entropy(_to_f64(logits[c[0]:c[1]]), w.topk_entropy)
+
+    Hs, rows_h, t_h = _rounds(ent, chunks, T, deadline)
+    deadline = time.perf_counter() + budget_s / 3
+
+    def dist(c):
+        b = _to_f64(hf[c[0]:c[1]])
+        return [infokv.repr_distance(_to_f64(hl[l][c[0]:c[1]]), b, w.tau) for l in range(L)]
+
+    Ds, rows_d, t_d = _rounds(dist, chunks, T, deadline)
+    H = np.resize(np.concatenate(Hs), period)
+    D = [np.resize(np.concatenate([c[l] for c in Ds]), period) for l in range(L)]
+    deadline = time.perf_counter() + budget_s / 3
+
+    def layer(l):
+        qf, Kf = _to_f64(q[l]), _to_f64(Kc[l])
+        for g in range(w.heads_kv):
+            infokv.recompress_period(qf[g * G:(g + 1) * G], Kf[g:g + 1], Vc[l][g:g + 1],
+                                     Ec[l][g:g + 1, :k], D[l], H, w.alpha_fuse, k, w.window)
+
+    _, layers, t_l = _rounds(layer, list(range(L)), T, deadline)
+    rh, rd = chunks[rows_h - 1][1], chunks[rows_d - 1][1]
+    total = t_h * period / rh + t_d * period / rd + t_l * L / layers
+    threads = {"topk_entropy": min(T, rows_h), "repr_distance": min(T, rows_d),
+               "recompression": min(T, layers)}
+    sample = (f"oracle on {T} host threads for {time.perf_counter() - t_start - t_copy:.1f} s: "
+              f"top-k entropy on {rh} and representation distance on {rd} of {period} new token "
+              f"rows, re-compression of {layers} of {L} layers (all KV heads); each leg's wall "
+              f"time scaled by rows or layers to the whole period")
+    return {"value": plan.cap / total, "unit": "tokens/s", "cores": max(threads.values()),
+            "threads": threads, "cpu": host_cpu(), "kind": "oracle", "sample": sample,
+            "sample_s": round(time.perf_counter() - t_start - t_copy, 2), "est_step_s": total}
 
 
 def main():
