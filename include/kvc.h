@@ -303,6 +303,28 @@ int kvc_decode_attn(const void* const* q, const void* const* K, const void* cons
                     float* lse_out, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Dropped-attention-mass monitor of a compacted cache ([RECAS] section 2.B,
+ * error-bounded compression: the formal bound ||o - o'||_2 <= 2 V_max delta,
+ * checked exactly at a full-attention probe step).  With lse_full and lse_kept
+ * the log normalisers of one decode query per head over the full cache and over
+ * the kept rows only (two kvc_decode_attn calls without a bias):
+ *   delta_out[l, h] = max(0, 1 - exp(lse_kept[l, h] - lse_full[l, h]))
+ *                     (the evicted tokens' share of the full softmax)
+ *   vmax_out[l, g]  = max over j of ||V[l][g, j, :]||_2 over the full cache
+ *   bound_out[l, h] = 2 * vmax_out[l, g(h)] * delta_out[l, h]
+ * With a merged, bias-compensated cache (SelKV) lse_kept is not the kept share
+ * and delta is not the dropped mass.
+ *   lse_kept, lse_full  device float32 [L, Hq].
+ *   V          host array of L device pointers, each [Hkv, n, d] of dtype (the
+ *              full cache).
+ *   delta_out, bound_out  device float32 [L, Hq];  vmax_out device float32 [L, Hkv].
+ *   n >= 1; 1 <= d <= 4096; Hq % Hkv == 0.
+ */
+int kvc_dropped_mass(const float* lse_kept, const float* lse_full, const void* const* V,
+                     int dtype, int L, int Hq, int Hkv, int64_t n, int d, float* delta_out,
+                     float* vmax_out, float* bound_out, void* stream);
+
+/*
  * Active-set scores of one decode step ([RECAS] section 2.C, dynamic sparse
  * decoding attention: a query-aware sparse score over the retained cache, whose
  * top K_t entries form the active set attended this step):

@@ -51,6 +51,8 @@ _SIGNATURES = {
     "kvc_decode_attn_active": ([_vp, _vp, _vp, _i32, _vp, _f32, _vp, _i64, _i32, _i32, _i32, _i64,
                                 _i32, _f32, _vp, _vp, _vp, _sz, _vp], _i32),
     "kvc_rope_reposition": ([_vp, _i32, _vp, _i64, _f64, _i32, _i32, _i64, _i32, _vp], _i32),
+    "kvc_dropped_mass": ([_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i64, _i32, _vp, _vp, _vp, _vp],
+                         _i32),
     "kvc_decode_attn_workspace_size": ([_i32, _i32, _i64, _i32], _sz),
     "kvc_decode_attn": ([_vp, _vp, _vp, _i32, _vp, _f32, _i32, _i32, _i32, _i64, _i32, _f32, _vp,
                          _vp, _vp, _sz, _vp], _i32),
@@ -396,3 +398,19 @@ def kvc_rope_reposition(K, pos_old, new_pos0: int, base: float, stream=None):
     _check("kvc_rope_reposition", lib().kvc_rope_reposition(
         kp, _dtype(K[0]), pp, new_pos0, base, L, Hkv, m, d, _stream(stream)))
     return K
+
+
+def kvc_dropped_mass(lse_kept: torch.Tensor, lse_full: torch.Tensor, V, delta_out: torch.Tensor,
+                     vmax_out: torch.Tensor, bound_out: torch.Tensor, stream=None):
+    """delta_out [L, Hq] = 1 - exp(lse_kept - lse_full) (clamped at 0), vmax_out [L, Hkv] =
+    largest value norm of the full cache V[l] [Hkv, n, d], bound_out = 2 * vmax * delta."""
+    L, Hq = lse_full.shape
+    Hkv, n, d = V[0].shape
+    if tuple(lse_kept.shape) != (L, Hq) or len(V) != L:
+        raise ValueError("lse_kept / lse_full must be [L, Hq] and V a list of L tensors")
+    vp, keep = _ptrs(V, V[0].dtype)
+    _check("kvc_dropped_mass", lib().kvc_dropped_mass(
+        _ptr(lse_kept, torch.float32), _ptr(lse_full, torch.float32), vp, _dtype(V[0]), L, Hq, Hkv,
+        n, d, _ptr(delta_out, torch.float32), _ptr(vmax_out, torch.float32),
+        _ptr(bound_out, torch.float32), _stream(stream)))
+    return delta_out, vmax_out, bound_out

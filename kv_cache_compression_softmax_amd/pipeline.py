@@ -120,6 +120,42 @@ class InfoKVPlan:
         mark("compact")
         return self
 
+    def probe(self, inp: dict, q, stream=None, mark=None):
+        """A full-attention probe step of [RECAS] section 2.B over the compacted
+        cache: decode one query per head (q[l] [Hq, d]) over the kept rows and
+        over the full cache, then the exact dropped mass delta [L, Hq], the
+        largest value norm V_max [L, Hkv] and the bound 2 * V_max * delta.
+        Returns a dict of the plan's own buffers (allocated on the first call,
+        overwritten by the next)."""
+        w = self.w
+        mark = mark or (lambda name: None)
+        if getattr(self, "_probe", None) is None:
+            L, Hq, Hkv, d, dev = w.layers, w.heads_q, w.heads_kv, w.head_dim, self.S.device
+            f32 = torch.float32
+            nbytes = B.kvc_decode_attn_workspace_size(L, Hq, w.n, d)
+            self._probe = {"o_kept": torch.empty(L, Hq, d, dtype=f32, device=dev),
+                           "lse_kept": torch.empty(L, Hq, dtype=f32, device=dev),
+                           "o_full": torch.empty(L, Hq, d, dtype=f32, device=dev),
+                           "lse_full": torch.empty(L, Hq, dtype=f32, device=dev),
+                           "delta": torch.empty(L, Hq, dtype=f32, device=dev),
+                           "vmax": torch.empty(L, Hkv, dtype=f32, device=dev),
+                           "bound": torch.empty(L, Hq, dtype=f32, device=dev),
+                           "ws": torch.empty(max(1, nbytes), dtype=torch.uint8, device=dev)}
+        p = self._probe
+        if len(set(self.k)) != 1:
+            raise ValueError("probe() needs the same budget in every layer (one compacted length)")
+        mark("start")
+        B.kvc_decode_attn(q, self.Kc, self.Vc, None, 0.0, self.scale, p["o_kept"], p["lse_kept"],
+                          ws=p["ws"], stream=stream)
+        mark("decode_kept")
+        B.kvc_decode_attn(q, inp["k"], inp["v"], None, 0.0, self.scale, p["o_full"], p["lse_full"],
+                          ws=p["ws"], stream=stream)
+        mark("decode_full")
+        B.kvc_dropped_mass(p["lse_kept"], p["lse_full"], inp["v"], p["delta"], p["vmax"], p["bound"],
+                           stream=stream)
+        mark("dropped_mass")
+        return p
+
 
 class InfoKVDecodePlan:
     """Compression repeated during decoding ([InfoKV] Technical detail: at
