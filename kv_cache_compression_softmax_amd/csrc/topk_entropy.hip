@@ -34,6 +34,12 @@ namespace kvc {
 namespace {
 
 constexpr int NT = 256;      // 4 waves = 4 rows per workgroup
+
+__device__ __forceinline__ int wave_sum_int(int v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
 constexpr int RESEL = 1536;  // list length that triggers a re-select (>= k rounded up)
 
 typedef short s16x2 __attribute__((ext_vector_type(2)));
@@ -340,23 +346,32 @@ topk_entropy_kernel(const T* __restrict__ logits, int64_t rows, int64_t vocab, i
   }
   if (!exact) select(true);
 
-  // entropy over the k held keys (float32, fixed reduction order)
+  // Entropy over the k held keys (float32, fixed reduction order).  With
+  // x = t - m <= 0 and Z = sum e^x:  H = ln Z + (1/Z) sum e^x (-x).  A row whose
+  // softmax is nearly one-hot has Z = 1 + S with S tiny, and a float32 Z keeps
+  // few digits of S: ln Z from it is off by ~6e-8 absolute, which was a 1.7e-3
+  // relative error at H = 1.2e-4.  So S is summed apart: the keys equal to m
+  // contribute exactly 1 each, one of them is the 1 of Z, and ln Z = log1p(S).
+  // Both parts of H are then sums of terms >= 0, accurate to a few ulp.
   float mloc = -INFINITY;
   for (int i = lane; i < k; i += 64) mloc = fmaxf(mloc, Tr<T>::value(Tr<T>::key(cand[i])));
   const float m = wave_max(mloc);
-  float zloc = 0.f;
-  for (int i = lane; i < k; i += 64) zloc += expf(Tr<T>::value(Tr<T>::key(cand[i])) - m);
-  const float Z = wave_sum(zloc);
-  const float lnZ = logf(Z), invZ = 1.0f / Z;
-  float hloc = 0.f;
+  float sloc = 0.f, hloc = 0.f;
+  int ties = 0;
   for (int i = lane; i < k; i += 64) {
     const float t = Tr<T>::value(Tr<T>::key(cand[i]));
-    const float e = expf(t - m);
-    // -p ln p, every term >= 0; p = 0 (a -inf logit held because fewer than k
-    // are finite, or an underflow) contributes its limit 0, not 0 * inf
-    if (e > 0.f) hloc += e * invZ * ((m - t) + lnZ);
+    if (t < m) {
+      const float e = expf(t - m);
+      sloc += e;
+      // e = 0 (a -inf logit held because fewer than k are finite, or an
+      // underflow) contributes its limit 0, not 0 * inf
+      if (e > 0.f) hloc += e * (m - t);
+    } else {
+      ++ties;
+    }
   }
-  const float h = wave_sum(hloc);
+  const float S = wave_sum(sloc) + (float)(wave_sum_int(ties) - 1);
+  const float h = log1pf(S) + wave_sum(hloc) / (1.0f + S);
   if (lane == 0) H[rowi] = m == -INFINITY ? NAN : h;   // no finite logit: no entropy
 }
 

@@ -60,6 +60,8 @@ ENTROPY_CASES = [
     (5, 1000, 1000, 256, torch.bfloat16, "normal4"),       # row shorter than one step
     (5, 700, 701, 100, torch.float32, "normal4"),          # the same in float32, odd pitch
     (6, 9000, 9000, 256, torch.bfloat16, "descending"),
+    (64, 128256, 128256, 256, torch.bfloat16, "onehot"),  # nearly one-hot: H from ~1e-6 to 1e-2
+    (32, 9000, 9000, 1000, torch.float32, "onehot"),
 ]
 
 
@@ -90,6 +92,14 @@ def entropy_input(rows, stride, kind, dtype, dev, seed):
         x = gen((rows, stride), seed, dev, torch.float32, 4.0)
         x[torch.rand((rows, stride), generator=g, device=dev) < 0.9] = -math.inf
         return x.to(dtype)
+    if kind == "onehot":     # one logit 10..24 above a N(0, 1) row: Z = 1 + S with S tiny
+        x = gen((rows, stride), seed, dev, torch.float32, 1.0)
+        g = torch.Generator(device=dev)
+        g.manual_seed(seed + 3)
+        col = torch.randint(0, stride, (rows, 1), generator=g, device=dev)
+        lift = 10.0 + 14.0 * torch.arange(rows, device=dev, dtype=torch.float32)[:, None] / rows
+        x.scatter_(1, col, x.gather(1, col) + lift)
+        return x.to(dtype)
     scale = 3.0 if kind == "normal3" else 4.0
     x = gen((rows, stride), seed, dev, torch.float32, scale)
     if kind == "spiked":
@@ -113,6 +123,10 @@ def test_topk_entropy(dev, case):
     got = H.cpu().numpy()
     if k == 1:
         assert np.all(got == 0)
+    elif kind == "onehot":
+        # no cancellation in ln Z: a few float32 ulp even where H is 1e-6
+        assert ref.min() < 1e-4
+        assert_rel(got, ref, 1e-4, what="H")
     else:
         assert_rel(got, ref, 1e-3, what="H")
     if kind == "flat":
@@ -384,6 +398,10 @@ SELKV_CASES = [
     (1, 4, 2, 2048, 32, 128, 40, 64),        # 40 kept: no search round, most buckets empty
     (1, 4, 2, 1000, 16, 64, 990, 64),        # nearly all kept: long kept runs, few merges
     (1, 8, 2, 3001, 32, 128, 1500, 32),      # bucket 32, ragged last bucket
+    # more than 8192 kept: the kept-list search takes rounds of 64 probes after the
+    # first round of 128 (as at 102400 tokens, 25% kept)
+    (1, 4, 1, 40960, 32, 128, 10240, 64),
+    (1, 8, 2, 49999, 32, 64, 25600, 64),
     (34, 4, 2, 300, 16, 64, 100, 32),        # more layers than one launch holds
 ]
 
