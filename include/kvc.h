@@ -113,6 +113,25 @@ int kvc_score_window_attn(const void* const* q_win, const void* const* k, int dt
                           void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * kvc_score_window_attn for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same computation and kernels, with the workspace taken from
+ * a fixed device scratch array of kvc_score_window_attn_noalloc_max_workspace()
+ * bytes (32 MiB) that each GPU the library runs on holds until the process
+ * ends.  Nothing is allocated or freed.  A shape whose
+ * kvc_score_window_attn_workspace_size() exceeds the scratch returns
+ * KVC_ERR_WORKSPACE before anything is enqueued (the Llama-shaped workloads
+ * need 1.4 MB at 16K tokens and 13.1 MB at 102400).  Every call on one GPU
+ * shares that GPU's scratch: calls that overlap on one GPU (other streams or
+ * threads) race and must be ordered by the caller.  Arguments otherwise as
+ * kvc_score_window_attn.
+ */
+size_t kvc_score_window_attn_noalloc_max_workspace(void);
+int kvc_score_window_attn_noalloc(const void* const* q_win, const void* const* k, int dtype,
+                                  int L, int Hq, int Hkv, int64_t n, int w, int d,
+                                  float scale, int per_query_head, float* A_out, void* stream);
+
+/*
  * Importance fusion ([InfoKV] Contributions, Method, Technical detail):
  *   E[l, i] = D[l, i] * H[i];  sigma[l, :] = softmax over the n tokens of E[l, :]
  *   S[l, g, i] = alpha_fuse * A[l, g, i] + (1 - alpha_fuse) * sigma[l, i]

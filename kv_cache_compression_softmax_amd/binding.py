@@ -32,6 +32,9 @@ _SIGNATURES = {
     "kvc_score_window_attn_workspace_size": ([_i32, _i32, _i32, _i64, _i32, _i32, _i32], _sz),
     "kvc_score_window_attn": ([_vp, _vp, _i32, _i32, _i32, _i32, _i64, _i32, _i32, _f32, _i32,
                                _vp, _vp, _sz, _vp], _i32),
+    "kvc_score_window_attn_noalloc_max_workspace": ([], _sz),
+    "kvc_score_window_attn_noalloc": ([_vp, _vp, _i32, _i32, _i32, _i32, _i64, _i32, _i32, _f32,
+                                       _i32, _vp, _vp], _i32),
     "kvc_fuse_scores_workspace_size": ([_i32, _i64], _sz),
     "kvc_fuse_scores": ([_vp, _vp, _vp, _i32, _i32, _i64, _f32, _vp, _vp, _vp, _sz, _vp], _i32),
     "kvc_uniform_budget": ([_f64, _i64, _i32, _c_i64p], _i32),
@@ -181,6 +184,25 @@ def kvc_score_window_attn(q_win, k, scale: float, per_query_head: bool, A_out: t
     _check("kvc_score_window_attn", lib().kvc_score_window_attn(
         qp, kp, dt, L, Hq, Hkv, n, w, d, scale, int(per_query_head), _ptr(A_out, torch.float32),
         _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+    return A_out
+
+
+def kvc_score_window_attn_noalloc_max_workspace() -> int:
+    return lib().kvc_score_window_attn_noalloc_max_workspace()
+
+
+def kvc_score_window_attn_noalloc(q_win, k, scale: float, per_query_head: bool, A_out: torch.Tensor,
+                                  stream=None):
+    """kvc_score_window_attn with the library's fixed device scratch as its
+    workspace: nothing is allocated (calls that overlap on one GPU race)."""
+    L = len(k)
+    Hq, w, d = q_win[0].shape
+    Hkv, n, _ = k[0].shape
+    qp, kq = _ptrs(q_win, k[0].dtype)
+    kp, kk = _ptrs(k, k[0].dtype)
+    _check("kvc_score_window_attn_noalloc", lib().kvc_score_window_attn_noalloc(
+        qp, kp, _dtype(k[0]), L, Hq, Hkv, n, w, d, scale, int(per_query_head),
+        _ptr(A_out, torch.float32), _stream(stream)))
     return A_out
 
 

@@ -28,6 +28,7 @@
 // plain K stream).  Q is staged once per workgroup in LDS in fragment order, one
 // ds_read_b128 per fragment.
 #include <cmath>
+#include <mutex>
 #include <type_traits>
 
 #include "common.h"
@@ -684,4 +685,66 @@ extern "C" int kvc_score_window_attn(const void* const* q_win, const void* const
     }
   }
   return launch_status("kvc_score_window_attn");
+}
+
+// ------------------------------------------------------------------ no-alloc variant
+// For callers that cannot allocate device memory (code under HIP graph capture,
+// tight serving loops, harnesses that forbid it): the workspace lives in a
+// file-scope device array that every GPU the library runs on holds until the
+// process ends.  Host code never passes the array's name to a kernel (on the
+// host it is only a stand-in): its device address is taken once per device
+// with hipGetSymbolAddress, with that device current, and that address is what
+// the kernels receive.  Every call on one GPU shares that GPU's copy, so calls
+// that overlap on one GPU (different streams, or threads) race.  The workspace
+// needs no initial contents, so nothing is cleared.
+namespace {
+
+constexpr size_t kNoAllocScratchBytes = size_t(32) << 20;     // 32 MiB per device
+constexpr int kMaxDevices = 64;
+
+__device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of this device's scratch array (looked up on first use).
+int scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return KVC_FAIL(KVC_ERR_HIP, "kvc_score_window_attn_noalloc: hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return KVC_FAIL(KVC_ERR_HIP, "kvc_score_window_attn_noalloc: device %d beyond %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return KVC_FAIL(KVC_ERR_HIP, "kvc_score_window_attn_noalloc: hipGetSymbolAddress: %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return KVC_OK;
+}
+
+}  // namespace
+
+extern "C" size_t kvc_score_window_attn_noalloc_max_workspace(void) { return kNoAllocScratchBytes; }
+
+extern "C" int kvc_score_window_attn_noalloc(const void* const* q_win, const void* const* k, int dtype,
+                                             int L, int Hq, int Hkv, int64_t n, int w, int d,
+                                             float scale, int per_query_head, float* A_out,
+                                             void* stream) {
+  clear_error();
+  // size check first, before the device is touched
+  const size_t need = kvc_score_window_attn_workspace_size(L, Hq, Hkv, n, w, d, dtype);
+  if (need > kNoAllocScratchBytes)
+    return KVC_FAIL(KVC_ERR_WORKSPACE,
+                    "kvc_score_window_attn_noalloc: this shape needs %zu bytes of workspace, more than "
+                    "the %zu-byte device scratch (use kvc_score_window_attn with a workspace)",
+                    need, kNoAllocScratchBytes);
+  void* ws = nullptr;
+  const int st = scratch_address(&ws);
+  if (st != KVC_OK) return st;
+  return kvc_score_window_attn(q_win, k, dtype, L, Hq, Hkv, n, w, d, scale, per_query_head, A_out,
+                               ws, kNoAllocScratchBytes, stream);
 }

@@ -162,3 +162,21 @@ def test_adaptive_budget_rejects_nonpositive():
     from kv_cache_compression_softmax_amd import binding
     with pytest.raises(binding.KvcError):
         binding.kvc_adaptive_budget([1.0, 0.0], 100, 0, 1000)
+
+
+def test_noalloc_window_attention_rejects_oversize_before_launch(lib):
+    """The no-alloc window attention checks its workspace need against the fixed
+    scratch before it touches the device."""
+    arr = (ctypes.c_void_p * 1)(0x1000)
+    pa = ctypes.cast(arr, ctypes.c_void_p)
+    cap = lib.kvc_score_window_attn_noalloc_max_workspace()
+    assert cap == 32 << 20
+    # 32 layers of 32/8 heads at 2^23 tokens need far more than the scratch
+    need = lib.kvc_score_window_attn_workspace_size(32, 32, 8, 1 << 23, 32, 128, 1)
+    assert need > cap
+    assert lib.kvc_score_window_attn_noalloc(pa, pa, 1, 32, 32, 8, 1 << 23, 32, 128, ctypes.c_float(0.1), 0,
+                                             ctypes.c_void_p(0x1000), None) == -3
+    assert "scratch" in err(lib)
+    # the Llama-shaped workloads fit
+    for L, Hq, n in [(28, 24, 16384), (32, 32, 32768), (32, 32, 65536), (32, 32, 102400)]:
+        assert lib.kvc_score_window_attn_workspace_size(L, Hq, 8, n, 32, 128, 1) <= cap
