@@ -17,9 +17,14 @@
 // they are 16-byte loads, since a lone workgroup per CU is bound by the bytes it
 // has in flight, not by the histogram work.  When [0, n - w) fits in LDS beside
 // the histograms, the first pass copies it there and the other four passes read
-// it from LDS, so the row comes from memory once; otherwise every pass re-reads
-// it.  The histograms are per wave, with wave-aggregated increments where lanes
-// crowd into one bin.
+// it from LDS, so the row comes from memory once.  A longer row of up to
+// REGV * 512 vectors of 4 scores (102400 scores) is held in registers instead,
+// by a 512-thread workgroup: thread t keeps vectors t, t + 512, ..., which is
+// also the vector it needs in
+// each chunk of the ordered pass, so again the row is read once (all of a
+// thread's loads in flight together).  Longer rows still are re-read by every
+// pass.  The histograms are per wave, with wave-aggregated increments where
+// lanes crowd into one bin.
 #include "common.h"
 
 namespace kvc {
@@ -29,6 +34,8 @@ constexpr int NT = 1024;
 constexpr int NW = NT / 64;     // waves
 constexpr int EPT = 4;          // consecutive elements per thread in the output pass
 constexpr int HU = 8;           // elements per thread loaded together in a histogram pass
+constexpr int NTR = 768;        // threads of the register path (3 waves per SIMD)
+constexpr int REGV = 34;        // 16-byte vectors per thread held in registers (REG path)
 
 // Adds 1 to hist[bin] for every active lane with valid set.  When many lanes share
 // the first valid lane's bin (scores spread over few binades make the high digits
@@ -53,13 +60,16 @@ __device__ __forceinline__ void hist_add(int* hist, bool valid, int bin) {
 }
 
 // VEC: 16-byte loads (n % 4 == 0, S 16-byte aligned).  CACHE: [0, n - w) is held in
-// dynamic LDS, as float4, from the first pass on.
-template <bool VEC, bool CACHE>
-__global__ void __launch_bounds__(NT)
+// dynamic LDS, as float4, from the first pass on.  REG (with VEC): [0, n - w) is
+// held in registers, REGV vectors per thread.
+template <bool VEC, bool CACHE, bool REG = false>
+__global__ void __launch_bounds__(REG ? NTR : NT)
 select_kernel(const float* __restrict__ S, int Hkv, int64_t n, I64s kk, int w, MutPtrs idx) {
+  constexpr int NTB = REG ? NTR : NT;             // threads of this variant
+  constexpr int NWB = NTB / 64;
   extern __shared__ float4 rc[];
-  __shared__ int hist[NW][256];                   // one histogram per wave
-  __shared__ int scan[NT / 64];
+  __shared__ int hist[NWB][256];                   // one histogram per wave
+  __shared__ int scan[NTB / 64];
   __shared__ int pick[2];
   const int tid = threadIdx.x;
   const int wv = tid / 64;
@@ -68,14 +78,28 @@ select_kernel(const float* __restrict__ S, int Hkv, int64_t n, I64s kk, int w, M
   const float* row = S + ((int64_t)l * Hkv + g) * n;
   int32_t* out = (int32_t*)idx.p[l] + (int64_t)g * k;
   if (k <= w) {                                   // the window alone overflows the budget
-    for (int64_t j = tid; j < k; j += NT) out[j] = (int32_t)(n - k + j);
+    for (int64_t j = tid; j < k; j += NTB) out[j] = (int32_t)(n - k + j);
     return;
   }
   const int64_t nb = n - w, need = k - w;
-  for (int64_t j = tid; j < w; j += NT) out[need + j] = (int32_t)(nb + j);
+  for (int64_t j = tid; j < w; j += NTB) out[need + j] = (int32_t)(nb + j);
   if (need >= nb) {                               // everything is kept
-    for (int64_t j = tid; j < nb; j += NT) out[j] = (int32_t)j;
+    for (int64_t j = tid; j < nb; j += NTB) out[j] = (int32_t)j;
     return;
+  }
+  // REG: the thread's vectors t + r * NTB, loaded once, all in flight together
+  // (vectors past the row repeat its last one and are never counted)
+  // (held as order-preserving keys, converted once)
+  uint4 rk[REG ? REGV : 1];
+  if constexpr (REG) {
+    const int64_t nv = (nb + 3) / 4;
+    const float4* row4 = reinterpret_cast<const float4*>(row);
+    float4 t[REG ? REGV : 1];
+#pragma unroll
+    for (int r = 0; r < REGV; ++r) t[r] = row4[min((int64_t)r * NTB + tid, nv - 1)];
+#pragma unroll
+    for (int r = 0; r < REGV; ++r)
+      rk[r] = make_uint4(f32_key(t[r].x), f32_key(t[r].y), f32_key(t[r].z), f32_key(t[r].w));
   }
   // ---- 1. radix select of the need-th largest key
   uint32_t prefix = 0;
@@ -84,34 +108,45 @@ select_kernel(const float* __restrict__ S, int Hkv, int64_t n, I64s kk, int w, M
   for (int p = 3; p >= 0; --p) {
     const int shift = 8 * p;
     const uint32_t hi_mask = (p == 3) ? 0u : (uint32_t)(~0ull << (shift + 8));
-    for (int i = tid; i < NW * 256; i += NT) (&hist[0][0])[i] = 0;
+    for (int i = tid; i < NWB * 256; i += NTB) (&hist[0][0])[i] = 0;
     __syncthreads();
     auto count = [&](uint32_t key, bool in) __attribute__((always_inline)) {
       hist_add(hist[wv], in && (key & hi_mask) == (prefix & hi_mask), (int)((key >> shift) & 255));
     };
-    if constexpr (VEC) {
+    if constexpr (REG) {
+      // element 4 (r NTB + tid) + q is in the row iff 4 r NTB + q < lim: a
+      // constant against one register
+      const int lim = (int)nb - 4 * tid;
+#pragma unroll
+      for (int r = 0; r < REGV; ++r) {
+        count(rk[r].x, 4 * r * NTB + 0 < lim);
+        count(rk[r].y, 4 * r * NTB + 1 < lim);
+        count(rk[r].z, 4 * r * NTB + 2 < lim);
+        count(rk[r].w, 4 * r * NTB + 3 < lim);
+      }
+    } else if constexpr (VEC) {
       // vectors [0, nv) of 4 scores; the last may reach past nb but not past n
       const int64_t nv = (nb + 3) / 4;
       const float4* row4 = reinterpret_cast<const float4*>(row);
       const bool lds = CACHE && p != 3;
 #pragma unroll 1
-      for (int64_t i0 = 0; i0 < nv; i0 += (int64_t)NT * HU) {
+      for (int64_t i0 = 0; i0 < nv; i0 += (int64_t)NTB * HU) {
         float4 v[HU];                             // HU 16-byte loads in flight per thread
         if (lds) {
 #pragma unroll
-          for (int u = 0; u < HU; ++u) v[u] = rc[min(i0 + (int64_t)u * NT + tid, nv - 1)];
+          for (int u = 0; u < HU; ++u) v[u] = rc[min(i0 + (int64_t)u * NTB + tid, nv - 1)];
         } else {
 #pragma unroll
-          for (int u = 0; u < HU; ++u) v[u] = row4[min(i0 + (int64_t)u * NT + tid, nv - 1)];
+          for (int u = 0; u < HU; ++u) v[u] = row4[min(i0 + (int64_t)u * NTB + tid, nv - 1)];
           if (CACHE) {
 #pragma unroll
             for (int u = 0; u < HU; ++u)
-              if (i0 + (int64_t)u * NT + tid < nv) rc[i0 + (int64_t)u * NT + tid] = v[u];
+              if (i0 + (int64_t)u * NTB + tid < nv) rc[i0 + (int64_t)u * NTB + tid] = v[u];
           }
         }
 #pragma unroll
         for (int u = 0; u < HU; ++u) {
-          const int64_t e0 = 4 * (i0 + (int64_t)u * NT + tid);
+          const int64_t e0 = 4 * (i0 + (int64_t)u * NTB + tid);
           count(f32_key(v[u].x), e0 < nb);
           count(f32_key(v[u].y), e0 + 1 < nb);
           count(f32_key(v[u].z), e0 + 2 < nb);
@@ -120,22 +155,22 @@ select_kernel(const float* __restrict__ S, int Hkv, int64_t n, I64s kk, int w, M
       }
     } else {
 #pragma unroll 1
-      for (int64_t i0 = 0; i0 < nb; i0 += (int64_t)NT * HU) {
+      for (int64_t i0 = 0; i0 < nb; i0 += (int64_t)NTB * HU) {
         float v[HU];                              // HU loads in flight per thread
 #pragma unroll
-        for (int u = 0; u < HU; ++u) v[u] = row[min(i0 + (int64_t)u * NT + tid, nb - 1)];
+        for (int u = 0; u < HU; ++u) v[u] = row[min(i0 + (int64_t)u * NTB + tid, nb - 1)];
 #pragma unroll
-        for (int u = 0; u < HU; ++u) count(f32_key(v[u]), i0 + (int64_t)u * NT + tid < nb);
+        for (int u = 0; u < HU; ++u) count(f32_key(v[u]), i0 + (int64_t)u * NTB + tid < nb);
       }
     }
     __syncthreads();
     int c = 0;
     if (tid < 256) {
 #pragma unroll
-      for (int x = 0; x < NW; ++x) c += hist[x][255 - tid];
+      for (int x = 0; x < NWB; ++x) c += hist[x][255 - tid];
     }
     int tot;
-    const int incl = block_exclusive_scan<NT>(c, scan, &tot) + c;
+    const int incl = block_exclusive_scan<NTB>(c, scan, &tot) + c;
     if (tid < 256 && incl >= rem && incl - c < rem) { pick[0] = 255 - tid; pick[1] = incl - c; }
     __syncthreads();
     prefix |= (uint32_t)pick[0] << shift;
@@ -161,9 +196,46 @@ select_kernel(const float* __restrict__ S, int Hkv, int64_t n, I64s kk, int w, M
       for (int e = 0; e < EPT; ++e) v[e] = row[min(i0 + e, nb - 1)];
     }
   };
+  if constexpr (REG) {
+    // chunk r of the ordered pass is vector r * NTB + tid of this thread: registers
+#pragma unroll
+    for (int r = 0; r < REGV; ++r) {
+      // 32-bit index arithmetic: n < 2^31
+      if (r * NTB * EPT >= (int)nb) break;        // uniform
+      const int i0 = r * NTB * EPT + tid * EPT;
+      const int lim = (int)nb - 4 * tid;
+      const uint32_t k4[EPT] = {rk[r].x, rk[r].y, rk[r].z, rk[r].w};
+      uint32_t gt = 0, eq = 0;
+#pragma unroll
+      for (int e = 0; e < EPT; ++e) {
+        const uint32_t key = k4[e];
+        const bool in = 4 * r * NTB + e < lim;
+        gt |= (uint32_t)(in && key > T) << e;
+        eq |= (uint32_t)(in && key == T) << e;
+      }
+      const int packed = __builtin_popcount(gt) | (__builtin_popcount(eq) << 16);
+      int tot;
+      const int ex = block_exclusive_scan<NTB>(packed, scan, &tot);
+      int gtb = (int)run_gt + (ex & 0xffff), eqb = (int)run_eq + (ex >> 16);
+      const int teq = (int)take_eq;
+#pragma unroll
+      for (int e = 0; e < EPT; ++e) {
+        if (gt & (1u << e)) {
+          out[gtb + min(eqb, teq)] = i0 + e;
+          ++gtb;
+        } else if (eq & (1u << e)) {
+          if (eqb < teq) out[gtb + eqb] = i0 + e;
+          ++eqb;
+        }
+      }
+      run_gt += tot & 0xffff;
+      run_eq += tot >> 16;
+    }
+    return;
+  }
   fetch(0, cur);
 #pragma unroll 1
-  for (int64_t c0 = 0; c0 < nb; c0 += (int64_t)NT * EPT) {
+  for (int64_t c0 = 0; c0 < nb; c0 += (int64_t)NTB * EPT) {
     const int64_t i0 = c0 + (int64_t)tid * EPT;
     uint32_t gt = 0, eq = 0;
 #pragma unroll
@@ -173,10 +245,10 @@ select_kernel(const float* __restrict__ S, int Hkv, int64_t n, I64s kk, int w, M
       gt |= (uint32_t)(in && key > T) << e;
       eq |= (uint32_t)(in && key == T) << e;
     }
-    fetch(min(c0 + (int64_t)NT * EPT, nb - 1), cur);
+    fetch(min(c0 + (int64_t)NTB * EPT, nb - 1), cur);
     const int packed = __builtin_popcount(gt) | (__builtin_popcount(eq) << 16);
     int tot;
-    const int ex = block_exclusive_scan<NT>(packed, scan, &tot);
+    const int ex = block_exclusive_scan<NTB>(packed, scan, &tot);
     int64_t gtb = run_gt + (ex & 0xffff), eqb = run_eq + (ex >> 16);
 #pragma unroll
     for (int e = 0; e < EPT; ++e) {
@@ -226,6 +298,8 @@ extern "C" int kvc_select_topk(const float* S, int L, int Hkv, int64_t n, const 
                 hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)cache) == hipSuccess;
     if (!use_cache) (void)hipGetLastError();      // a refused query only selects the other path
   }
+  // a row too long for LDS but within REGV vectors per thread stays in registers
+  const bool use_reg = vec && !use_cache && n > w && (n - w + 3) / 4 <= (int64_t)REGV * NTR;
   for (int l0 = 0; l0 < L; l0 += kLayersPerLaunch) {
     const int lc = min(kLayersPerLaunch, L - l0);
     I64s kk{};
@@ -234,6 +308,7 @@ extern "C" int kvc_select_topk(const float* S, int L, int Hkv, int64_t n, const 
     const dim3 grid((unsigned)(lc * Hkv));
     const float* Sl = S + (int64_t)l0 * Hkv * n;
     if (use_cache) hipLaunchKernelGGL((select_kernel<true, true>), grid, dim3(NT), cache, s, Sl, Hkv, n, kk, w, ip);
+    else if (use_reg) hipLaunchKernelGGL((select_kernel<true, false, true>), grid, dim3(NTR), 0, s, Sl, Hkv, n, kk, w, ip);
     else if (vec) hipLaunchKernelGGL((select_kernel<true, false>), grid, dim3(NT), 0, s, Sl, Hkv, n, kk, w, ip);
     else hipLaunchKernelGGL((select_kernel<false, false>), grid, dim3(NT), 0, s, Sl, Hkv, n, kk, w, ip);
   }
