@@ -245,10 +245,13 @@ def cpu_baseline(w, inp, budget_s=15.0):
             selkv.selkv_layer(_to_f64(qb[l]), _to_f64(kb[l]), _to_f64(vb[l]),
                               int(w.keep_fraction * n), w.window, w.bucket)
 
-        _, layers, t_l = _rounds(layer, list(range(L)), T, deadline)
+        # rounds of at most 4 layers: the merge's Python loop holds the
+        # interpreter lock, so a wider round mostly adds wall time per round
+        TS = min(T, 4)
+        _, layers, t_l = _rounds(layer, list(range(L)), TS, deadline)
         total = t_l * L / layers
-        threads = {"selkv_layer": min(T, layers)}
-        sample = (f"oracle on {T} host threads for {time.perf_counter() - t_start - t_copy:.1f} s: "
+        threads = {"selkv_layer": min(TS, layers)}
+        sample = (f"oracle on {TS} host threads for {time.perf_counter() - t_start - t_copy:.1f} s: "
                   f"the SelKV layer (attention, union, select, route, gate, merge) on all {n} "
                   f"tokens of {layers} of {L} layers, one layer per thread, scaled by layers to "
                   f"the whole step (route and merge loop in Python, which holds the interpreter "
