@@ -34,8 +34,8 @@ constexpr int NT = 1024;
 constexpr int NW = NT / 64;     // waves
 constexpr int EPT = 4;          // consecutive elements per thread in the output pass
 constexpr int HU = 8;           // elements per thread loaded together in a histogram pass
-constexpr int NTR = 768;        // threads of the register path (3 waves per SIMD)
-constexpr int REGV = 34;        // 16-byte vectors per thread held in registers (REG path)
+constexpr int NTR = 512;        // threads of the register path (2 waves per SIMD)
+constexpr int REGV = 50;        // 16-byte vectors per thread held in registers (register path)
 
 // Adds 1 to hist[bin] for every active lane with valid set.  When many lanes share
 // the first valid lane's bin (scores spread over few binades make the high digits
@@ -60,12 +60,11 @@ __device__ __forceinline__ void hist_add(int* hist, bool valid, int bin) {
 }
 
 // VEC: 16-byte loads (n % 4 == 0, S 16-byte aligned).  CACHE: [0, n - w) is held in
-// dynamic LDS, as float4, from the first pass on.  REG (with VEC): [0, n - w) is
-// held in registers, REGV vectors per thread.
-template <bool VEC, bool CACHE, bool REG = false>
-__global__ void __launch_bounds__(REG ? NTR : NT)
+// dynamic LDS, as float4, from the first pass on.
+template <bool VEC, bool CACHE>
+__global__ void __launch_bounds__(NT)
 select_kernel(const float* __restrict__ S, int Hkv, int64_t n, I64s kk, int w, MutPtrs idx) {
-  constexpr int NTB = REG ? NTR : NT;             // threads of this variant
+  constexpr int NTB = NT;
   constexpr int NWB = NTB / 64;
   extern __shared__ float4 rc[];
   __shared__ int hist[NWB][256];                   // one histogram per wave
@@ -87,20 +86,6 @@ select_kernel(const float* __restrict__ S, int Hkv, int64_t n, I64s kk, int w, M
     for (int64_t j = tid; j < nb; j += NTB) out[j] = (int32_t)j;
     return;
   }
-  // REG: the thread's vectors t + r * NTB, loaded once, all in flight together
-  // (vectors past the row repeat its last one and are never counted)
-  // (held as order-preserving keys, converted once)
-  uint4 rk[REG ? REGV : 1];
-  if constexpr (REG) {
-    const int64_t nv = (nb + 3) / 4;
-    const float4* row4 = reinterpret_cast<const float4*>(row);
-    float4 t[REG ? REGV : 1];
-#pragma unroll
-    for (int r = 0; r < REGV; ++r) t[r] = row4[min((int64_t)r * NTB + tid, nv - 1)];
-#pragma unroll
-    for (int r = 0; r < REGV; ++r)
-      rk[r] = make_uint4(f32_key(t[r].x), f32_key(t[r].y), f32_key(t[r].z), f32_key(t[r].w));
-  }
   // ---- 1. radix select of the need-th largest key
   uint32_t prefix = 0;
   int64_t above = 0, rem = need;
@@ -113,18 +98,7 @@ select_kernel(const float* __restrict__ S, int Hkv, int64_t n, I64s kk, int w, M
     auto count = [&](uint32_t key, bool in) __attribute__((always_inline)) {
       hist_add(hist[wv], in && (key & hi_mask) == (prefix & hi_mask), (int)((key >> shift) & 255));
     };
-    if constexpr (REG) {
-      // element 4 (r NTB + tid) + q is in the row iff 4 r NTB + q < lim: a
-      // constant against one register
-      const int lim = (int)nb - 4 * tid;
-#pragma unroll
-      for (int r = 0; r < REGV; ++r) {
-        count(rk[r].x, 4 * r * NTB + 0 < lim);
-        count(rk[r].y, 4 * r * NTB + 1 < lim);
-        count(rk[r].z, 4 * r * NTB + 2 < lim);
-        count(rk[r].w, 4 * r * NTB + 3 < lim);
-      }
-    } else if constexpr (VEC) {
+    if constexpr (VEC) {
       // vectors [0, nv) of 4 scores; the last may reach past nb but not past n
       const int64_t nv = (nb + 3) / 4;
       const float4* row4 = reinterpret_cast<const float4*>(row);
@@ -196,43 +170,6 @@ select_kernel(const float* __restrict__ S, int Hkv, int64_t n, I64s kk, int w, M
       for (int e = 0; e < EPT; ++e) v[e] = row[min(i0 + e, nb - 1)];
     }
   };
-  if constexpr (REG) {
-    // chunk r of the ordered pass is vector r * NTB + tid of this thread: registers
-#pragma unroll
-    for (int r = 0; r < REGV; ++r) {
-      // 32-bit index arithmetic: n < 2^31
-      if (r * NTB * EPT >= (int)nb) break;        // uniform
-      const int i0 = r * NTB * EPT + tid * EPT;
-      const int lim = (int)nb - 4 * tid;
-      const uint32_t k4[EPT] = {rk[r].x, rk[r].y, rk[r].z, rk[r].w};
-      uint32_t gt = 0, eq = 0;
-#pragma unroll
-      for (int e = 0; e < EPT; ++e) {
-        const uint32_t key = k4[e];
-        const bool in = 4 * r * NTB + e < lim;
-        gt |= (uint32_t)(in && key > T) << e;
-        eq |= (uint32_t)(in && key == T) << e;
-      }
-      const int packed = __builtin_popcount(gt) | (__builtin_popcount(eq) << 16);
-      int tot;
-      const int ex = block_exclusive_scan<NTB>(packed, scan, &tot);
-      int gtb = (int)run_gt + (ex & 0xffff), eqb = (int)run_eq + (ex >> 16);
-      const int teq = (int)take_eq;
-#pragma unroll
-      for (int e = 0; e < EPT; ++e) {
-        if (gt & (1u << e)) {
-          out[gtb + min(eqb, teq)] = i0 + e;
-          ++gtb;
-        } else if (eq & (1u << e)) {
-          if (eqb < teq) out[gtb + eqb] = i0 + e;
-          ++eqb;
-        }
-      }
-      run_gt += tot & 0xffff;
-      run_eq += tot >> 16;
-    }
-    return;
-  }
   fetch(0, cur);
 #pragma unroll 1
   for (int64_t c0 = 0; c0 < nb; c0 += (int64_t)NTB * EPT) {
@@ -262,6 +199,276 @@ select_kernel(const float* __restrict__ S, int Hkv, int64_t n, I64s kk, int w, M
     }
     run_gt += tot & 0xffff;
     run_eq += tot >> 16;
+  }
+}
+
+// ---------------------------------------------------------------- register path
+// A row of up to REGV * NTR vectors of 4 scores (102400 scores) is held in
+// registers, as order-preserving keys, by a workgroup of NTR threads: thread t
+// keeps vectors t, t + NTR, ..., all loads in flight together, so the row is read
+// once.
+//   1. The row's smallest and largest keys bound the search.  Each pass cuts
+//      the current key range [lo, lo + 2^sp) into at most 256 bins of width
+//      2^(sp-8), so scores spread over a few binades fill many bins (digits of
+//      the raw key would put a whole binade into one or two).  The bin holding
+//      the need-th largest key becomes the next range; keys outside the range
+//      were counted by earlier passes and are not counted again.
+//   2. After the first pass the keys of the chosen bin (when at most CAND) are
+//      copied to an LDS list, and the remaining passes read the list only.
+//   3. Ordered output: chunk r of the row is vector r * NTR + t of thread t.
+//      Per chunk, each wave's prefix counts come from ballots of the bit
+//      planes of the per-thread counts (0..4); the chunk and wave offsets come
+//      from one table in LDS, so the whole output takes two barriers.
+constexpr int NWR = NTR / 64;   // waves of the register path
+constexpr int CAND = 8192;      // candidate keys copied to LDS after the first pass
+
+// Exclusive prefix of v (0..7) over the wave's lanes, and the wave total.
+__device__ __forceinline__ int lane_prefix_small(int v, int& total) {
+  int pre = 0, tot = 0;
+#pragma unroll
+  for (int j = 0; j < 3; ++j) {
+    const uint64_t b = __ballot((v >> j) & 1);
+    pre += (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(b >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0u)) << j;
+    tot += __builtin_popcountll(b) << j;
+  }
+  total = tot;
+  return pre;
+}
+
+__global__ void __launch_bounds__(NTR)
+select_reg_kernel(const float* __restrict__ S, int Hkv, int64_t n, I64s kk, int w, MutPtrs idx) {
+  __shared__ int hist[NWR][256];                   // one histogram per wave
+  __shared__ uint32_t cand[CAND];
+  __shared__ uint32_t red[2][NWR];
+  __shared__ int wtot[REGV][NWR];                  // per chunk and wave: gt | eq << 16
+  __shared__ int wpre[REGV][NWR];                  // exclusive prefix over waves, packed
+  __shared__ int cbase[REGV][2];                   // exclusive prefix over chunks (gt, eq)
+  __shared__ int scan[NWR];
+  __shared__ int pick[3];
+  __shared__ int wcnt[NWR];                        // candidates of each wave's list segment
+  __shared__ int flag[2];                          // crowded bins seen; a list segment overflowed
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid / 64;
+  const int l = blockIdx.x / Hkv, g = blockIdx.x % Hkv;
+  const int64_t k = kk.v[l];
+  const float* row = S + ((int64_t)l * Hkv + g) * n;
+  int32_t* out = (int32_t*)idx.p[l] + (int64_t)g * k;
+  if (k <= w) {                                   // the window alone overflows the budget
+    for (int64_t j = tid; j < k; j += NTR) out[j] = (int32_t)(n - k + j);
+    return;
+  }
+  const int nb = (int)(n - w), need = (int)(k - w);  // n < 2^31
+  for (int j = tid; j < w; j += NTR) out[need + j] = nb + j;
+  if (need >= nb) {                               // everything is kept
+    for (int j = tid; j < nb; j += NTR) out[j] = j;
+    return;
+  }
+  // the thread's vectors t + r NTR, loaded once (vectors past the row repeat its
+  // last one and are never counted); element 4 (r NTR + t) + e is in the row iff
+  // 4 r NTR + e < lim
+  uint4 rk[REGV];
+  const int lim = nb - 4 * tid;
+  uint32_t kmin = ~0u, kmax = 0u;                 // the row's key range, formed as the keys arrive
+  {
+    const int nv = (nb + 3) / 4;
+    const float4* row4 = reinterpret_cast<const float4*>(row);
+    float4 t[REGV];
+#pragma unroll
+    for (int r = 0; r < REGV; ++r) t[r] = row4[min(r * NTR + tid, nv - 1)];
+#pragma unroll
+    for (int r = 0; r < REGV; ++r) {
+      rk[r] = make_uint4(f32_key(t[r].x), f32_key(t[r].y), f32_key(t[r].z), f32_key(t[r].w));
+      const uint32_t k4[4] = {rk[r].x, rk[r].y, rk[r].z, rk[r].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (4 * r * NTR + e < lim) { kmin = min(kmin, k4[e]); kmax = max(kmax, k4[e]); }
+    }
+  }
+  // f(key, in the row) for every held key.  The limit is made opaque per call
+  // so that the 136 row-membership masks are formed where they are used, not
+  // hoisted out of the pass loop and held in scalar registers across it.
+  auto each = [&](auto&& f) __attribute__((always_inline)) {
+    int lm = lim;
+    asm volatile("" : "+v"(lm));
+#pragma unroll
+    for (int r = 0; r < REGV; ++r) {
+      f(rk[r].x, 4 * r * NTR + 0 < lm);
+      f(rk[r].y, 4 * r * NTR + 1 < lm);
+      f(rk[r].z, 4 * r * NTR + 2 < lm);
+      f(rk[r].w, 4 * r * NTR + 3 < lm);
+    }
+  };
+  // ---- 1. the row's key range
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o, 64));
+    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o, 64));
+  }
+  if (lane == 0) { red[0][wv] = kmin; red[1][wv] = kmax; }
+  __syncthreads();
+#pragma unroll
+  for (int x = 0; x < NWR; ++x) { kmin = min(kmin, red[0][x]); kmax = max(kmax, red[1][x]); }
+  // ---- 2. descent over the range: T = the need-th largest key, above = keys > T
+  uint32_t lo = kmin;
+  int above = 0, rem = need;
+  if (kmax != kmin) {
+    int sp = 32 - __builtin_clz(kmax - kmin);   // the range is [lo, lo + 2^sp)
+    bool list = false;
+#pragma unroll 1
+    for (;;) {
+      const int s = sp > 8 ? sp - 8 : 0;          // bin width 2^s: at most 256 bins
+      for (int i = tid; i < NWR * 256; i += NTR) (&hist[0][0])[i] = 0;
+      if (tid == 0) flag[0] = 0;
+      __syncthreads();
+      // keys in [lo, lo + 2^sp): bin (key - lo) >> s
+      auto bin_of = [&](uint32_t key, bool in, bool& valid) __attribute__((always_inline)) {
+        const uint32_t d = key - lo;
+        valid = in && key >= lo && ((uint64_t)d >> sp) == 0;
+        return (int)((d >> s) & 255u);
+      };
+      auto count_agg = [&](uint32_t key, bool in) __attribute__((always_inline)) {
+        bool v;
+        const int b = bin_of(key, in, v);
+        hist_add(hist[wv], v, b);
+      };
+      if (list) {
+        for (int i = tid; i < CAND; i += NTR) count_agg(cand[i], (i & (CAND / NWR - 1)) < wcnt[i / (CAND / NWR)]);
+      } else {
+        // A sample (two chunks of the row) tells whether many lanes share bins;
+        // if not, every lane adds its own 1 (no ballots), else the wave
+        // aggregates per bin.
+        bool crowd = false;
+#pragma unroll
+        for (int r = 0; r < REGV; r += REGV / 2) {
+          const uint32_t k4[4] = {rk[r].x, rk[r].y, rk[r].z, rk[r].w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            bool v;
+            const int b = bin_of(k4[e], 4 * r * NTR + e < lim, v);
+            const uint64_t act = __ballot(v);
+            if (act) {
+              const int b0 = __builtin_amdgcn_readlane(b, __builtin_ctzll(act));
+              crowd |= __builtin_popcountll(__ballot(v && b == b0)) >= 16;
+            }
+          }
+        }
+        if (crowd && lane == 0) flag[0] = 1;
+        __syncthreads();
+        if (flag[0]) {
+          each(count_agg);
+        } else {
+          each([&](uint32_t key, bool in) {
+            bool v;
+            const int b = bin_of(key, in, v);
+            if (v) atomicAdd(&hist[wv][b], 1);
+          });
+        }
+      }
+      __syncthreads();
+      int c = 0;
+      if (tid < 256) {
+#pragma unroll
+        for (int x = 0; x < NWR; ++x) c += hist[x][255 - tid];
+      }
+      int tot;
+      const int incl = block_exclusive_scan<NTR>(c, scan, &tot) + c;
+      if (tid < 256 && incl >= rem && incl - c < rem) { pick[0] = 255 - tid; pick[1] = incl - c; pick[2] = c; }
+      __syncthreads();
+      const int b = pick[0], bin_count = pick[2];
+      above += pick[1];
+      rem -= pick[1];
+      lo += (uint32_t)b << s;
+      sp = s;
+      if (s == 0) break;
+      if (!list && bin_count <= CAND) {         // the chosen bin's keys to LDS
+        // each wave appends to its own segment of CAND / NWR slots (a running
+        // count, no atomics); a segment that would overflow drops the list
+        constexpr int SEG = CAND / NWR;
+        const uint32_t width = 1u << s;
+        int wn = 0;                               // wave-uniform
+        if (tid == 0) flag[1] = 0;
+        each([&](uint32_t key, bool in) {
+          const bool hit = in && key >= lo && key - lo < width;
+          const uint64_t m = __ballot(hit);
+          if (m) {
+            const int at = wn + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                               __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+            if (hit && at < SEG) cand[wv * SEG + at] = key;
+            wn += __builtin_popcountll(m);
+          }
+        });
+        __syncthreads();                          // flag[1] cleared before any wave sets it
+        if (lane == 0) {
+          wcnt[wv] = wn;
+          if (wn > SEG) flag[1] = 1;
+        }
+        __syncthreads();
+        list = flag[1] == 0;
+      }
+    }
+  }
+  const uint32_t T = lo;
+  const int teq = need - above;                   // >= 1 copies of T are kept
+  // ---- 3. ordered output
+  const int nchunk = (nb + 4 * NTR - 1) / (4 * NTR);
+  auto masks = [&](int r, uint32_t& gt, uint32_t& eq) __attribute__((always_inline)) {
+    const uint32_t k4[4] = {rk[r].x, rk[r].y, rk[r].z, rk[r].w};
+    int lm = lim;
+    asm volatile("" : "+v"(lm));
+    gt = 0; eq = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const bool in = 4 * r * NTR + e < lm;
+      gt |= (uint32_t)(in && k4[e] > T) << e;
+      eq |= (uint32_t)(in && k4[e] == T) << e;
+    }
+  };
+#pragma unroll
+  for (int r = 0; r < REGV; ++r) {
+    if (r < nchunk) {                             // uniform
+      uint32_t gt, eq;
+      masks(r, gt, eq);
+      int tg, te;
+      (void)lane_prefix_small(__builtin_popcount(gt), tg);
+      (void)lane_prefix_small(__builtin_popcount(eq), te);
+      if (lane == 0) wtot[r][wv] = tg | (te << 16);
+    }
+  }
+  __syncthreads();
+  if (tid < 64) {                                 // wave 0: offsets of chunks and waves
+    int cg = 0, ce = 0;
+    if (tid < nchunk) {
+      int run = 0;
+#pragma unroll
+      for (int x = 0; x < NWR; ++x) { wpre[tid][x] = run; run += wtot[tid][x]; }
+      cg = run & 0xffff;
+      ce = run >> 16;
+    }
+    const int ig = wave_inclusive_scan(cg), ie = wave_inclusive_scan(ce);
+    if (tid < nchunk) { cbase[tid][0] = ig - cg; cbase[tid][1] = ie - ce; }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < REGV; ++r) {
+    if (r < nchunk) {                             // uniform
+      uint32_t gt, eq;
+      masks(r, gt, eq);
+      int tg, te;
+      const int pg = lane_prefix_small(__builtin_popcount(gt), tg);
+      const int pe = lane_prefix_small(__builtin_popcount(eq), te);
+      const int wp = wpre[r][wv];
+      int gtb = cbase[r][0] + (wp & 0xffff) + pg, eqb = cbase[r][1] + (wp >> 16) + pe;
+      const int i0 = 4 * (r * NTR + tid);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (gt & (1u << e)) {
+          out[gtb + min(eqb, teq)] = i0 + e;
+          ++gtb;
+        } else if (eq & (1u << e)) {
+          if (eqb < teq) out[gtb + eqb] = i0 + e;
+          ++eqb;
+        }
+      }
+    }
   }
 }
 
@@ -308,7 +515,7 @@ extern "C" int kvc_select_topk(const float* S, int L, int Hkv, int64_t n, const 
     const dim3 grid((unsigned)(lc * Hkv));
     const float* Sl = S + (int64_t)l0 * Hkv * n;
     if (use_cache) hipLaunchKernelGGL((select_kernel<true, true>), grid, dim3(NT), cache, s, Sl, Hkv, n, kk, w, ip);
-    else if (use_reg) hipLaunchKernelGGL((select_kernel<true, false, true>), grid, dim3(NTR), 0, s, Sl, Hkv, n, kk, w, ip);
+    else if (use_reg) hipLaunchKernelGGL(select_reg_kernel, grid, dim3(NTR), 0, s, Sl, Hkv, n, kk, w, ip);
     else if (vec) hipLaunchKernelGGL((select_kernel<true, false>), grid, dim3(NT), 0, s, Sl, Hkv, n, kk, w, ip);
     else hipLaunchKernelGGL((select_kernel<false, false>), grid, dim3(NT), 0, s, Sl, Hkv, n, kk, w, ip);
   }
