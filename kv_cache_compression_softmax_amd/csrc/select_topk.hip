@@ -216,24 +216,11 @@ select_kernel(const float* __restrict__ S, int Hkv, int64_t n, I64s kk, int w, M
 //   2. After the first pass the keys of the chosen bin (when at most CAND) are
 //      copied to an LDS list, and the remaining passes read the list only.
 //   3. Ordered output: chunk r of the row is vector r * NTR + t of thread t.
-//      Per chunk, each wave's prefix counts come from ballots of the bit
-//      planes of the per-thread counts (0..4); the chunk and wave offsets come
-//      from one table in LDS, so the whole output takes two barriers.
+//      Per chunk and element, each wave's counts and lane prefixes come from
+//      ballots (popcounts and mbcnts); the chunk and wave offsets come from one
+//      table in LDS, so the whole output takes two barriers.
 constexpr int NWR = NTR / 64;   // waves of the register path
 constexpr int CAND = 8192;      // candidate keys copied to LDS after the first pass
-
-// Exclusive prefix of v (0..7) over the wave's lanes, and the wave total.
-__device__ __forceinline__ int lane_prefix_small(int v, int& total) {
-  int pre = 0, tot = 0;
-#pragma unroll
-  for (int j = 0; j < 3; ++j) {
-    const uint64_t b = __ballot((v >> j) & 1);
-    pre += (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(b >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0u)) << j;
-    tot += __builtin_popcountll(b) << j;
-  }
-  total = tot;
-  return pre;
-}
 
 __global__ void __launch_bounds__(NTR)
 select_reg_kernel(const float* __restrict__ S, int Hkv, int64_t n, I64s kk, int w, MutPtrs idx) {
@@ -316,14 +303,17 @@ select_reg_kernel(const float* __restrict__ S, int Hkv, int64_t n, I64s kk, int 
 #pragma unroll 1
     for (;;) {
       const int s = sp > 8 ? sp - 8 : 0;          // bin width 2^s: at most 256 bins
+      const uint32_t dmax = sp >= 32 ? ~0u : (1u << sp) - 1u;
       for (int i = tid; i < NWR * 256; i += NTR) (&hist[0][0])[i] = 0;
       if (tid == 0) flag[0] = 0;
       __syncthreads();
-      // keys in [lo, lo + 2^sp): bin (key - lo) >> s
+      // keys in [lo, lo + 2^sp): key - lo <= dmax (a key below lo wraps past
+      // dmax, except in the first pass, where every key is >= lo); bin
+      // (key - lo) >> s, below 256 for every valid key
       auto bin_of = [&](uint32_t key, bool in, bool& valid) __attribute__((always_inline)) {
         const uint32_t d = key - lo;
-        valid = in && key >= lo && ((uint64_t)d >> sp) == 0;
-        return (int)((d >> s) & 255u);
+        valid = in && d <= dmax;
+        return (int)(d >> s);
       };
       auto count_agg = [&](uint32_t key, bool in) __attribute__((always_inline)) {
         bool v;
@@ -337,13 +327,15 @@ select_reg_kernel(const float* __restrict__ S, int Hkv, int64_t n, I64s kk, int 
         // if not, every lane adds its own 1 (no ballots), else the wave
         // aggregates per bin.
         bool crowd = false;
+        int lm = lim;
+        asm volatile("" : "+v"(lm));
 #pragma unroll
         for (int r = 0; r < REGV; r += REGV / 2) {
           const uint32_t k4[4] = {rk[r].x, rk[r].y, rk[r].z, rk[r].w};
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             bool v;
-            const int b = bin_of(k4[e], 4 * r * NTR + e < lim, v);
+            const int b = bin_of(k4[e], 4 * r * NTR + e < lm, v);
             const uint64_t act = __ballot(v);
             if (act) {
               const int b0 = __builtin_amdgcn_readlane(b, __builtin_ctzll(act));
@@ -408,28 +400,32 @@ select_reg_kernel(const float* __restrict__ S, int Hkv, int64_t n, I64s kk, int 
   }
   const uint32_t T = lo;
   const int teq = need - above;                   // >= 1 copies of T are kept
-  // ---- 3. ordered output
+  // ---- 3. ordered output.  Per chunk and element e, the lanes keeping their
+  // element as "> T" or "== T" are compare masks, so the wave totals are
+  // popcounts and a lane's prefix is a sum of mbcnts.
   const int nchunk = (nb + 4 * NTR - 1) / (4 * NTR);
-  auto masks = [&](int r, uint32_t& gt, uint32_t& eq) __attribute__((always_inline)) {
+  auto masks = [&](int r, bool (&g)[4], bool (&q)[4]) __attribute__((always_inline)) {
     const uint32_t k4[4] = {rk[r].x, rk[r].y, rk[r].z, rk[r].w};
     int lm = lim;
     asm volatile("" : "+v"(lm));
-    gt = 0; eq = 0;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const bool in = 4 * r * NTR + e < lm;
-      gt |= (uint32_t)(in && k4[e] > T) << e;
-      eq |= (uint32_t)(in && k4[e] == T) << e;
+      g[e] = in && k4[e] > T;
+      q[e] = in && k4[e] == T;
     }
+  };
+  auto below = [&](uint64_t m) __attribute__((always_inline)) {   // set lanes below this one
+    return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
   };
 #pragma unroll
   for (int r = 0; r < REGV; ++r) {
     if (r < nchunk) {                             // uniform
-      uint32_t gt, eq;
-      masks(r, gt, eq);
-      int tg, te;
-      (void)lane_prefix_small(__builtin_popcount(gt), tg);
-      (void)lane_prefix_small(__builtin_popcount(eq), te);
+      bool g[4], q[4];
+      masks(r, g, q);
+      int tg = 0, te = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) { tg += __builtin_popcountll(__ballot(g[e])); te += __builtin_popcountll(__ballot(q[e])); }
       if (lane == 0) wtot[r][wv] = tg | (te << 16);
     }
   }
@@ -450,20 +446,24 @@ select_reg_kernel(const float* __restrict__ S, int Hkv, int64_t n, I64s kk, int 
 #pragma unroll
   for (int r = 0; r < REGV; ++r) {
     if (r < nchunk) {                             // uniform
-      uint32_t gt, eq;
-      masks(r, gt, eq);
-      int tg, te;
-      const int pg = lane_prefix_small(__builtin_popcount(gt), tg);
-      const int pe = lane_prefix_small(__builtin_popcount(eq), te);
+      bool g[4], q[4];
+      masks(r, g, q);
       const int wp = wpre[r][wv];
-      int gtb = cbase[r][0] + (wp & 0xffff) + pg, eqb = cbase[r][1] + (wp >> 16) + pe;
+      int gtb = cbase[r][0] + (wp & 0xffff), eqb = cbase[r][1] + (wp >> 16);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) gtb += below(__ballot(g[e]));
+      const bool anyq = __ballot(q[0] || q[1] || q[2] || q[3]) != 0;   // rare: copies of T
+      if (anyq) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) eqb += below(__ballot(q[e]));
+      }
       const int i0 = 4 * (r * NTR + tid);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        if (gt & (1u << e)) {
+        if (g[e]) {
           out[gtb + min(eqb, teq)] = i0 + e;
           ++gtb;
-        } else if (eq & (1u << e)) {
+        } else if (q[e]) {
           if (eqb < teq) out[gtb + eqb] = i0 + e;
           ++eqb;
         }
