@@ -459,14 +459,12 @@ select_reg_kernel(const float* __restrict__ S, int Hkv, int64_t n, I64s kk, int 
       }
       const int i0 = 4 * (r * NTR + tid);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if (g[e]) {
-          out[gtb + min(eqb, teq)] = i0 + e;
-          ++gtb;
-        } else if (q[e]) {
-          if (eqb < teq) out[gtb + eqb] = i0 + e;
-          ++eqb;
-        }
+      for (int e = 0; e < 4; ++e) {              // positions without branches, one masked store
+        const int pos = gtb + min(eqb, teq);      // for "== T" kept: eqb < teq, so pos = gtb + eqb
+        const bool keep = g[e] || (q[e] && eqb < teq);
+        if (keep) out[pos] = i0 + e;
+        gtb += g[e] ? 1 : 0;
+        eqb += q[e] ? 1 : 0;
       }
     }
   }
