@@ -237,9 +237,17 @@ __device__ __forceinline__ uint4 load_tail(const T* row, int64_t e0, int64_t voc
   return u;
 }
 
-template <typename T, int CAP, bool ALIGNED>
+// SPLIT waves share a row when rows are few (short row counts would leave most
+// of the GPU idle with one wave per row): wave q of a row treats its part, the
+// q-th run of whole steps (the last part also takes the ragged end), exactly as
+// a row of its own and ends with that part's top-k.  Every element of the row's
+// top-k multiset is in its part's top-k, so after a workgroup barrier the
+// first wave of the row re-selects the top-k of the SPLIT lists and takes the
+// entropy.  The host picks SPLIT so that every part has a whole step (at least
+// k elements for the part's first select) and the SPLIT lists fit one list.
+template <typename T, int CAP, bool ALIGNED, int SPLIT>
 __global__ void __launch_bounds__(NT)
-topk_entropy_kernel(const T* __restrict__ logits, int64_t rows, int64_t vocab, int64_t stride,
+topk_entropy_kernel(const T* __restrict__ logits, int64_t rows, int64_t vocab_all, int64_t stride,
                     int k, float* __restrict__ H) {
   using Raw = typename Tr<T>::Raw;
   constexpr int VEC = Tr<T>::VEC;
@@ -248,13 +256,23 @@ topk_entropy_kernel(const T* __restrict__ logits, int64_t rows, int64_t vocab, i
   // the first select takes the first step alone, which must hold k elements
   static_assert(STEP >= KVC_MAX_TOPK_ENTROPY, "a step holds at least the largest k");
   static_assert(CAP == RESEL + STEP && CAP % VEC == 0, "list capacity");
+  static_assert(SPLIT == 1 || SPLIT == 2 || SPLIT == 4, "waves per row");
   __shared__ WaveSmem<Raw, CAP> smem[NT / 64];
   const int lane = threadIdx.x & 63, wv = threadIdx.x / 64;
-  const int64_t rowi = (int64_t)blockIdx.x * (NT / 64) + wv;
-  if (rowi >= rows) return;                      // no block barriers below
+  const int64_t rowi = (int64_t)blockIdx.x * (NT / 64 / SPLIT) + wv / SPLIT;
+  const int part = wv % SPLIT;
+  if constexpr (SPLIT == 1) {
+    if (rowi >= rows) return;                    // no block barriers with one wave per row
+  }
+  const bool live = rowi < rows;                 // with SPLIT > 1 every wave reaches the barrier
   Raw* cand = reinterpret_cast<Raw*>(smem[wv].cand4);
   int* hist = smem[wv].hist;
-  const T* row = logits + rowi * stride;
+  const int64_t steps_all = vocab_all / STEP;    // whole steps of the row
+  const int64_t per = (steps_all + SPLIT - 1) / SPLIT;
+  const int64_t s0 = min((int64_t)part * per, steps_all);
+  // this wave's part: whole steps [s0, s0 + nfull), plus the ragged end for the last part
+  const T* row = logits + rowi * stride + s0 * STEP;
+  const int64_t vocab = (part == SPLIT - 1) ? vocab_all - s0 * STEP : min(per, steps_all - s0) * STEP;
   const int64_t nfull = vocab / STEP;            // steps with every element present
 
   int count = 0;                                 // list length, a multiple of VEC
@@ -320,7 +338,8 @@ topk_entropy_kernel(const T* __restrict__ logits, int64_t rows, int64_t vocab, i
   // an L2 hit): a load issued on only some paths would make the compiler wait for
   // every outstanding load before each step.
   uint4 ba[NV], bb[NV];
-  if (nfull > 0) {
+  if (!live) {
+  } else if (nfull > 0) {
     const int64_t last = nfull - 1;
     load(0, ba);
     load(min((int64_t)1, last), bb);
@@ -344,7 +363,22 @@ topk_entropy_kernel(const T* __restrict__ logits, int64_t rows, int64_t vocab, i
     load_last(ba);
     first(ba);
   }
-  if (!exact) select(true);
+  if (live && !exact) select(true);
+  if constexpr (SPLIT > 1) {
+    // the row's top-k from its parts' lists (each padded to kr with the
+    // smallest key); the first wave of the row gathers them after its own
+    const int kr = (k + VEC - 1) / VEC * VEC;
+    __syncthreads();
+    if (part == 0 && live) {
+      for (int q = 1; q < SPLIT; ++q) {
+        const Raw* src = reinterpret_cast<const Raw*>(smem[wv + q].cand4);
+        for (int i = lane; i < kr; i += 64) cand[q * kr + i] = src[i];
+      }
+      count = SPLIT * kr;
+      select(false);
+    }
+    if (part != 0 || !live) return;
+  }
 
   // Entropy over the k held keys (float32, fixed reduction order).  With
   // x = t - m <= 0 and Z = sum e^x:  H = ln Z + (1/Z) sum e^x (-x).  A row whose
@@ -375,20 +409,38 @@ topk_entropy_kernel(const T* __restrict__ logits, int64_t rows, int64_t vocab, i
   if (lane == 0) H[rowi] = m == -INFINITY ? NAN : h;   // no finite logit: no entropy
 }
 
+template <typename T, int SPLIT>
+void launch_split(const void* logits, int64_t rows, int64_t vocab, int64_t stride, int k, float* H,
+                  hipStream_t s) {
+  constexpr int CAP = RESEL + 64 * Tr<T>::NV * Tr<T>::VEC;
+  static_assert(RESEL >= KVC_MAX_TOPK_ENTROPY + 8, "a re-selected list must fit below RESEL");
+  constexpr int RPW = NT / 64 / SPLIT;           // rows per workgroup
+  const unsigned grid = (unsigned)((rows + RPW - 1) / RPW);
+  // every row start is 16-byte aligned iff the base and the row pitch are; a
+  // part starts a whole number of 16-byte steps after its row
+  const bool aligned = ((uintptr_t)logits % 16 == 0) && ((stride * (int64_t)sizeof(T)) % 16 == 0);
+  if (aligned)
+    hipLaunchKernelGGL((topk_entropy_kernel<T, CAP, true, SPLIT>), dim3(grid), dim3(NT), 0, s,
+                       (const T*)logits, rows, vocab, stride, k, H);
+  else
+    hipLaunchKernelGGL((topk_entropy_kernel<T, CAP, false, SPLIT>), dim3(grid), dim3(NT), 0, s,
+                       (const T*)logits, rows, vocab, stride, k, H);
+}
+
 template <typename T>
 void launch(const void* logits, int64_t rows, int64_t vocab, int64_t stride, int k, float* H,
             hipStream_t s) {
-  constexpr int CAP = RESEL + 64 * Tr<T>::NV * Tr<T>::VEC;
-  static_assert(RESEL >= KVC_MAX_TOPK_ENTROPY + 8, "a re-selected list must fit below RESEL");
-  const unsigned grid = (unsigned)((rows + NT / 64 - 1) / (NT / 64));
-  // every row start is 16-byte aligned iff the base and the row pitch are
-  const bool aligned = ((uintptr_t)logits % 16 == 0) && ((stride * (int64_t)sizeof(T)) % 16 == 0);
-  if (aligned)
-    hipLaunchKernelGGL((topk_entropy_kernel<T, CAP, true>), dim3(grid), dim3(NT), 0, s,
-                       (const T*)logits, rows, vocab, stride, k, H);
-  else
-    hipLaunchKernelGGL((topk_entropy_kernel<T, CAP, false>), dim3(grid), dim3(NT), 0, s,
-                       (const T*)logits, rows, vocab, stride, k, H);
+  constexpr int STEP = 64 * Tr<T>::NV * Tr<T>::VEC;
+  constexpr int CAP = RESEL + STEP;
+  const int64_t kr = (k + Tr<T>::VEC - 1) / Tr<T>::VEC * Tr<T>::VEC;
+  // waves per row: enough for about 16 waves per CU when rows are few, while
+  // every part keeps a whole step and the parts' lists fit one list
+  auto fits = [&](int sp) { return vocab / STEP >= sp && sp * kr <= CAP; };
+  int split = 1;
+  if (rows < 4096) split = (rows < 2048 && fits(4)) ? 4 : (fits(2) ? 2 : 1);
+  if (split == 4) launch_split<T, 4>(logits, rows, vocab, stride, k, H, s);
+  else if (split == 2) launch_split<T, 2>(logits, rows, vocab, stride, k, H, s);
+  else launch_split<T, 1>(logits, rows, vocab, stride, k, H, s);
 }
 
 }  // namespace
