@@ -12,7 +12,10 @@
 // A needs each row's softmax normaliser before any column can be summed, so the
 // bf16 path makes two passes over K:
 //   pass 1  per 32-key block, S^T = K * Q^T on MFMA (keys on M, queries on N);
-//           each lane keeps an online (max, sum of exp2) for one query row.  The
+//           each lane keeps a (reference, sum of exp2) pair for one query row:
+//           the wave's first block sets the reference to the row's maximum there,
+//           later blocks only add exp2(s - reference) (no running maximum; a sum
+//           that overflows sends the wave back over its keys with one).  The
 //           four waves of a workgroup merge in LDS and write one partial;
 //           Each pass-2 workgroup merges its (layer, KV head)'s partials in index
 //           order into c_r = max + log2(sum), +inf for padding rows;
@@ -213,14 +216,27 @@ __device__ __forceinline__ void pass1(const WinArgs& a, WinSmem<D, TG>& sm, int 
   const int64_t safe_end = g.n - g.w;            // keys <= this are seen by every row
   // one 32-key block; kc holds its key fragments
   // FULL: every key of the block is visible to every row (no mask code at all)
-  auto block_t = [&](const bf16x8 (&kc)[S], int64_t j0, auto full_t) __attribute__((always_inline)) {
+  // FIXED: the lane's rows keep the reference m set by the wave's first block and
+  // add exp2(s - m) with no running maximum.  The partial (m, sum) is then a valid
+  // normaliser pair for any m; a term above 2^128 would make the sum infinite,
+  // which the check after the stream catches (the wave then redoes its keys with
+  // the running maximum).
+  auto block_t = [&](const bf16x8 (&kc)[S], int64_t j0, auto full_t, auto fixed_t) __attribute__((always_inline)) {
     constexpr bool full = decltype(full_t)::value;
+    constexpr bool fixed = decltype(fixed_t)::value;
     int qo = lane;
     asm volatile("" : "+v"(qo));                 // keep the Q reads in the loop (LDS, not VGPRs)
     // scores in log2 units are acc * sl2 (sl2 > 0): take the block max on the raw
     // accumulator, then one FMA and one v_exp_f32 per element (results below
     // 2^-126 flush to zero, which changes no sum at float32 precision)
     auto epi = [&](int t, f32x16 acc) __attribute__((always_inline)) {
+      if constexpr (fixed) {
+        float sum = __builtin_amdgcn_exp2f(fmaf(acc[0], a.sl2, -m[t]));
+#pragma unroll
+        for (int v = 1; v < 16; ++v) sum += __builtin_amdgcn_exp2f(fmaf(acc[v], a.sl2, -m[t]));
+        sm_[t] += sum;
+        return;
+      }
       float bm = -INFINITY;
       if constexpr (full) {
 #pragma unroll
@@ -247,11 +263,29 @@ __device__ __forceinline__ void pass1(const WinArgs& a, WinSmem<D, TG>& sm, int 
     };
     pipelined_tiles<S, TG, true>(kc, sm.q, qo, epi);
   };
+  // full blocks after the wave's first take the fixed reference; the first block
+  // (where m is set) and the masked blocks at the end of K keep the running maximum
   auto block = [&](const bf16x8 (&kc)[S], int64_t j0) {
-    if (j0 + 31 <= safe_end) block_t(kc, j0, std::true_type{});   // wave-uniform branch
-    else block_t(kc, j0, std::false_type{});
+    if (j0 + 31 <= safe_end) {                   // wave-uniform branches
+      if (j0 != jb) block_t(kc, j0, std::true_type{}, std::true_type{});
+      else block_t(kc, j0, std::true_type{}, std::false_type{});
+    } else {
+      block_t(kc, j0, std::false_type{}, std::false_type{});
+    }
+  };
+  auto careful = [&](const bf16x8 (&kc)[S], int64_t j0) {
+    if (j0 + 31 <= safe_end) block_t(kc, j0, std::true_type{}, std::false_type{});
+    else block_t(kc, j0, std::false_type{}, std::false_type{});
   };
   stream_blocks<D>(kh, g.n, jb, nb, lane, prologue, block);
+  bool bad = false;
+#pragma unroll
+  for (int t = 0; t < TG; ++t) bad = bad || !(sm_[t] <= 3.0e38f);   // inf or NaN
+  if (__builtin_amdgcn_ballot_w64(bad) != 0) {   // wave-uniform; not seen on finite logits
+#pragma unroll
+    for (int t = 0; t < TG; ++t) { m[t] = -INFINITY; sm_[t] = 0.f; }
+    stream_blocks<D>(kh, g.n, jb, nb, lane, []() {}, careful);
+  }
   // halves (lanes i, i+32 share a query row), then the 4 waves, in fixed order
 #pragma unroll
   for (int t = 0; t < TG; ++t) {
@@ -279,7 +313,7 @@ __device__ __forceinline__ void pass1(const WinArgs& a, WinSmem<D, TG>& sm, int 
 }
 
 // ---------------------------------------------------------------- pass 2
-template <int D, int TG>
+template <int D, int TG, bool PH>
 __device__ __forceinline__ void pass2(const WinArgs& a, WinSmem<D, TG>& sm, int l, int kvh, int wgi) {
   constexpr int S = D / 16;
   const Geo& g = a.g;
@@ -375,7 +409,7 @@ __device__ __forceinline__ void pass2(const WinArgs& a, WinSmem<D, TG>& sm, int 
     for (int t = 0; t < TG; ++t) {
       const float cs = hs[t] + __shfl_xor(hs[t], 32, 64);
       total += cs;
-      if (a.per_head) {
+      if constexpr (PH) {
         hsum += cs;
         const int tile = a.tile0 + t;
         const bool last_of_head = (t == TG - 1) || ((tile + 1) % g.tph == 0);
@@ -390,7 +424,7 @@ __device__ __forceinline__ void pass2(const WinArgs& a, WinSmem<D, TG>& sm, int 
         }
       }
     }
-    if (!a.per_head && hf == 0 && key < g.n) {
+    if (!PH && hf == 0 && key < g.n) {
       float* dst = A + ((int64_t)l * g.Hkv + kvh) * g.n + key;
       *dst = a.tile0 == 0 ? total * inv_group : *dst + total * inv_group;
     }
@@ -402,7 +436,9 @@ __device__ __forceinline__ void pass2(const WinArgs& a, WinSmem<D, TG>& sm, int 
   stream_blocks<D>(kh, g.n, jb, nb, lane, prologue, block);
 }
 
-template <int D, int TG>
+// PH: A per query head (else the group mean), fixed at compile time so that the
+// pass-2 block stays one scheduling region
+template <int D, int TG, bool PH>
 __global__ void __launch_bounds__(NTW)
 win_kernel(WinArgs a) {
   __shared__ WinSmem<D, TG> sm;
@@ -416,7 +452,7 @@ win_kernel(WinArgs a) {
     const int wgi = (int)(local % a.g.nwg);
     const int l = sp.l0 + (int)(lgl / a.g.Hkv), kvh = (int)(lgl % a.g.Hkv);
     if (sp.pass == 1) pass1<D, TG>(a, sm, l, kvh, wgi);
-    else pass2<D, TG>(a, sm, l, kvh, wgi);
+    else pass2<D, TG, PH>(a, sm, l, kvh, wgi);
     __syncthreads();                             // LDS is reused by the next task
   }
 }
@@ -550,12 +586,18 @@ int resident_blocks(const void* kern) {
   return (ncu > 0 ? ncu : 1) * (per_cu > 0 ? per_cu : 1);
 }
 
-template <int D, int TG>
-void launch_win_tg(WinArgs a, hipStream_t s) {
-  const void* kern = reinterpret_cast<const void*>(&win_kernel<D, TG>);
+template <int D, int TG, bool PH>
+void launch_win_ph(WinArgs a, hipStream_t s) {
+  const void* kern = reinterpret_cast<const void*>(&win_kernel<D, TG, PH>);
   const int64_t res = resident_blocks(kern);
   const dim3 grid((unsigned)(a.ntask < res ? a.ntask : res)), block(NTW);
-  hipLaunchKernelGGL((win_kernel<D, TG>), grid, block, 0, s, a);
+  hipLaunchKernelGGL((win_kernel<D, TG, PH>), grid, block, 0, s, a);
+}
+
+template <int D, int TG>
+void launch_win_tg(WinArgs a, hipStream_t s) {
+  if (a.per_head) launch_win_ph<D, TG, true>(a, s);
+  else launch_win_ph<D, TG, false>(a, s);
 }
 
 template <int D>

@@ -273,6 +273,33 @@ def test_window_attention(dev, case, per_head):
     np.testing.assert_allclose(A.sum(dim=2).cpu().numpy(), 1.0, atol=1e-4)
 
 
+@pytest.mark.parametrize("per_head", [False, True])
+def test_window_attention_late_dominant_keys(dev, per_head):
+    """Keys whose logit for one window row lies far (over 2^7 in log2 units) above
+    everything the row met before in the same 512-key stretch of K: pass 1 must
+    still produce exact normalisers (its sums against the first block's maximum
+    would overflow there).  One such key also sits in the first block of a
+    stretch, one in the masked tail."""
+    L, Hq, Hkv, n, w, d = 1, 8, 2, 3000, 32, 128
+    announce("window_attn_dominant", per_head)
+    q = [gen((Hq, w, d), 70, dev, torch.bfloat16)]
+    k = [gen((Hkv, n, d), 71, dev, torch.bfloat16)]
+    G = Hq // Hkv
+    # (kv head, key, query head within the group, window row, multiple of q)
+    for g, j, hh, r, c in [(0, 700, 1, 5, 12.0), (0, 1030, 0, 0, 10.0), (0, 515, 2, 7, 12.0),
+                           (1, 2200, 3, 31, 14.0), (1, n - 3, 1, 31, 12.0)]:
+        k[0][g, j] = (c * q[0][g * G + hh, r].float()).to(torch.bfloat16)
+    A = torch.empty(L, Hq if per_head else Hkv, n, device=dev)
+    B().kvc_score_window_attn(q, k, 1 / math.sqrt(d), per_head, A)
+    torch.cuda.synchronize()
+    ref = infokv.window_attention(host_f64(q[0]), host_f64(k[0]), per_query_head=per_head)
+    assert ref.max() > 0.02                       # the planted keys do dominate their rows
+    # a dominated row leaves some per-head values near 1e-70, which float32 holds
+    # as 0: relative error against a floor of 1e-30
+    assert_rel(A[0].cpu().numpy(), ref, 1e-3, floor=1e-30, what="A")
+    np.testing.assert_allclose(A.sum(dim=2).cpu().numpy(), 1.0, atol=1e-4)
+
+
 # ----------------------------------------------------------------- fuse
 @pytest.mark.parametrize("L,Hkv,n", [(1, 2, 512), (3, 8, 20001), (2, 4, 70000), (34, 2, 300)])
 def test_fuse_scores(dev, L, Hkv, n):
