@@ -72,6 +72,15 @@ struct WinArgs {
   int64_t ntask;                       // tasks of all spans
 };
 
+// x of this lane plus x of lane ^ 32, the same value in both lanes (one
+// v_permlane32_swap: lane i < 32 receives (own, partner), lane i + 32 (partner,
+// own), so the sum of the pair is the same in both halves)
+__device__ __forceinline__ float add_halves(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 __device__ __forceinline__ bf16x8 as_bf16x8(const uint4& u) {
   bf16x8 r;
   __builtin_memcpy(&r, &u, 16);
@@ -326,6 +335,7 @@ __device__ __forceinline__ void pass2(const WinArgs& a, WinSmem<D, TG>& sm, int 
   // per row each merge every P-th partial (loads issued 8 at a time), then the P
   // results are merged in a fixed order; +inf for padding rows and rows that see
   // no key
+  float cr[TG][16];                              // row normalisers (set by the prologue)
   auto prologue = [&]() __attribute__((always_inline)) {
     stage_q<D, TG>((const uint16_t*)a.q.p[l], g, kvh, a.tile0, sm.q);
     constexpr int R = TG * 32, P = NTW / R;
@@ -365,6 +375,16 @@ __device__ __forceinline__ void pass2(const WinArgs& a, WinSmem<D, TG>& sm, int 
       sm.c[r] = (!pad && Mt > -INFINITY) ? Mt + log2f(St) : INFINITY;
     }
     __syncthreads();
+    // this lane's 16 normalisers of each tile, held for the whole task (pass 2
+    // would otherwise read them from LDS in every block, beside the Q fragments)
+#pragma unroll
+    for (int t = 0; t < TG; ++t)
+#pragma unroll
+      for (int qd = 0; qd < 4; ++qd) {
+        const float4 c4 = reinterpret_cast<const float4*>(sm.c)[t * 8 + 2 * qd + hf];
+        cr[t][4 * qd + 0] = c4.x; cr[t][4 * qd + 1] = c4.y;
+        cr[t][4 * qd + 2] = c4.z; cr[t][4 * qd + 3] = c4.w;
+      }
   };
 
   const int64_t jb = ((int64_t)wgi * (NTW / 64) + wv) * KPW;
@@ -376,10 +396,8 @@ __device__ __forceinline__ void pass2(const WinArgs& a, WinSmem<D, TG>& sm, int 
   auto block_t = [&](const bf16x8 (&kc)[S], int64_t j0, auto full_t) __attribute__((always_inline)) {
     constexpr bool full = decltype(full_t)::value;
     const int64_t key = j0 + qi;                 // this lane's key column
-    // keep the Q and c reads in the loop; c is indexed in float4 units so that
-    // each read is one aligned ds_read_b128 with an immediate offset
-    int qo = lane, co = hf;
-    asm volatile("" : "+v"(qo), "+v"(co));
+    int qo = lane;
+    asm volatile("" : "+v"(qo));                 // keep the Q reads in the loop (LDS, not VGPRs)
     // this lane's 16 rows of tile t: exp2(s - c_r) summed (the partner lane adds
     // the other 16 at the end of the block); the key is seen by rows rr with
     // key - (n - w) <= rr < w, and only if key < n
@@ -391,12 +409,10 @@ __device__ __forceinline__ void pass2(const WinArgs& a, WinSmem<D, TG>& sm, int 
       float colsum = 0.f;
 #pragma unroll
       for (int qd = 0; qd < 4; ++qd) {
-        const float4 c4 = reinterpret_cast<const float4*>(sm.c)[t * 8 + 2 * qd + co];
-        const float cc[4] = {c4.x, c4.y, c4.z, c4.w};
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const int v = 4 * qd + u, off = 8 * qd + u;
-          float e = __builtin_amdgcn_exp2f(fmaf(acc[v], a.sl2, -cc[u]));
+          float e = __builtin_amdgcn_exp2f(fmaf(acc[v], a.sl2, -cr[t][v]));
           if constexpr (!full) e = (off >= lo && off < hi) ? e : 0.f;
           colsum += e;
         }
@@ -404,12 +420,21 @@ __device__ __forceinline__ void pass2(const WinArgs& a, WinSmem<D, TG>& sm, int 
       hs[t] = colsum;
     };
     pipelined_tiles<S, TG, false>(kc, sm.q, qo, epi);
+    // pin the column sums here: otherwise the compiler sinks each tile's
+    // epilogue into the per-head store branch below, after every MFMA
+#pragma unroll
+    for (int t = 0; t < TG; ++t) asm volatile("" : "+v"(hs[t]));
     float total = 0.f, hsum = 0.f;
+    if constexpr (!PH) {                         // one cross-half add for the group
+      float own = hs[0];
+#pragma unroll
+      for (int t = 1; t < TG; ++t) own += hs[t];
+      total = add_halves(own);
+    }
 #pragma unroll
     for (int t = 0; t < TG; ++t) {
-      const float cs = hs[t] + __shfl_xor(hs[t], 32, 64);
-      total += cs;
       if constexpr (PH) {
+        const float cs = add_halves(hs[t]);
         hsum += cs;
         const int tile = a.tile0 + t;
         const bool last_of_head = (t == TG - 1) || ((tile + 1) % g.tph == 0);
