@@ -45,7 +45,10 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 constexpr int NTW = 256;        // threads per workgroup (4 waves)
 constexpr int MAX_TILES = 8;    // G * ceil(w/32)
 constexpr int MAX_TG = 4;       // tiles per launch
-constexpr int KPW = 512;        // keys per wave
+constexpr int KPW = 512;        // keys per wave (twice that from kLongRow keys on)
+// 1024 keys per wave halve the per-task costs (Q staging, pass-2 partial merge):
+// 2.85 -> 2.74 ms at 102400 tokens, but 1.71 -> 1.83 ms at 65536 (8B shape)
+constexpr int64_t kLongRow = 98304;
 constexpr int64_t kMallBytes = 256ll << 20;  // MI355X last-level cache (MALL)
 constexpr int kLargeChunk = 16;  // layers per chunk when a layer's keys exceed half the MALL
 constexpr float LOG2E = 1.4426950408889634f;
@@ -54,6 +57,7 @@ struct Geo {
   int Hq, Hkv, G, w, d, tph, ntiles;   // tiles per head, tiles per KV group
   int64_t n;
   int nwg;                             // workgroups per (layer, KV head)
+  int kpw;                             // keys per wave
 };
 
 struct Span { int l0, nl, pass; };     // layers [l0, l0 + nl) of the table, pass 1 or 2
@@ -219,8 +223,8 @@ __device__ __forceinline__ void pass1(const WinArgs& a, WinSmem<D, TG>& sm, int 
 #pragma unroll
   for (int t = 0; t < TG; ++t) { m[t] = -INFINITY; sm_[t] = 0.f; }
 
-  const int64_t jb = ((int64_t)wgi * (NTW / 64) + wv) * KPW;
-  const int64_t je = min(g.n, jb + KPW);
+  const int64_t jb = ((int64_t)wgi * (NTW / 64) + wv) * g.kpw;
+  const int64_t je = min(g.n, jb + g.kpw);
   const int nb = (int)((je - jb + 31) / 32);     // <= 0 past the end of K
   const int64_t safe_end = g.n - g.w;            // keys <= this are seen by every row
   // one 32-key block; kc holds its key fragments
@@ -387,8 +391,8 @@ __device__ __forceinline__ void pass2(const WinArgs& a, WinSmem<D, TG>& sm, int 
       }
   };
 
-  const int64_t jb = ((int64_t)wgi * (NTW / 64) + wv) * KPW;
-  const int64_t je = min(g.n, jb + KPW);
+  const int64_t jb = ((int64_t)wgi * (NTW / 64) + wv) * g.kpw;
+  const int64_t je = min(g.n, jb + g.kpw);
   const int nb = (int)((je - jb + 31) / 32);
   const int64_t safe_end = g.n - g.w;
   const float inv_group = 1.0f / (float)(g.G * g.w), inv_w = 1.0f / (float)g.w;
@@ -578,7 +582,8 @@ void make_plan(int L, int Hq, int Hkv, int64_t n, int w, int d, int dtype, Plan*
   g.Hq = Hq; g.Hkv = Hkv; g.G = Hq / Hkv; g.w = w; g.d = d; g.n = n;
   g.tph = (w + 31) / 32;
   g.ntiles = g.G * g.tph;
-  g.nwg = (int)((n + 4LL * KPW - 1) / (4LL * KPW));
+  g.kpw = n >= kLongRow ? 2 * KPW : KPW;
+  g.nwg = (int)((n + 4LL * g.kpw - 1) / (4LL * g.kpw));
   P->g = g;
   P->mfma = (dtype == KVC_BF16);
   const int lg_max = L < kLayersPerLaunch ? L : kLayersPerLaunch;

@@ -254,6 +254,7 @@ WIN_CASES = [
     (1, 2, 1, 31, 31, 64, torch.bfloat16),          # w = n < 32
     (1, 6, 2, 150, 20, 32, torch.float32),          # float32 path, G = 3
     (34, 4, 2, 300, 16, 64, torch.bfloat16),        # more layers than one launch holds
+    (1, 4, 1, 100003, 32, 128, torch.bfloat16),     # long rows (1024 keys per wave), ragged
 ]
 
 
