@@ -487,6 +487,427 @@ win_kernel(WinArgs a) {
 }
 
 
+// ---------------------------------------------------------------- XCD-resident path
+// Pass 2 of the kernel above reads every key a second time.  When a (layer, KV
+// head) unit's keys fit in the registers of one XCD's workgroups, this kernel
+// reads them once: a team of workgroups on one XCD loads the unit's keys into
+// registers (128 VGPRs of keys per wave), runs pass 1 on them, meets at a team
+// barrier, merges the members' row normalisers and runs pass 2 on the same
+// registers.  While pass 2 works through a key block, that block's registers are
+// refilled with the team's next unit, and pass 1 of that unit follows right
+// behind the loads.
+//
+// Workgroups are 512 threads (two waves per SIMD) and need more than half of a
+// CU's registers, so a CU holds one; the launch is cooperative (every workgroup
+// resident at once), so each XCD holds exactly as many workgroups as it has CUs.
+// A workgroup learns its XCD from the hardware register and takes a slot on that
+// XCD from an atomic counter; teams are formed from slots, so a team's members
+// share one L2 whatever order the dispatcher used.  Pass-1 records are plain
+// stores read back with plain loads through that L2 (each record line is read
+// only after the team barrier, and only once); the team counters are atomics.
+// A barrier that runs out of spins sets bit 1 of the status word and turns the
+// team's outputs into NaN rather than leaving plausible wrong values.  (Teams of
+// one workgroup per CU keep the members in step: with two 256-thread workgroups
+// per CU the younger one lost the issue arbitration and every barrier waited
+// for it.)
+// stage_q for the threads t0 .. of a group of nthr (tile0 = 0).
+template <int D, int TG>
+__device__ __forceinline__ void stage_q_part(const uint16_t* q, const Geo& g, int kvh, uint4* qlds, int t0,
+                                             int nthr) {
+  constexpr int S = D / 16, C = D / 8;
+  for (int f = t0; f < TG * 32 * C; f += nthr) {
+    const int c16 = f % C, i = (f / C) % 32, t = f / (32 * C);
+    const int hf = c16 & 1, st = c16 >> 1;
+    const int head = kvh * g.G + t / g.tph;
+    const int rr = (t % g.tph) * 32 + i;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (rr < g.w) v = *reinterpret_cast<const uint4*>(q + ((int64_t)head * g.w + rr) * D + c16 * 8);
+    qlds[(t * S + st) * 64 + hf * 32 + i] = v;
+  }
+}
+
+constexpr int kXcds = 8;
+constexpr int NTX = 512;             // threads per workgroup
+constexpr int kXRows = 128;          // partial record stride (rows, 512 bytes)
+constexpr int kXCntStride = 32;      // team counters 128 bytes apart
+constexpr int kXSpinLimit = 1 << 20; // polls before a team barrier gives up (seconds)
+constexpr int kXMaxTeam = 32;        // workgroups per team at most (one XCD, one per CU)
+constexpr int kXMaxRec = kXMaxTeam / 2;   // records each merging thread reads (>= 2 threads per row)
+
+struct XArgs {
+  ConstPtrs q, k;                    // per-layer pointers of the current layer group
+  Geo g;
+  float sl2;                         // scale * log2(e)
+  int per_head;
+  int nunits;                        // (layer, KV head) units of the group
+  int tw;                            // workgroups per team
+  int tpx;                           // teams per XCD (workgroups past tpx * tw idle)
+  int nteams;                        // teams on the chip (kXcds * tpx)
+  int stagger;                       // start delay of odd XCDs, in 10 ns ticks
+  float* part;                       // [nunits][kXRows][kXMaxTeam] row log-normalisers of each member
+  unsigned* cnt;                     // [nunits][kXCntStride] team counters (first word used)
+  unsigned* status;                  // bit 1: a barrier gave up; bit 2: an XCD beyond kXcds
+  unsigned* reg;                     // [kXcds] slots taken on each XCD
+  float* A;                          // output of the layer group
+};
+
+template <int D, int NT>
+struct XSmem {
+  uint4 q[2][NT * (D / 16) * 64];                // Q of this unit and of the next, fragment order
+  float2 wst[NTX / 64][NT * 32];                 // pass 1: per-wave row stats
+  __attribute__((aligned(16))) float c[NT * 32]; // pass 2: row normalisers
+  float2 red[NTX];                               // partial merges
+  int ok;                                        // team barrier completed
+  int xcc, slot;                                 // this workgroup's XCD and its slot there
+};
+
+// Keys of one unit for this wave: blocks b0 .. b0 + KBM - 1 of 32 keys, in the
+// MFMA k layout (step st, half hf: elements 16 st + 8 hf .. + 8 of key i).  Rows
+// past the end of K are clamped to the last key, so the loads are unconditional.
+template <int D, int KBM>
+__device__ __forceinline__ void x_load_block(bf16x8 (&kr)[D / 16], const XArgs& a, int u, int64_t key0,
+                                             int lane) {
+  constexpr int S = D / 16;
+  const int l = u / a.g.Hkv, kvh = u % a.g.Hkv;
+  const int i = lane & 31, hf = lane >> 5;
+  const uint16_t* kh = (const uint16_t*)a.k.p[l] + (int64_t)kvh * a.g.n * D;
+  const int64_t key = min(key0 + i, a.g.n - 1);
+  const uint16_t* p = kh + key * D + 8 * hf;
+#pragma unroll
+  for (int st = 0; st < S; ++st) kr[st] = *reinterpret_cast<const bf16x8*>(p + 16 * st);
+}
+
+template <int D, int NT, bool PH>
+__global__ void __launch_bounds__(NTX) __attribute__((amdgpu_waves_per_eu(2, 2)))
+win_xcd(XArgs a) {
+  constexpr int S = D / 16, KBM = 512 / D, R = NT * 32;
+  __shared__ XSmem<D, NT> sm;
+  const Geo& g = a.g;
+  const int lane = threadIdx.x & 63, hf = lane >> 5, qi = lane & 31;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
+  // this workgroup's XCD (hardware register XCC_ID) and its slot there
+  if (threadIdx.x == 0) {
+    const int xcc = (int)(__builtin_amdgcn_s_getreg((3 << 11) | 20) & 15);
+    int slot = 1 << 20;                          // no team
+    if (xcc < kXcds) slot = (int)__hip_atomic_fetch_add(&a.reg[xcc], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else __hip_atomic_fetch_or(a.status, 4u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    sm.xcc = xcc;
+    sm.slot = slot;
+  }
+  __syncthreads();
+  const int x = __builtin_amdgcn_readfirstlane(sm.xcc), rank = __builtin_amdgcn_readfirstlane(sm.slot);
+  const int team = rank / a.tw, mem = rank % a.tw;
+  const int first = team * kXcds + x;
+  if (team >= a.tpx || first >= a.nunits) return;   // whole workgroup: no team, or no unit
+  const int64_t nblk = (g.n + 31) / 32;
+  const int64_t b0 = (int64_t)(mem * (NTX / 64) + wv) * KBM;     // this wave's first key block
+  const int nb = (int)max((int64_t)0, min((int64_t)KBM, nblk - b0));
+  const int64_t safe_end = g.n - g.w;            // keys <= this are seen by every row
+  const float inv_group = 1.0f / (float)(g.G * g.w), inv_w = 1.0f / (float)g.w;
+
+  int pos[NT];                                   // window position of this lane's row (pass 1)
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    pos[t] = qi < g.w ? (int)(g.n - g.w) + qi : -1;
+  }
+
+  bf16x8 kr[KBM][S];
+  {
+    const int u = first;
+    stage_q_part<D, NT>((const uint16_t*)a.q.p[u / g.Hkv], g, u % g.Hkv, sm.q[0], threadIdx.x, NTX);
+#pragma unroll
+    for (int b = 0; b < KBM; ++b) x_load_block<D, KBM>(kr[b], a, u, (b0 + b) * 32, lane);
+    __syncthreads();
+  }
+  // Odd XCDs start about half a unit later.  The XCDs then take turns: while
+  // one half streams the next unit's keys (pass 2), the other half computes
+  // pass 1 and meets at its barrier, instead of all eight loading at once.
+  if (x & 1) {
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();    // 100 MHz
+    while (__builtin_amdgcn_s_memrealtime() - t0 < (uint64_t)a.stagger) __builtin_amdgcn_s_sleep(8);
+  }
+  // pass 1 of unit u (keys in kr, Q in ql), its record, and the arrival at the
+  // unit's team barrier
+  auto do_p1 = [&](int u, const uint4* ql, int64_t bk) __attribute__((always_inline)) {
+    // ---- pass 1: per-lane online (max, sum of exp2) of each row over this wave's keys
+    float m[NT], sx[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) { m[t] = -INFINITY; sx[t] = 0.f; }
+    auto p1 = [&](const bf16x8 (&kc)[S], int64_t j0, auto full_t, auto fixed_t) __attribute__((always_inline)) {
+      constexpr bool full = decltype(full_t)::value;
+      constexpr bool fixed = decltype(fixed_t)::value;
+      int qo = lane;
+      asm volatile("" : "+v"(qo));               // keep the Q reads in the loop (LDS, not VGPRs)
+      auto epi = [&](int t, f32x16 acc) __attribute__((always_inline)) {
+        if constexpr (fixed) {
+          float sum = __builtin_amdgcn_exp2f(fmaf(acc[0], a.sl2, -m[t]));
+#pragma unroll
+          for (int v = 1; v < 16; ++v) sum += __builtin_amdgcn_exp2f(fmaf(acc[v], a.sl2, -m[t]));
+          sx[t] += sum;
+          return;
+        }
+        float bm = -INFINITY;
+        if constexpr (full) {
+#pragma unroll
+          for (int v = 0; v < 16; ++v) bm = fmaxf(bm, acc[v]);
+        } else {
+          // key offset limit within the block.  The mask is a min with +inf or
+          // -inf whose sign comes from lim - off (sign-bit arithmetic, no
+          // compares), so it needs no per-element compare masks in SGPRs.
+          const int lim = (int)(min((int64_t)pos[t], g.n - 1) - j0) - 4 * hf;
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int off = 8 * (v >> 2) + (v & 3);
+            const float cap = __uint_as_float(((unsigned)(lim - off) & 0x80000000u) | 0x7f800000u);
+            acc[v] = fminf(acc[v], cap);
+            bm = fmaxf(bm, acc[v]);
+          }
+        }
+        const float mn = fmaxf(m[t], bm * a.sl2);
+        const float ms = full ? mn : (mn > -INFINITY ? mn : 0.f);
+        float sum = 0.f;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) sum += __builtin_amdgcn_exp2f(fmaf(acc[v], a.sl2, -ms));
+        sx[t] = sx[t] * __builtin_amdgcn_exp2f(m[t] - ms) + sum;
+        m[t] = mn;
+      };
+      pipelined_tiles<S, NT, true>(kc, ql, qo, epi);
+    };
+#pragma unroll
+    for (int b = 0; b < KBM; ++b) {
+      if (b < nb) {                              // wave-uniform
+        const int64_t j0 = (bk + b) * 32;
+        if (j0 + 31 <= safe_end) {
+          if (b > 0) p1(kr[b], j0, std::true_type{}, std::true_type{});
+          else p1(kr[b], j0, std::true_type{}, std::false_type{});
+        } else {
+          p1(kr[b], j0, std::false_type{}, std::false_type{});
+        }
+      }
+    }
+    bool bad = false;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) bad = bad || !(sx[t] <= 3.0e38f);     // inf or NaN
+    if (__builtin_amdgcn_ballot_w64(bad) != 0) {  // again with the running maximum
+#pragma unroll
+      for (int t = 0; t < NT; ++t) { m[t] = -INFINITY; sx[t] = 0.f; }
+#pragma unroll
+      for (int b = 0; b < KBM; ++b) {
+        if (b < nb) {
+          const int64_t j0 = (bk + b) * 32;
+          if (j0 + 31 <= safe_end) p1(kr[b], j0, std::true_type{}, std::false_type{});
+          else p1(kr[b], j0, std::false_type{}, std::false_type{});
+        }
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {               // halves (lanes i, i+32 share a row), then waves
+      const float mo = __shfl_xor(m[t], 32, 64), so = __shfl_xor(sx[t], 32, 64);
+      const float M = fmaxf(m[t], mo);
+      float Sx = 0.f;
+      if (M > -INFINITY) Sx = sx[t] * exp2f(m[t] - M) + so * exp2f(mo - M);
+      if (hf == 0) sm.wst[wv][t * 32 + qi] = make_float2(M, Sx);
+    }
+    __syncthreads();
+    if (threadIdx.x < R) {
+      float M = -INFINITY;
+#pragma unroll
+      for (int w2 = 0; w2 < NTX / 64; ++w2) M = fmaxf(M, sm.wst[w2][threadIdx.x].x);
+      float Sx = 0.f;
+      if (M > -INFINITY) {
+#pragma unroll
+        for (int w2 = 0; w2 < NTX / 64; ++w2)
+          if (sm.wst[w2][threadIdx.x].x > -INFINITY)
+            Sx += sm.wst[w2][threadIdx.x].y * exp2f(sm.wst[w2][threadIdx.x].x - M);
+      }
+      a.part[((int64_t)u * kXRows + threadIdx.x) * kXMaxTeam + mem] = Sx > 0.f ? M + log2f(Sx) : -INFINITY;
+      __builtin_amdgcn_s_waitcnt(0xF70);         // vmcnt(0): the record is in L2 before we count
+    }
+    __syncthreads();
+    if (threadIdx.x == 0)
+      __hip_atomic_fetch_add(&a.cnt[(int64_t)u * kXCntStride], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
+  auto wait_team = [&](int u) __attribute__((always_inline)) {
+    if (threadIdx.x == 0) {
+      int it = 0;
+      for (; it < kXSpinLimit; ++it) {
+        unsigned z = 0;
+        asm volatile("" : "+v"(z));              // a real read-modify-write: it reads the atomic's value
+        if (__hip_atomic_fetch_add(&a.cnt[(int64_t)u * kXCntStride], z, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT) >= (unsigned)a.tw)
+          break;
+        __builtin_amdgcn_s_sleep(2);
+      }
+      sm.ok = it < kXSpinLimit;
+      if (it == kXSpinLimit) __hip_atomic_fetch_or(a.status, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+  };
+  auto merge_c = [&](int u) __attribute__((always_inline)) {
+    // ---- row normalisers: thread j of a row merges the j-th run of kXMaxRec
+    // members, then the runs are merged in order (a fixed order: the result
+    // does not depend on arrival); +inf for padding rows, NaN if the barrier
+    // gave up
+    {
+      constexpr int P = NTX / R;
+      const int r = threadIdx.x % R, j = threadIdx.x / R;
+      if (j < P) {
+        // members j*kXMaxRec .. +kXMaxRec of row r, contiguous: eight 16-byte
+        // loads requested at once (one L2 round trip); members past the team
+        // are read from the row's padding and ignored
+        float M = -INFINITY, Sx = 0.f;
+        if (j * kXMaxRec < a.tw) {
+          const float4* pr = reinterpret_cast<const float4*>(a.part + ((int64_t)u * kXRows + r) * kXMaxTeam + j * kXMaxRec);
+          float v[kXMaxRec];
+#pragma unroll
+          for (int e = 0; e < kXMaxRec / 4; ++e) {
+            const float4 f = pr[e];
+            v[4 * e] = f.x; v[4 * e + 1] = f.y; v[4 * e + 2] = f.z; v[4 * e + 3] = f.w;
+          }
+#pragma unroll
+          for (int e = 0; e < kXMaxRec; ++e)
+            if (j * kXMaxRec + e >= a.tw) v[e] = -INFINITY;
+#pragma unroll
+          for (int e = 0; e < kXMaxRec; ++e) M = fmaxf(M, v[e]);
+          if (M > -INFINITY) {                   // independent terms, summed as a tree
+            float t[kXMaxRec];
+#pragma unroll
+            for (int e = 0; e < kXMaxRec; ++e) t[e] = exp2f(v[e] - M);
+#pragma unroll
+            for (int h = kXMaxRec / 2; h > 0; h /= 2)
+#pragma unroll
+              for (int e = 0; e < h; ++e) t[e] += t[e + h];
+            Sx = t[0];
+          }
+        }
+        sm.red[j * R + r] = make_float2(M, Sx);
+      }
+      __syncthreads();
+      if (threadIdx.x < R) {
+        float Mt = -INFINITY, St = 0.f;
+        for (int jj = 0; jj < P; ++jj) {
+          const float2 v = sm.red[jj * R + r];
+          if (v.x > -INFINITY) {
+            const float mn = fmaxf(Mt, v.x);
+            St = St * exp2f(Mt - mn) + v.y * exp2f(v.x - mn);
+            Mt = mn;
+          }
+        }
+        const bool pad = (r & 31) >= g.w;
+        float cr = (!pad && Mt > -INFINITY) ? Mt + log2f(St) : INFINITY;
+        if (!sm.ok) cr = __builtin_nanf("");
+        sm.c[r] = cr;
+      }
+      __syncthreads();
+    }
+
+  };
+  // pass 2 of unit u; each key block's registers then take the same block of
+  // unit uload (the team's next unit, or u again after its last)
+  auto do_p2 = [&](int u, int uload, const uint4* ql, int64_t bk) __attribute__((always_inline)) {
+    const int l = u / g.Hkv, kvh = u % g.Hkv;
+    // ---- pass 2: column sums of exp2(s - c_r); each block's registers then take
+    // the same block of the team's next unit.  No load is in flight here (pass 1
+    // consumed every key); saying so lets the compiler see that pass 2's reads of
+    // the key registers wait for nothing, not for the next unit's loads.
+    __builtin_amdgcn_s_waitcnt(0xF70);           // vmcnt(0)
+    auto p2 = [&](const bf16x8 (&kc)[S], int64_t j0, auto full_t) __attribute__((always_inline)) {
+      constexpr bool full = decltype(full_t)::value;
+      const int64_t key = j0 + qi;               // this lane's key column
+      int qo = lane, co = hf;
+      asm volatile("" : "+v"(qo), "+v"(co));
+      float hs[NT];
+      auto epi = [&](int t, const f32x16& acc) __attribute__((always_inline)) {
+        const int base = 4 * hf;
+        const int lo = (int)(key - safe_end) - base;
+        const int hi = (key < g.n) ? g.w - base : -1;
+        float colsum = 0.f;
+        int cot = co;                            // c reads of tile t not before its epilogue
+        asm volatile("" : "+v"(cot));
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd) {
+          const float4 c4 = reinterpret_cast<const float4*>(sm.c)[t * 8 + 2 * qd + cot];
+          const float cc[4] = {c4.x, c4.y, c4.z, c4.w};
+#pragma unroll
+          for (int uu = 0; uu < 4; ++uu) {
+            const int v = 4 * qd + uu, off = 8 * qd + uu;
+            float z = fmaf(acc[v], a.sl2, -cc[uu]);
+            if constexpr (!full) {                 // rows lo <= off < hi only: -inf otherwise
+              const unsigned sg = (unsigned)((off - lo) | (hi - 1 - off)) & 0x80000000u;
+              z = fminf(z, __uint_as_float(sg | 0x7f800000u));
+            }
+            colsum += __builtin_amdgcn_exp2f(z);
+          }
+        }
+        hs[t] = colsum;
+      };
+      pipelined_tiles<S, NT, false>(kc, ql, qo, epi);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) asm volatile("" : "+v"(hs[t]));
+      if constexpr (PH) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {           // one tile per query head
+          const float cs = add_halves(hs[t]);
+          if (hf == 0 && key < g.n) a.A[((int64_t)l * g.Hq + kvh * g.G + t) * g.n + key] = cs * inv_w;
+        }
+      } else {
+        float own = hs[0];
+#pragma unroll
+        for (int t = 1; t < NT; ++t) own += hs[t];
+        const float total = add_halves(own);
+        if (hf == 0 && key < g.n) a.A[((int64_t)l * g.Hkv + kvh) * g.n + key] = total * inv_group;
+      }
+    };
+#pragma unroll
+    for (int b = 0; b < KBM; ++b) {
+      if (b < nb) {
+        const int64_t j0 = (bk + b) * 32;
+        if (j0 + 31 <= safe_end) p2(kr[b], j0, std::true_type{});
+        else p2(kr[b], j0, std::false_type{});
+      }
+      x_load_block<D, KBM>(kr[b], a, uload, (bk + b) * 32, lane);
+    }
+  };
+  int64_t bk0 = b0;
+  asm volatile("" : "+s"(bk0));
+  do_p1(first, sm.q[0], bk0);
+  if (wv > 0 && first + a.nteams < a.nunits)     // waves 1..3 stage the next Q while wave 0 waits
+    stage_q_part<D, NT>((const uint16_t*)a.q.p[(first + a.nteams) / g.Hkv], g, (first + a.nteams) % g.Hkv,
+                        sm.q[1], threadIdx.x - 64, NTX - 64);
+  int qb = 0;
+#pragma unroll 1
+  for (int u = first; u < a.nunits; u += a.nteams, qb ^= 1) {
+    const int un = u + a.nteams;                 // this team's next unit
+    const bool more = un < a.nunits;
+    // the key offsets are the same for every unit; made opaque here so that the
+    // masks derived from them are computed per unit, not hoisted out of the loop
+    // and held in registers across it
+    int64_t bk = b0;
+    asm volatile("" : "+s"(bk));
+    wait_team(u);
+    merge_c(u);
+    // No load is in flight here (pass 1 consumed every key); saying so lets the
+    // compiler see that pass 2's reads of the key registers wait for nothing.
+    __builtin_amdgcn_s_waitcnt(0xF70);           // vmcnt(0)
+    do_p2(u, more ? un : u, sm.q[qb], bk);
+    __syncthreads();                             // c and this unit's Q are rewritten next
+    if (more) {
+      // pass 1 of the next unit right behind the loads pass 2 issued, in the same
+      // straight-line code, so that each block waits only for its own keys
+      do_p1(un, sm.q[qb ^ 1], bk);
+      const int un2 = un + a.nteams;
+      if (wv > 0 && un2 < a.nunits)
+        stage_q_part<D, NT>((const uint16_t*)a.q.p[un2 / g.Hkv], g, un2 % g.Hkv, sm.q[qb], threadIdx.x - 64, NTX - 64);
+    }
+  }
+}
+
+__global__ void win_xcd_zero(unsigned* p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+
 // ---------------------------------------------------------------- float32 path
 // Plain vector-ALU version for float32 inputs (small shapes).  Rows are indexed
 // (head in group, window row) without padding.
@@ -575,6 +996,10 @@ struct Plan {
   bool mfma;
   int lch;                      // layers per chunk
   size_t part_bytes, c_bytes;
+  // XCD-resident kernel: the shape fits it, workgroups per team, workspace
+  bool xshape;
+  int xtw;
+  size_t x_head_bytes, x_part_bytes;
 };
 
 void make_plan(int L, int Hq, int Hkv, int64_t n, int w, int d, int dtype, Plan* P) {
@@ -604,6 +1029,62 @@ void make_plan(int L, int Hq, int Hkv, int64_t n, int w, int d, int dtype, Plan*
     P->part_bytes = 0;
     P->c_bytes = (size_t)lg_max * Hkv * g.G * w * sizeof(float);
   }
+  // XCD-resident kernel: one tile per head (w <= 32), each wave holds 512/d key
+  // blocks, a team is at most one XCD's workgroups (checked against the device at
+  // launch).  Workspace: status word, XCD slot counters, team counters, records.
+  P->xshape = false;
+  P->xtw = 0;
+  P->x_head_bytes = P->x_part_bytes = 0;
+  if (P->mfma && (d == 64 || d == 128) && g.tph == 1 && g.ntiles <= MAX_TG) {
+    const int64_t kbm = 512 / d, nblk = (n + 31) / 32, per_wg = (NTX / 64) * kbm;
+    const int64_t tw = (nblk + per_wg - 1) / per_wg;
+    if (tw <= kXMaxTeam) {
+      P->xshape = true;
+      P->xtw = (int)tw;
+      P->x_head_bytes = 256 + (size_t)lg_max * Hkv * kXCntStride * sizeof(unsigned);
+      P->x_part_bytes = (size_t)lg_max * Hkv * kXRows * kXMaxTeam * sizeof(float);
+    }
+  }
+}
+
+// Dynamic LDS that takes a workgroup of the XCD-resident kernel past half of a
+// CU's 160 KB, so that a CU holds one (the slot counting relies on it).
+constexpr size_t kXMinLds = 80 * 1024 + 256;
+
+template <int D, int NT, bool PH>
+bool launch_xcd_t(XArgs a, hipStream_t s) {
+  const void* kern = reinterpret_cast<const void*>(&win_xcd<D, NT, PH>);
+  const size_t stat = sizeof(XSmem<D, NT>);
+  const size_t dyn = stat < kXMinLds ? kXMinLds - stat : 0;
+  int dev = 0, ncu = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, NTX, dyn) != hipSuccess)
+    return false;
+  if (per_cu != 1 || ncu <= 0 || ncu % kXcds) return false;
+  const int wpx = ncu / kXcds;                   // workgroups on each XCD
+  if (wpx < a.tw) return false;
+  a.tpx = wpx / a.tw;
+  a.nteams = kXcds * a.tpx;
+  if (a.nunits <= a.nteams) a.stagger = 0;      // one unit per team: nothing to interleave
+  void* args[] = {&a};
+  // cooperative: every workgroup resident at once (the team barriers need it)
+  return hipLaunchCooperativeKernel(kern, dim3((unsigned)ncu), dim3(NTX), args, (unsigned)dyn, s) == hipSuccess;
+}
+
+template <int D, bool PH>
+bool launch_xcd_d(const XArgs& a, hipStream_t s) {
+  switch (a.g.ntiles) {
+    case 1: return launch_xcd_t<D, 1, PH>(a, s);
+    case 2: return launch_xcd_t<D, 2, PH>(a, s);
+    case 3: return launch_xcd_t<D, 3, PH>(a, s);
+    default: return launch_xcd_t<D, 4, PH>(a, s);
+  }
+}
+
+bool launch_xcd(const XArgs& a, hipStream_t s) {
+  if (a.g.d == 64) return a.per_head ? launch_xcd_d<64, true>(a, s) : launch_xcd_d<64, false>(a, s);
+  return a.per_head ? launch_xcd_d<128, true>(a, s) : launch_xcd_d<128, false>(a, s);
 }
 
 // Workgroups of `kern` resident at once on the current device.
@@ -664,7 +1145,8 @@ extern "C" size_t kvc_score_window_attn_workspace_size(int L, int Hq, int Hkv, i
   if (L < 1 || Hkv < 1 || Hq < Hkv || n < 1 || w < 1 || d < 1) return 0;
   Plan P;
   make_plan(L, Hq, Hkv, n, w, d, dtype, &P);
-  return P.part_bytes + P.c_bytes + 256;
+  const size_t two = P.part_bytes + P.c_bytes, xcd = P.x_head_bytes + P.x_part_bytes;
+  return (two > xcd ? two : xcd) + 256;
 }
 
 extern "C" int kvc_score_window_attn(const void* const* q_win, const void* const* k, int dtype,
@@ -701,6 +1183,7 @@ extern "C" int kvc_score_window_attn(const void* const* q_win, const void* const
                 "kvc_score_window_attn: float32 path needs (Hq/Hkv)*w*d*4 <= 64 KB");
   }
   const size_t need = P.part_bytes + P.c_bytes;
+  const size_t xneed = P.x_head_bytes + P.x_part_bytes;
   char* base = ws ? (char*)(((uintptr_t)ws + 255) & ~(uintptr_t)255) : nullptr;
   if (!ws || (size_t)(base - (char*)ws) + need > ws_bytes)
     return KVC_FAIL(KVC_ERR_WORKSPACE, "kvc_score_window_attn: workspace needs %zu bytes", need + 256);
@@ -715,7 +1198,34 @@ extern "C" int kvc_score_window_attn(const void* const* q_win, const void* const
     ConstPtrs qt{}, kt{};
     for (int i = 0; i < lc; ++i) { qt.p[i] = q_win[l0 + i]; kt.p[i] = k[l0 + i]; }
     float* A = A_out + (int64_t)l0 * Aheads * n;
-    if (P.mfma) {
+    bool done = false;
+    if (P.xshape && (size_t)(base - (char*)ws) + xneed <= ws_bytes) {
+      // keys read once; not under stream capture (cooperative launch), and the
+      // two-pass kernel below when the device cannot hold the grid
+      hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+      if (hipStreamIsCapturing(s, &cs) == hipSuccess && cs == hipStreamCaptureStatusNone) {
+        XArgs xa{};
+        xa.q = qt; xa.k = kt; xa.g = g; xa.sl2 = sl2; xa.per_head = per_query_head;
+        xa.nunits = lc * Hkv;
+        xa.tw = P.xtw;
+        // odd XCDs start about half a unit's time later (10 us at 1024 key
+        // blocks), when the teams have more than one unit each
+        const int64_t nblk = (n + 31) / 32;
+        xa.stagger = (int)(nblk * 1000 / 1024);
+        xa.status = (unsigned*)base;
+        xa.reg = (unsigned*)(base + 64);
+        xa.cnt = (unsigned*)(base + 256);
+        xa.part = (float*)(base + P.x_head_bytes);
+        xa.A = A;
+        // status and counters start at zero (a fill kernel, not a memset)
+        const int nz = (int)(P.x_head_bytes / sizeof(unsigned));
+        hipLaunchKernelGGL(win_xcd_zero, dim3((nz + 255) / 256), dim3(256), 0, s, (unsigned*)base, nz);
+        done = launch_xcd(xa, s);
+        if (!done) (void)hipGetLastError();      // the two-pass kernel takes over
+      }
+    }
+    if (done) {
+    } else if (P.mfma) {
       WinArgs a{};
       a.q = qt; a.k = kt; a.g = g; a.sl2 = sl2; a.per_head = per_query_head;
       a.part = part; a.A = A;

@@ -275,6 +275,36 @@ def test_window_attention(dev, case, per_head):
 
 
 @pytest.mark.parametrize("per_head", [False, True])
+@pytest.mark.parametrize("case", [WIN_CASES[2], WIN_CASES[5], WIN_CASES[6], WIN_CASES[8]], ids=str)
+def test_window_attention_graph_replays(dev, case, per_head):
+    """Under stream capture the call takes the two-pass kernel (the kernel that
+    keeps each unit's keys in registers needs a cooperative launch, which is not
+    captured): every replay of the captured graph, with eager work and
+    synchronisation between replays, matches the oracle."""
+    L, Hq, Hkv, n, w, d, dtype = case
+    announce("window_attn_graph", case, per_head)
+    q = [gen((Hq, w, d), 20 + l, dev, dtype) for l in range(L)]
+    k = [gen((Hkv, n, d), 40 + l, dev, dtype) for l in range(L)]
+    A = torch.empty(L, Hq if per_head else Hkv, n, device=dev)
+    dt = 1 if dtype == torch.bfloat16 else 0
+    ws = torch.empty(B().kvc_score_window_attn_workspace_size(L, Hq, Hkv, n, w, d, dt),
+                     dtype=torch.uint8, device=dev)
+    B().kvc_score_window_attn(q, k, 1 / math.sqrt(d), per_head, A, ws=ws)    # eager call first
+    torch.cuda.synchronize()
+    refs = [infokv.window_attention(host_f64(q[l]), host_f64(k[l]), per_query_head=per_head)
+            for l in range(L)]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        B().kvc_score_window_attn(q, k, 1 / math.sqrt(d), per_head, A, ws=ws)
+    for rep in range(3):
+        A.fill_(-1.0)
+        graph.replay()
+        torch.cuda.synchronize()
+        for l in range(L):
+            assert_rel(A[l].cpu().numpy(), refs[l], 1e-3, what=f"replay {rep} layer {l}")
+
+
+@pytest.mark.parametrize("per_head", [False, True])
 def test_window_attention_late_dominant_keys(dev, per_head):
     """Keys whose logit for one window row lies far (over 2^7 in log2 units) above
     everything the row met before in the same 512-key stretch of K: pass 1 must
