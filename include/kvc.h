@@ -103,7 +103,15 @@ int kvc_repr_distance(const void* const* h_layers, const void* h_final, int dtyp
  *   scale: finite and > 0 (1/sqrt(d) in the pages' attention).
  *   1 <= w <= n; Hq % Hkv == 0; bf16 needs d in {64, 128} and
  *   (Hq/Hkv) * ceil(w/32) <= 8; float32 needs d <= 256.
- *   ws         device workspace, kvc_score_window_attn_workspace_size() bytes.
+ *   ws         device workspace, kvc_score_window_attn_workspace_size() bytes;
+ *              calls that share one workspace must not overlap.
+ * Two bf16 kernels: when one (layer, KV head)'s keys fit the registers of one
+ * XCD (w <= 32, (Hq/Hkv) <= 4, n <= 32768 at d = 128 or 65536 at d = 64) they
+ * are read once, by a cooperative launch that holds every CU while it runs;
+ * otherwise, under stream capture, or when the device cannot hold that grid
+ * (or the workspace is smaller than the size above), two passes read them
+ * twice.  If the cooperative grid were ever not resident at once, its team
+ * barriers give up after about a second and write NaN for the affected units.
  */
 size_t kvc_score_window_attn_workspace_size(int L, int Hq, int Hkv, int64_t n,
                                             int w, int d, int dtype);
