@@ -435,6 +435,23 @@ __device__ __forceinline__ void pass2(const WinArgs& a, WinSmem<D, TG>& sm, int 
       for (int t = 1; t < TG; ++t) own += hs[t];
       total = add_halves(own);
     }
+    if (PH && g.tph == 1) {                      // one tile per head (w <= 32): no sums over tiles
+      // both halves hold every head's column sum; the upper half stores the
+      // next head, so one store instruction writes two heads' 32 keys
+      float cs[TG];
+#pragma unroll
+      for (int t = 0; t < TG; ++t) cs[t] = add_halves(hs[t]);
+#pragma unroll
+      for (int t = 0; t < TG; t += 2) {
+        const bool two = t + 1 < TG;
+        const float v = (two && hf) ? cs[t + 1] : cs[t];
+        if ((two || hf == 0) && key < g.n) {
+          const int head = kvh * g.G + a.tile0 + t + (two ? hf : 0);
+          A[((int64_t)l * g.Hq + head) * g.n + key] = v * inv_w;
+        }
+      }
+      return;
+    }
 #pragma unroll
     for (int t = 0; t < TG; ++t) {
       if constexpr (PH) {
