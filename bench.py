@@ -54,8 +54,9 @@ def algorithmic_bytes(w, k_list):
         out["select_topk"] = L * Hkv * n * 4 + kept * 4
         out["compact"] = 2 * 2 * kept * d * e + kept * 4
     else:
-        out["window_attn"] = L * Hkv * n * d * e + L * Hq * w.window * d * e + L * Hq * n * 4
-        out["vatp_union"] = L * Hkv * n * d * e + L * Hq * n * 4 + 2 * L * Hkv * n * 4
+        # group mean and group max written; the union reads V and the max, writes U
+        out["window_attn"] = L * Hkv * n * d * e + L * Hq * w.window * d * e + 2 * L * Hkv * n * 4
+        out["vatp_union"] = L * Hkv * n * d * e + 2 * L * Hkv * n * 4
         out["select_topk"] = L * Hkv * n * 4 + kept * 4
         # V read, kept K read, K_c and V'_c written, A read, ln R written
         out["merge_gated"] = L * Hkv * n * d * e + 3 * kept * d * e + L * Hkv * n * 4 + kept * 8

@@ -97,6 +97,11 @@ int kvc_repr_distance(const void* const* h_layers, const void* h_final, int dtyp
  *   P[h, r, j] = softmax over j <= p_r of scale * <q[l][h, r, :], k[l][g, j, :]>
  *   per_query_head = 1:  A[l, h, j] = (1/w) sum_r P[h, r, j]          [L, Hq, n]
  *   per_query_head = 0:  A[l, g, j] = mean over the group's heads      [L, Hkv, n]
+ *   per_query_head = 2:  A_out[0, l, g, j] = the group mean (as 0) and
+ *                        A_out[1, l, g, j] = max over the group's heads of
+ *                        A[l, h, j] (as 1)                          [2, L, Hkv, n]
+ *                        (what SelKV's VATP union and merge need, without
+ *                        the per-head rows; bf16 needs w <= 32, Hq/Hkv <= 4)
  *   q_win      host array of L device pointers, each [Hq, w, d] of dtype.
  *   k          host array of L device pointers, each [Hkv, n, d] of dtype.
  *   A_out      device float32, shape above.  Every row of A sums to 1.
@@ -263,6 +268,18 @@ int kvc_compact_into(const void* const* K, const void* const* V, int dtype, int 
  */
 int kvc_vatp_union(const float* A_hq, const void* const* V, int dtype, int L, int Hq,
                    int Hkv, int64_t n, int d, float* U_out, float* Ag_out, void* stream);
+
+/*
+ * The VATP union from the group max of the attention ([SelKV] section 2,
+ * pipeline steps 1-2): U_out[l, g, j] = A_gmax[l, g, j] * ||v[l][g, j, :]||_2,
+ * equal to kvc_vatp_union's U (max_h (A_h * ||v||) = (max_h A_h) * ||v|| for
+ * ||v|| >= 0, and a rounded product is monotone in each factor).
+ *   A_gmax     device float32 [L, Hkv, n]: plane 1 of kvc_score_window_attn
+ *              with per_query_head = 2 (its plane 0 is A_g).
+ *   V          as kvc_vatp_union.   U_out  device float32 [L, Hkv, n].
+ */
+int kvc_vatp_union_gmax(const float* A_gmax, const void* const* V, int dtype, int L,
+                        int Hkv, int64_t n, int d, float* U_out, void* stream);
 
 /*
  * Selective gated merge with attention compensation ([SelKV] section 2: soft

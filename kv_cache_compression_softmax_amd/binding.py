@@ -42,6 +42,7 @@ _SIGNATURES = {
     "kvc_select_topk": ([_vp, _i32, _i32, _i64, _c_i64p, _i32, _vp, _vp], _i32),
     "kvc_compact": ([_vp, _vp, _i32, _i32, _i32, _i64, _i32, _vp, _c_i64p, _vp, _vp, _vp], _i32),
     "kvc_vatp_union": ([_vp, _vp, _i32, _i32, _i32, _i32, _i64, _i32, _vp, _vp, _vp], _i32),
+    "kvc_vatp_union_gmax": ([_vp, _vp, _i32, _i32, _i32, _i64, _i32, _vp, _vp], _i32),
     "kvc_merge_gated": ([_vp, _vp, _i32, _vp, _i32, _i32, _i64, _i32, _vp, _c_i64p, _i32, _vp, _vp,
                          _vp, _vp], _i32),
     "kvc_compact_into": ([_vp, _vp, _i32, _i32, _i32, _i64, _i32, _vp, _c_i64p, _i64, _vp, _vp, _vp],
@@ -170,9 +171,11 @@ def kvc_score_window_attn_workspace_size(L, Hq, Hkv, n, w, d, dtype) -> int:
     return lib().kvc_score_window_attn_workspace_size(L, Hq, Hkv, n, w, d, dtype)
 
 
-def kvc_score_window_attn(q_win, k, scale: float, per_query_head: bool, A_out: torch.Tensor,
+def kvc_score_window_attn(q_win, k, scale: float, per_query_head, A_out: torch.Tensor,
                           ws: torch.Tensor | None = None, stream=None):
-    """A_out [L, Hkv or Hq, n] from per-layer q_win [Hq, w, d] and k [Hkv, n, d]."""
+    """A_out from per-layer q_win [Hq, w, d] and k [Hkv, n, d]: [L, Hkv, n] for
+    per_query_head 0 (or False), [L, Hq, n] for 1 (or True), [2, L, Hkv, n]
+    (group mean, group max over heads) for 2."""
     L = len(k)
     Hq, w, d = q_win[0].shape
     Hkv, n, _ = k[0].shape
@@ -323,6 +326,17 @@ def kvc_vatp_union(A_hq: torch.Tensor, V, U_out: torch.Tensor, Ag_out: torch.Ten
         _ptr(A_hq, torch.float32), vp, _dtype(V[0]), L, Hq, Hkv, n, d,
         _ptr(U_out, torch.float32), _ptr(Ag_out, torch.float32), _stream(stream)))
     return U_out, Ag_out
+
+
+def kvc_vatp_union_gmax(A_gmax: torch.Tensor, V, U_out: torch.Tensor, stream=None):
+    """U_out = A_gmax * ||v|| (A_gmax: the group max over heads, [L, Hkv, n])."""
+    L, Hkv, n = A_gmax.shape
+    d = V[0].shape[2]
+    vp, keep = _ptrs(V, V[0].dtype)
+    _check("kvc_vatp_union_gmax", lib().kvc_vatp_union_gmax(
+        _ptr(A_gmax, torch.float32), vp, _dtype(V[0]), L, Hkv, n, d,
+        _ptr(U_out, torch.float32), _stream(stream)))
+    return U_out
 
 
 def kvc_merge_gated(K, V, Ag: torch.Tensor, idx, m_keep, bucket: int, K_out, V_out, logR_out,

@@ -61,7 +61,10 @@ constexpr int CPW = 4;
 // before the merge pass evicts them), squared norms are reduced per row, then
 // lane q takes row q: it reads the group's G attention values of its row
 // (coalesced across lanes) and writes U = max_h A_h * |v| and the group mean A_g.
-template <typename T, int LG>
+// GM: the attention input is already the group's max over heads ([L, Hkv, n]):
+// one value per row, U = A_max * |v| (the same value, since |v| >= 0 and a
+// rounded product is monotone in each factor), and no A_g.
+template <typename T, int LG, bool GM>
 __global__ void __launch_bounds__(NT)
 vatp_union_kernel(const float* A_hq, ConstPtrs V, int Hq, int Hkv, int64_t n, int d,
                   int64_t nchunk, int64_t nwave, float* __restrict__ U, float* __restrict__ Ag) {
@@ -98,9 +101,13 @@ vatp_union_kernel(const float* A_hq, ConstPtrs V, int Hq, int Hkv, int64_t n, in
       const int64_t j = min(j0 + u * RPI + rg, n - 1);
       raw[cc][u] = ld_stream(Vg + j * d + c * W);
     }
-    const float* Ah = A_hq + ((int64_t)l * Hq + (int64_t)g * G) * n + min(j0 + q, n - 1);
+    if constexpr (GM) {
+      av[cc][0] = A_hq[((int64_t)l * Hkv + g) * n + min(j0 + q, n - 1)];
+    } else {
+      const float* Ah = A_hq + ((int64_t)l * Hq + (int64_t)g * G) * n + min(j0 + q, n - 1);
 #pragma unroll
-    for (int h = 0; h < MAXG; ++h) av[cc][h] = Ah[(int64_t)min(h, G - 1) * n];
+      for (int h = 0; h < MAXG; ++h) av[cc][h] = Ah[(int64_t)min(h, G - 1) * n];
+    }
   }
   // without this the attention loads are sunk into the branch below and the
   // first V row is waited for before the others are requested (A_hq is not
@@ -129,7 +136,9 @@ vatp_union_kernel(const float* A_hq, ConstPtrs V, int Hq, int Hkv, int64_t n, in
       s2 = (q / RPI == u) ? v : s2;
     }
     const int64_t j = j0 + q;
-    if (q < RW && j < n) {
+    if (GM && q < RW && j < n) {
+      U[((int64_t)l * Hkv + g) * n + j] = av[cc][0] * sqrtf(s2);
+    } else if (!GM && q < RW && j < n) {
       const float vn = sqrtf(s2);
       float mx = -INFINITY, sum = 0.f;
 #pragma unroll
@@ -514,14 +523,14 @@ merge_kernel(MergeTables t, int lc, const float* Ag, int Hkv, int64_t n, int d,
   }
 }
 
-template <typename T>
+template <typename T, bool GM>
 bool launch_vatp(int LG, int lc, hipStream_t s, const float* A_hq, const ConstPtrs& V, int Hq,
                  int Hkv, int64_t n, int d, float* U, float* Ag) {
   const int64_t rw = (int64_t)(64 / LG) * (LG < VNL ? LG : VNL);
   const int64_t nchunk = (n + rw - 1) / rw;
   const int64_t nwave = (int64_t)lc * Hkv * ((nchunk + CPW - 1) / CPW);
   const dim3 grid((unsigned)((nwave + NT / 64 - 1) / (NT / 64)));
-#define KVC_V(LGV) hipLaunchKernelGGL((vatp_union_kernel<T, LGV>), grid, dim3(NT), 0, s, A_hq, V, Hq, Hkv, n, d, nchunk, nwave, U, Ag)
+#define KVC_V(LGV) hipLaunchKernelGGL((vatp_union_kernel<T, LGV, GM>), grid, dim3(NT), 0, s, A_hq, V, Hq, Hkv, n, d, nchunk, nwave, U, Ag)
   switch (LG) {
     case 4: KVC_V(4); return true;
     case 8: KVC_V(8); return true;
@@ -587,11 +596,39 @@ extern "C" int kvc_vatp_union(const float* A_hq, const void* const* V, int dtype
     for (int i = 0; i < lc; ++i) vt.p[i] = V[l0 + i];
     const int64_t off = (int64_t)l0 * Hkv * n;
     if (dtype == KVC_BF16)
-      launch_vatp<uint16_t>(LG, lc, s, A_hq + (int64_t)l0 * Hq * n, vt, Hq, Hkv, n, d, U_out + off, Ag_out + off);
+      launch_vatp<uint16_t, false>(LG, lc, s, A_hq + (int64_t)l0 * Hq * n, vt, Hq, Hkv, n, d, U_out + off, Ag_out + off);
     else
-      launch_vatp<float>(LG, lc, s, A_hq + (int64_t)l0 * Hq * n, vt, Hq, Hkv, n, d, U_out + off, Ag_out + off);
+      launch_vatp<float, false>(LG, lc, s, A_hq + (int64_t)l0 * Hq * n, vt, Hq, Hkv, n, d, U_out + off, Ag_out + off);
   }
   return launch_status("kvc_vatp_union");
+}
+
+extern "C" int kvc_vatp_union_gmax(const float* A_gmax, const void* const* V, int dtype, int L,
+                                   int Hkv, int64_t n, int d, float* U_out, void* stream) {
+  clear_error();
+  if (!dtype_ok(dtype)) return KVC_FAIL(KVC_ERR_DTYPE, "kvc_vatp_union_gmax: dtype %d", dtype);
+  KVC_REQUIRE(L >= 1 && L <= KVC_MAX_LAYERS, "kvc_vatp_union_gmax: need 1 <= L <= %d", KVC_MAX_LAYERS);
+  KVC_REQUIRE(Hkv >= 1, "kvc_vatp_union_gmax: need Hkv >= 1");
+  KVC_REQUIRE(n >= 1 && n <= 0x7fffffffLL, "kvc_vatp_union_gmax: need 1 <= n < 2^31");
+  KVC_REQUIRE(A_gmax && V && U_out, "kvc_vatp_union_gmax: null pointer");
+  int LG = 0;
+  KVC_REQUIRE(lg_ok(d, dtype, &LG), "kvc_vatp_union_gmax: need d * elsize in {64, 128, 256, 512} bytes");
+  for (int l = 0; l < L; ++l)
+    KVC_REQUIRE(V[l] && (uintptr_t)V[l] % 16 == 0, "kvc_vatp_union_gmax: V[%d] null or not 16-byte aligned", l);
+  KVC_REQUIRE((int64_t)kLayersPerLaunch * Hkv * ((n + 31) / 32) / 4 <= 0x7fffffffLL,
+              "kvc_vatp_union_gmax: grid too large");
+  hipStream_t s = as_stream(stream);
+  for (int l0 = 0; l0 < L; l0 += kLayersPerLaunch) {
+    const int lc = min(kLayersPerLaunch, L - l0);
+    ConstPtrs vt{};
+    for (int i = 0; i < lc; ++i) vt.p[i] = V[l0 + i];
+    const int64_t off = (int64_t)l0 * Hkv * n;
+    if (dtype == KVC_BF16)
+      launch_vatp<uint16_t, true>(LG, lc, s, A_gmax + off, vt, Hkv, Hkv, n, d, U_out + off, nullptr);
+    else
+      launch_vatp<float, true>(LG, lc, s, A_gmax + off, vt, Hkv, Hkv, n, d, U_out + off, nullptr);
+  }
+  return launch_status("kvc_vatp_union_gmax");
 }
 
 extern "C" int kvc_merge_gated(const void* const* K, const void* const* V, int dtype, const float* Ag,

@@ -1,4 +1,5 @@
-// Observation-window attention A (group mean, or per query head).
+// Observation-window attention A (group mean, per query head, or the group mean and the
+// group max over query heads).
 //
 // [InfoKV] Method and Technical detail: the attention each cached token receives
 // from the queries of the last w positions of layer l, averaged over the window
@@ -67,9 +68,10 @@ struct WinArgs {
   Geo g;
   int tile0;                           // first query tile of this launch
   float sl2;                           // scale * log2(e)
-  int per_head;
+  int per_head;                        // output form: 0 group mean, 1 per head, 2 group mean and max
   float2* part;                        // [32, Hkv, nwg, rows] pass-1 partials
   float* A;                            // output of the layer group
+  float* A2;                           // form 2: the group max plane of the layer group
   int nspan;
   Span span[2];
   int64_t blocks0;                     // tasks of span 0
@@ -326,7 +328,7 @@ __device__ __forceinline__ void pass1(const WinArgs& a, WinSmem<D, TG>& sm, int 
 }
 
 // ---------------------------------------------------------------- pass 2
-template <int D, int TG, bool PH>
+template <int D, int TG, int OM>
 __device__ __forceinline__ void pass2(const WinArgs& a, WinSmem<D, TG>& sm, int l, int kvh, int wgi) {
   constexpr int S = D / 16;
   const Geo& g = a.g;
@@ -429,6 +431,24 @@ __device__ __forceinline__ void pass2(const WinArgs& a, WinSmem<D, TG>& sm, int 
 #pragma unroll
     for (int t = 0; t < TG; ++t) asm volatile("" : "+v"(hs[t]));
     float total = 0.f, hsum = 0.f;
+    constexpr bool PH = OM == 1;
+    if constexpr (OM == 2) {                     // every head of the group in this launch, one tile each
+      // group mean (lower half-wave) and group max (upper half-wave) of the heads'
+      // column sums, one store instruction for both planes
+      float tot = 0.f, mx = 0.f;
+#pragma unroll
+      for (int t = 0; t < TG; ++t) {
+        const float cs = add_halves(hs[t]);
+        tot += cs;
+        mx = t == 0 ? cs : fmaxf(mx, cs);
+      }
+      if (key < g.n) {
+        const int64_t o = ((int64_t)l * g.Hkv + kvh) * g.n + key;
+        if (hf == 0) A[o] = tot * inv_group;
+        else a.A2[o] = mx * inv_w;
+      }
+      return;
+    }
     if constexpr (!PH) {                         // one cross-half add for the group
       float own = hs[0];
 #pragma unroll
@@ -482,9 +502,9 @@ __device__ __forceinline__ void pass2(const WinArgs& a, WinSmem<D, TG>& sm, int 
   stream_blocks<D>(kh, g.n, jb, nb, lane, prologue, block);
 }
 
-// PH: A per query head (else the group mean), fixed at compile time so that the
-// pass-2 block stays one scheduling region
-template <int D, int TG, bool PH>
+// OM: output form (0 group mean, 1 per query head, 2 group mean and group max),
+// fixed at compile time so that the pass-2 block stays one scheduling region
+template <int D, int TG, int OM>
 __global__ void __launch_bounds__(NTW)
 win_kernel(WinArgs a) {
   __shared__ WinSmem<D, TG> sm;
@@ -498,7 +518,7 @@ win_kernel(WinArgs a) {
     const int wgi = (int)(local % a.g.nwg);
     const int l = sp.l0 + (int)(lgl / a.g.Hkv), kvh = (int)(lgl % a.g.Hkv);
     if (sp.pass == 1) pass1<D, TG>(a, sm, l, kvh, wgi);
-    else pass2<D, TG, PH>(a, sm, l, kvh, wgi);
+    else pass2<D, TG, OM>(a, sm, l, kvh, wgi);
     __syncthreads();                             // LDS is reused by the next task
   }
 }
@@ -555,7 +575,7 @@ struct XArgs {
   ConstPtrs q, k;                    // per-layer pointers of the current layer group
   Geo g;
   float sl2;                         // scale * log2(e)
-  int per_head;
+  int per_head;                      // output form (as WinArgs)
   int nunits;                        // (layer, KV head) units of the group
   int tw;                            // workgroups per team
   int tpx;                           // teams per XCD (workgroups past tpx * tw idle)
@@ -566,6 +586,7 @@ struct XArgs {
   unsigned* status;                  // bit 1: a barrier gave up; bit 2: an XCD beyond kXcds
   unsigned* reg;                     // [kXcds] slots taken on each XCD
   float* A;                          // output of the layer group
+  float* A2;                         // form 2: the group max plane of the layer group
 };
 
 template <int D, int NT>
@@ -594,7 +615,7 @@ __device__ __forceinline__ void x_load_block(bf16x8 (&kr)[D / 16], const XArgs& 
   for (int st = 0; st < S; ++st) kr[st] = *reinterpret_cast<const bf16x8*>(p + 16 * st);
 }
 
-template <int D, int NT, bool PH>
+template <int D, int NT, int OM>
 __global__ void __launch_bounds__(NTX) __attribute__((amdgpu_waves_per_eu(2, 2)))
 win_xcd(XArgs a) {
   constexpr int S = D / 16, KBM = 512 / D, R = NT * 32;
@@ -861,11 +882,24 @@ win_xcd(XArgs a) {
       pipelined_tiles<S, NT, false>(kc, ql, qo, epi);
 #pragma unroll
       for (int t = 0; t < NT; ++t) asm volatile("" : "+v"(hs[t]));
-      if constexpr (PH) {
+      if constexpr (OM == 1) {
 #pragma unroll
         for (int t = 0; t < NT; ++t) {           // one tile per query head
           const float cs = add_halves(hs[t]);
           if (hf == 0 && key < g.n) a.A[((int64_t)l * g.Hq + kvh * g.G + t) * g.n + key] = cs * inv_w;
+        }
+      } else if constexpr (OM == 2) {            // group mean (lower half), group max (upper half)
+        float tot = 0.f, mx = 0.f;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          const float cs = add_halves(hs[t]);
+          tot += cs;
+          mx = t == 0 ? cs : fmaxf(mx, cs);
+        }
+        if (key < g.n) {
+          const int64_t o = ((int64_t)l * g.Hkv + kvh) * g.n + key;
+          if (hf == 0) a.A[o] = tot * inv_group;
+          else a.A2[o] = mx * inv_w;
         }
       } else {
         float own = hs[0];
@@ -966,7 +1000,7 @@ constexpr int NTA = 64;
 template <int D>
 __global__ void __launch_bounds__(NTA)
 win_f32_accum(ConstPtrs qs, ConstPtrs ks, Geo g, float scale_log2, const float* __restrict__ c,
-              int per_head, float* __restrict__ A) {
+              int per_head, float* __restrict__ A, float* __restrict__ A2) {
   extern __shared__ float qall[];              // [R, d]
   const int R = g.G * g.w;
   const int d = D > 0 ? D : g.d;
@@ -986,7 +1020,7 @@ win_f32_accum(ConstPtrs qs, ConstPtrs ks, Geo g, float scale_log2, const float* 
 #pragma unroll
     for (int e = 0; e < D; ++e) kreg[e] = kr[e];
   }
-  float total = 0.f;
+  float total = 0.f, mx = 0.f;
   for (int h = 0; h < g.G; ++h) {
     float hs = 0.f;
     for (int rr = 0; rr < g.w; ++rr) {
@@ -1001,10 +1035,12 @@ win_f32_accum(ConstPtrs qs, ConstPtrs ks, Geo g, float scale_log2, const float* 
       }
       hs += exp2f(dot * scale_log2 - cr[h * g.w + rr]);
     }
-    if (per_head) A[((int64_t)l * g.Hq + kvh * g.G + h) * g.n + j] = hs / (float)g.w;
+    if (per_head == 1) A[((int64_t)l * g.Hq + kvh * g.G + h) * g.n + j] = hs / (float)g.w;
     total += hs;
+    mx = h == 0 ? hs : fmaxf(mx, hs);
   }
-  if (!per_head) A[((int64_t)l * g.Hkv + kvh) * g.n + j] = total / (float)(g.G * g.w);
+  if (per_head != 1) A[((int64_t)l * g.Hkv + kvh) * g.n + j] = total / (float)(g.G * g.w);
+  if (per_head == 2) A2[((int64_t)l * g.Hkv + kvh) * g.n + j] = mx / (float)g.w;
 }
 
 // ---------------------------------------------------------------- host
@@ -1068,9 +1104,9 @@ void make_plan(int L, int Hq, int Hkv, int64_t n, int w, int d, int dtype, Plan*
 // CU's 160 KB, so that a CU holds one (the slot counting relies on it).
 constexpr size_t kXMinLds = 80 * 1024 + 256;
 
-template <int D, int NT, bool PH>
+template <int D, int NT, int OM>
 bool launch_xcd_t(XArgs a, hipStream_t s) {
-  const void* kern = reinterpret_cast<const void*>(&win_xcd<D, NT, PH>);
+  const void* kern = reinterpret_cast<const void*>(&win_xcd<D, NT, OM>);
   const size_t stat = sizeof(XSmem<D, NT>);
   const size_t dyn = stat < kXMinLds ? kXMinLds - stat : 0;
   int dev = 0, ncu = 0, per_cu = 0;
@@ -1089,19 +1125,22 @@ bool launch_xcd_t(XArgs a, hipStream_t s) {
   return hipLaunchCooperativeKernel(kern, dim3((unsigned)ncu), dim3(NTX), args, (unsigned)dyn, s) == hipSuccess;
 }
 
-template <int D, bool PH>
+template <int D, int OM>
 bool launch_xcd_d(const XArgs& a, hipStream_t s) {
   switch (a.g.ntiles) {
-    case 1: return launch_xcd_t<D, 1, PH>(a, s);
-    case 2: return launch_xcd_t<D, 2, PH>(a, s);
-    case 3: return launch_xcd_t<D, 3, PH>(a, s);
-    default: return launch_xcd_t<D, 4, PH>(a, s);
+    case 1: return launch_xcd_t<D, 1, OM>(a, s);
+    case 2: return launch_xcd_t<D, 2, OM>(a, s);
+    case 3: return launch_xcd_t<D, 3, OM>(a, s);
+    default: return launch_xcd_t<D, 4, OM>(a, s);
   }
 }
 
 bool launch_xcd(const XArgs& a, hipStream_t s) {
-  if (a.g.d == 64) return a.per_head ? launch_xcd_d<64, true>(a, s) : launch_xcd_d<64, false>(a, s);
-  return a.per_head ? launch_xcd_d<128, true>(a, s) : launch_xcd_d<128, false>(a, s);
+  if (a.g.d == 64)
+    return a.per_head == 1 ? launch_xcd_d<64, 1>(a, s)
+         : a.per_head == 2 ? launch_xcd_d<64, 2>(a, s) : launch_xcd_d<64, 0>(a, s);
+  return a.per_head == 1 ? launch_xcd_d<128, 1>(a, s)
+       : a.per_head == 2 ? launch_xcd_d<128, 2>(a, s) : launch_xcd_d<128, 0>(a, s);
 }
 
 // Workgroups of `kern` resident at once on the current device.
@@ -1114,18 +1153,19 @@ int resident_blocks(const void* kern) {
   return (ncu > 0 ? ncu : 1) * (per_cu > 0 ? per_cu : 1);
 }
 
-template <int D, int TG, bool PH>
+template <int D, int TG, int OM>
 void launch_win_ph(WinArgs a, hipStream_t s) {
-  const void* kern = reinterpret_cast<const void*>(&win_kernel<D, TG, PH>);
+  const void* kern = reinterpret_cast<const void*>(&win_kernel<D, TG, OM>);
   const int64_t res = resident_blocks(kern);
   const dim3 grid((unsigned)(a.ntask < res ? a.ntask : res)), block(NTW);
-  hipLaunchKernelGGL((win_kernel<D, TG, PH>), grid, block, 0, s, a);
+  hipLaunchKernelGGL((win_kernel<D, TG, OM>), grid, block, 0, s, a);
 }
 
 template <int D, int TG>
 void launch_win_tg(WinArgs a, hipStream_t s) {
-  if (a.per_head) launch_win_ph<D, TG, true>(a, s);
-  else launch_win_ph<D, TG, false>(a, s);
+  if (a.per_head == 1) launch_win_ph<D, TG, 1>(a, s);
+  else if (a.per_head == 2) launch_win_ph<D, TG, 2>(a, s);
+  else launch_win_ph<D, TG, 0>(a, s);
 }
 
 template <int D>
@@ -1176,7 +1216,7 @@ extern "C" int kvc_score_window_attn(const void* const* q_win, const void* const
   KVC_REQUIRE(Hkv >= 1 && Hq >= Hkv && Hq % Hkv == 0, "kvc_score_window_attn: need Hq %% Hkv == 0");
   KVC_REQUIRE(n >= 1 && w >= 1 && w <= n, "kvc_score_window_attn: need 1 <= w <= n");
   KVC_REQUIRE(n <= 0x7fffffffLL, "kvc_score_window_attn: n > 2^31-1");
-  KVC_REQUIRE(per_query_head == 0 || per_query_head == 1, "kvc_score_window_attn: per_query_head");
+  KVC_REQUIRE(per_query_head >= 0 && per_query_head <= 2, "kvc_score_window_attn: per_query_head not 0, 1 or 2");
   // The passes keep running maxima of the raw dot products and scale them
   // afterwards, which is the maximum of the scaled logits only for scale > 0.
   KVC_REQUIRE(scale > 0.f && std::isfinite(scale), "kvc_score_window_attn: need a finite scale > 0");
@@ -1194,6 +1234,10 @@ extern "C" int kvc_score_window_attn(const void* const* q_win, const void* const
                   "kvc_score_window_attn: bf16 tensors must be 16-byte aligned");
     KVC_REQUIRE((int64_t)2 * kLayersPerLaunch * Hkv * g.nwg <= 0x7fffffffLL,
                 "kvc_score_window_attn: grid too large");
+    // form 2 takes the group max over heads inside one launch: one tile per head
+    // and every head of the group in the launch
+    KVC_REQUIRE(per_query_head != 2 || (g.tph == 1 && g.ntiles <= MAX_TG),
+                "kvc_score_window_attn: per_query_head 2 needs w <= 32 and Hq/Hkv <= %d", MAX_TG);
   } else {
     KVC_REQUIRE(d >= 1 && d <= 256, "kvc_score_window_attn: float32 needs d <= 256");
     KVC_REQUIRE((int64_t)g.G * w * d * 4 <= 64 * 1024,
@@ -1208,13 +1252,14 @@ extern "C" int kvc_score_window_attn(const void* const* q_win, const void* const
   float* cfin = (float*)(base + P.part_bytes);
   hipStream_t s = as_stream(stream);
   const float sl2 = scale * LOG2E;
-  const int Aheads = per_query_head ? Hq : Hkv;
+  const int Aheads = per_query_head == 1 ? Hq : Hkv;
 
   for (int l0 = 0; l0 < L; l0 += kLayersPerLaunch) {        // layer groups of at most 32
     const int lc = min(kLayersPerLaunch, L - l0);
     ConstPtrs qt{}, kt{};
     for (int i = 0; i < lc; ++i) { qt.p[i] = q_win[l0 + i]; kt.p[i] = k[l0 + i]; }
     float* A = A_out + (int64_t)l0 * Aheads * n;
+    float* A2 = per_query_head == 2 ? A_out + ((int64_t)L + l0) * Hkv * n : nullptr;   // second plane
     bool done = false;
     if (P.xshape && (size_t)(base - (char*)ws) + xneed <= ws_bytes) {
       // keys read once; not under stream capture (cooperative launch), and the
@@ -1234,6 +1279,7 @@ extern "C" int kvc_score_window_attn(const void* const* q_win, const void* const
         xa.cnt = (unsigned*)(base + 256);
         xa.part = (float*)(base + P.x_head_bytes);
         xa.A = A;
+        xa.A2 = A2;
         // status and counters start at zero (a fill kernel, not a memset)
         const int nz = (int)(P.x_head_bytes / sizeof(unsigned));
         hipLaunchKernelGGL(win_xcd_zero, dim3((nz + 255) / 256), dim3(256), 0, s, (unsigned*)base, nz);
@@ -1245,7 +1291,7 @@ extern "C" int kvc_score_window_attn(const void* const* q_win, const void* const
     } else if (P.mfma) {
       WinArgs a{};
       a.q = qt; a.k = kt; a.g = g; a.sl2 = sl2; a.per_head = per_query_head;
-      a.part = part; a.A = A;
+      a.part = part; a.A = A; a.A2 = A2;
       const int nch = (lc + P.lch - 1) / P.lch;
       if (g.ntiles <= MAX_TG) {
         // launch i: pass 2 of chunk i-1 beside pass 1 of chunk i
@@ -1272,7 +1318,7 @@ extern "C" int kvc_score_window_attn(const void* const* q_win, const void* const
       const dim3 ga((unsigned)(lc * Hkv * nblk));
       const size_t lds = (size_t)R * d * sizeof(float);
 #define KVC_A(DD) hipLaunchKernelGGL((win_f32_accum<DD>), ga, dim3(NTA), lds, s, qt, kt, g, sl2, \
-                                     (const float*)cfin, per_query_head, A)
+                                     (const float*)cfin, per_query_head, A, A2)
       switch (d) {
         case 16: KVC_A(16); break;
         case 32: KVC_A(32); break;

@@ -259,9 +259,10 @@ class SelKVPlan:
         dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
         dtc = B.KVC_BF16 if w.dtype == "bf16" else B.KVC_F32
         self.scale = 1.0 / math.sqrt(d)
-        self.A_hq = torch.empty(L, Hq, n, dtype=f32, device=device)
+        # window attention's group mean (A_g) and group max over the query heads
+        self.A2 = torch.empty(2, L, Hkv, n, dtype=f32, device=device)
+        self.Ag, self.Amax = self.A2[0], self.A2[1]
         self.U = torch.empty(L, Hkv, n, dtype=f32, device=device)
-        self.Ag = torch.empty(L, Hkv, n, dtype=f32, device=device)
         self.ws_attn = torch.empty(max(1, B.kvc_score_window_attn_workspace_size(
             L, Hq, Hkv, n, w.window, d, dtc)), dtype=torch.uint8, device=device)
         m = B.kvc_uniform_budget(w.keep_fraction, n, w.window)
@@ -275,10 +276,10 @@ class SelKVPlan:
         w = self.w
         mark = mark or (lambda name: None)
         mark("start")
-        B.kvc_score_window_attn(inp["q_win"], inp["k"], self.scale, True, self.A_hq,
+        B.kvc_score_window_attn(inp["q_win"], inp["k"], self.scale, 2, self.A2,
                                 ws=self.ws_attn, stream=stream)
         mark("window_attn")
-        B.kvc_vatp_union(self.A_hq, inp["v"], self.U, self.Ag, stream=stream)
+        B.kvc_vatp_union_gmax(self.Amax, inp["v"], self.U, stream=stream)
         mark("vatp_union")
         B.kvc_select_topk(self.U, self.m, w.window, self.idx, stream=stream)
         mark("select_topk")

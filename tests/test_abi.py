@@ -86,6 +86,15 @@ def test_validation_before_launch(lib):
     for bad in (0.0, -0.1, float("inf"), float("nan")):
         assert lib.kvc_score_window_attn(pa, pa, 1, 1, 4, 2, 64, 8, 128, ctypes.c_float(bad), 0, fake, fake, 1 << 30, None) == -1
         assert "scale" in err(lib)
+    # window attention, per_query_head: only 0, 1, 2; form 2 in bf16 needs one tile
+    # per head (w <= 32) and at most 4 heads per group
+    assert lib.kvc_score_window_attn(pa, pa, 1, 1, 4, 2, 64, 8, 128, ctypes.c_float(0.1), 3, fake, fake, 1 << 30, None) == -1
+    assert lib.kvc_score_window_attn(pa, pa, 1, 1, 4, 2, 64, 48, 128, ctypes.c_float(0.1), 2, fake, fake, 1 << 30, None) == -1
+    assert "per_query_head 2" in err(lib)
+    assert lib.kvc_score_window_attn(pa, pa, 1, 1, 16, 2, 64, 8, 128, ctypes.c_float(0.1), 2, fake, fake, 1 << 30, None) == -1
+    # VATP from the group max: bad d * element size, null output
+    assert lib.kvc_vatp_union_gmax(fake, pa, 1, 1, 2, 64, 100, fake, None) == -1
+    assert lib.kvc_vatp_union_gmax(fake, pa, 1, 1, 2, 64, 128, None, None) == -1
     # select: k_keep outside [1, n]
     kk = (ctypes.c_int64 * 1)(65)
     assert lib.kvc_select_topk(fake, 1, 2, 64, kk, 8, pa, None) == -1

@@ -507,8 +507,21 @@ def _selkv_pieces(dev, case, dtype):
     U = torch.empty(L, Hkv, n, device=dev)
     Ag = torch.empty(L, Hkv, n, device=dev)
     B().kvc_vatp_union(A_hq, V, U, Ag)
-    torch.cuda.synchronize()
     G = Hq // Hkv
+    # the same from the group mean and max planes (per_query_head = 2, when the
+    # shape allows it) and the union from the max
+    fused = dtype == torch.float32 or (w <= 32 and G <= 4)
+    if fused:
+        A2 = torch.empty(2, L, Hkv, n, device=dev)
+        B().kvc_score_window_attn(q, K, 1 / math.sqrt(d), 2, A2)
+        U2 = torch.empty(L, Hkv, n, device=dev)
+        B().kvc_vatp_union_gmax(A2[1], V, U2)
+    torch.cuda.synchronize()
+    if fused:
+        # max over heads commutes with the rounded product by |v| >= 0, and both
+        # forms take the same per-head column sums: U is bitwise the same
+        assert torch.equal(A2[1], A_hq.view(L, Hkv, G, n).amax(dim=2))
+        assert torch.equal(U2, U)
     for l in range(L):
         Vn = host_f64(V[l])
         Ah = host_f64(A_hq[l])
@@ -517,6 +530,11 @@ def _selkv_pieces(dev, case, dtype):
         _, U_ref = selkv.vatp_union(ref_o["A_hq"], Vn)
         assert_rel(U[l].cpu().numpy(), U_ref, 1e-3, what="U")
         assert_rel(Ag[l].cpu().numpy(), ref_o["A_g"], 1e-3, what="Ag")
+        if fused:
+            A_ref = ref_o["A_hq"].reshape(Hkv, G, n)
+            assert_rel(A2[0, l].cpu().numpy(), A_ref.mean(axis=1), 1e-3, what="A_g (form 2)")
+            assert_rel(A2[1, l].cpu().numpy(), A_ref.max(axis=1), 1e-3, what="A group max (form 2)")
+            assert_rel(U2[l].cpu().numpy(), U_ref, 1e-3, what="U from the group max")
         # selection given identical scores (the oracle's float32 U): bit-exact
         U32 = torch.from_numpy(ref_o["U32"]).to(dev)[None].contiguous()
         idx = [torch.empty(Hkv, m, dtype=torch.int32, device=dev)]
