@@ -18,7 +18,9 @@ namespace kvc {
 namespace {
 
 constexpr int NT = 256;
-constexpr int CHUNK = 8192;     // tokens per stats block
+constexpr int CHUNK = 1024;     // tokens per stats block (4 per thread, held in registers)
+constexpr int PER = CHUNK / NT;
+static_assert(CHUNK % NT == 0, "whole tokens per thread");
 
 struct Part { float m, s, e; };
 
@@ -29,15 +31,19 @@ fuse_stats(const float* __restrict__ D, const float* __restrict__ H, int64_t n, 
   const int l = blockIdx.y, c = blockIdx.x;
   const int64_t i0 = (int64_t)c * CHUNK, i1 = min(n, i0 + CHUNK);
   const float* Dl = D + (int64_t)l * n;
+  float e[PER];
   float m = -INFINITY, esum = 0.f;
-  for (int64_t i = i0 + threadIdx.x; i < i1; i += NT) {
-    const float E = Dl[i] * H[i];
-    m = fmaxf(m, E);
-    esum += E;
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {                // this thread's tokens, read once
+    const int64_t i = i0 + threadIdx.x + (int64_t)u * NT;
+    e[u] = i < i1 ? Dl[i] * H[i] : 0.f;
+    if (i < i1) { m = fmaxf(m, e[u]); esum += e[u]; }
   }
   const float M = block_max<NT>(m, red);
   float s = 0.f;
-  for (int64_t i = i0 + threadIdx.x; i < i1; i += NT) s += expf(Dl[i] * H[i] - M);
+#pragma unroll
+  for (int u = 0; u < PER; ++u)
+    if (i0 + threadIdx.x + (int64_t)u * NT < i1) s += expf(e[u] - M);
   const float S = block_sum<NT>(s, red);
   const float ES = block_sum<NT>(esum, red);
   if (threadIdx.x == 0) part[(int64_t)l * nchunk + c] = Part{M, S, ES};
@@ -84,15 +90,19 @@ slot_stats(const float* __restrict__ E, int64_t n, int nchunk, Part* __restrict_
   const int c = blockIdx.x;
   const int64_t i0 = (int64_t)c * CHUNK, i1 = min(n, i0 + CHUNK);
   const float* Er = E + row * n;
+  float e[PER];
   float m = -INFINITY, esum = 0.f;
-  for (int64_t i = i0 + threadIdx.x; i < i1; i += NT) {
-    const float e = Er[i];
-    m = fmaxf(m, e);
-    esum += e;
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {                // this thread's tokens, read once
+    const int64_t i = i0 + threadIdx.x + (int64_t)u * NT;
+    e[u] = i < i1 ? Er[i] : 0.f;
+    if (i < i1) { m = fmaxf(m, e[u]); esum += e[u]; }
   }
   const float M = block_max<NT>(m, red);
   float s = 0.f;
-  for (int64_t i = i0 + threadIdx.x; i < i1; i += NT) s += expf(Er[i] - M);
+#pragma unroll
+  for (int u = 0; u < PER; ++u)
+    if (i0 + threadIdx.x + (int64_t)u * NT < i1) s += expf(e[u] - M);
   const float S = block_sum<NT>(s, red);
   const float ES = block_sum<NT>(esum, red);
   if (threadIdx.x == 0) part[row * nchunk + c] = Part{M, S, ES};
