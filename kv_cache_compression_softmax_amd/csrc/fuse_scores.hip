@@ -79,6 +79,32 @@ fuse_apply(const float* __restrict__ A, const float* __restrict__ D, const float
   }
 }
 
+// The same with 16-byte accesses, for rows a multiple of 4 long (16-byte
+// aligned); the per-element arithmetic is the same.
+__global__ void __launch_bounds__(NT)
+fuse_apply4(const float4* __restrict__ A, const float* __restrict__ D, const float* __restrict__ H,
+            const float2* __restrict__ stats, int Hkv, int64_t n, float alpha,
+            float4* __restrict__ S) {
+  const int64_t row = blockIdx.y;               // (layer, KV head)
+  const int l = (int)(row / Hkv);
+  const float2 st = stats[l];
+  const int64_t n4 = n / 4;
+  const float4* Dl = reinterpret_cast<const float4*>(D + (int64_t)l * n);
+  const float4* H4 = reinterpret_cast<const float4*>(H);
+  const float4* Ar = A + row * n4;
+  float4* Sr = S + row * n4;
+  const float beta = 1.0f - alpha;
+  for (int64_t i = (int64_t)blockIdx.x * NT + threadIdx.x; i < n4; i += (int64_t)gridDim.x * NT) {
+    const float4 a = Ar[i], d = Dl[i], h = H4[i];
+    float4 r;
+    r.x = alpha * a.x + beta * (expf(d.x * h.x - st.x) * st.y);
+    r.y = alpha * a.y + beta * (expf(d.y * h.y - st.x) * st.y);
+    r.z = alpha * a.z + beta * (expf(d.z * h.z - st.x) * st.y);
+    r.w = alpha * a.w + beta * (expf(d.w * h.w - st.x) * st.y);
+    Sr[i] = r;
+  }
+}
+
 // ---- cache slots: one entropy score per (layer, KV head, slot) ----------------
 // After a compaction each KV head holds its own token set, so E is a row per
 // (layer, KV head) and the softmax runs over that row.
@@ -186,10 +212,18 @@ extern "C" int kvc_fuse_scores(const float* A, const float* D, const float* H, i
                      (int)nchunk, part);
   hipLaunchKernelGGL(fuse_stats_merge, dim3((L + 63) / 64), dim3(64), 0, s, (const Part*)part,
                      (int)nchunk, L, n, stats, Ebar_out);
-  const int64_t gx64 = (n + NT * 4 - 1) / (NT * 4);
-  const unsigned gx = (unsigned)(gx64 < 1024 ? gx64 : 1024);
-  hipLaunchKernelGGL(fuse_apply, dim3(gx, (unsigned)rows), dim3(NT), 0, s, A, D, H,
-                     (const float2*)stats, Hkv, n, alpha_fuse, S_out);
+  const bool vec = n % 4 == 0 && ((uintptr_t)A | (uintptr_t)D | (uintptr_t)H | (uintptr_t)S_out) % 16 == 0;
+  if (vec) {
+    const int64_t gx64 = (n / 4 + NT - 1) / NT;  // one 16-byte group per thread
+    const unsigned gx = (unsigned)(gx64 < 1024 ? gx64 : 1024);
+    hipLaunchKernelGGL(fuse_apply4, dim3(gx, (unsigned)rows), dim3(NT), 0, s, (const float4*)A, D, H,
+                       (const float2*)stats, Hkv, n, alpha_fuse, (float4*)S_out);
+  } else {
+    const int64_t gx64 = (n + NT * 4 - 1) / (NT * 4);
+    const unsigned gx = (unsigned)(gx64 < 1024 ? gx64 : 1024);
+    hipLaunchKernelGGL(fuse_apply, dim3(gx, (unsigned)rows), dim3(NT), 0, s, A, D, H,
+                       (const float2*)stats, Hkv, n, alpha_fuse, S_out);
+  }
   return launch_status("kvc_fuse_scores");
 }
 
