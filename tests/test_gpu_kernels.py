@@ -274,7 +274,7 @@ def test_window_attention(dev, case, per_head):
     np.testing.assert_allclose(A.sum(dim=2).cpu().numpy(), 1.0, atol=1e-4)
 
 
-@pytest.mark.parametrize("per_head", [False, True])
+@pytest.mark.parametrize("per_head", [False, True, 2])
 @pytest.mark.parametrize("case", [WIN_CASES[2], WIN_CASES[5], WIN_CASES[6], WIN_CASES[8]], ids=str)
 def test_window_attention_graph_replays(dev, case, per_head):
     """Under stream capture the call takes the two-pass kernel (the kernel that
@@ -282,17 +282,29 @@ def test_window_attention_graph_replays(dev, case, per_head):
     captured): every replay of the captured graph, with eager work and
     synchronisation between replays, matches the oracle."""
     L, Hq, Hkv, n, w, d, dtype = case
+    G = Hq // Hkv
+    if per_head == 2 and not (w <= 32 and G <= 4):
+        pytest.skip("form 2 needs w <= 32 and Hq/Hkv <= 4")
     announce("window_attn_graph", case, per_head)
     q = [gen((Hq, w, d), 20 + l, dev, dtype) for l in range(L)]
     k = [gen((Hkv, n, d), 40 + l, dev, dtype) for l in range(L)]
-    A = torch.empty(L, Hq if per_head else Hkv, n, device=dev)
+    if per_head == 2:                            # group mean and group max planes
+        A = torch.empty(2, L, Hkv, n, device=dev)
+    else:
+        A = torch.empty(L, Hq if per_head else Hkv, n, device=dev)
     dt = 1 if dtype == torch.bfloat16 else 0
     ws = torch.empty(B().kvc_score_window_attn_workspace_size(L, Hq, Hkv, n, w, d, dt),
                      dtype=torch.uint8, device=dev)
     B().kvc_score_window_attn(q, k, 1 / math.sqrt(d), per_head, A, ws=ws)    # eager call first
     torch.cuda.synchronize()
-    refs = [infokv.window_attention(host_f64(q[l]), host_f64(k[l]), per_query_head=per_head)
-            for l in range(L)]
+    if per_head == 2:
+        refs = []
+        for l in range(L):
+            Ah = infokv.window_attention(host_f64(q[l]), host_f64(k[l]), per_query_head=True)
+            refs.append((Ah.reshape(Hkv, G, n).mean(axis=1), Ah.reshape(Hkv, G, n).max(axis=1)))
+    else:
+        refs = [infokv.window_attention(host_f64(q[l]), host_f64(k[l]), per_query_head=per_head)
+                for l in range(L)]
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
         B().kvc_score_window_attn(q, k, 1 / math.sqrt(d), per_head, A, ws=ws)
@@ -301,7 +313,11 @@ def test_window_attention_graph_replays(dev, case, per_head):
         graph.replay()
         torch.cuda.synchronize()
         for l in range(L):
-            assert_rel(A[l].cpu().numpy(), refs[l], 1e-3, what=f"replay {rep} layer {l}")
+            if per_head == 2:
+                assert_rel(A[0, l].cpu().numpy(), refs[l][0], 1e-3, what=f"replay {rep} layer {l} mean")
+                assert_rel(A[1, l].cpu().numpy(), refs[l][1], 1e-3, what=f"replay {rep} layer {l} max")
+            else:
+                assert_rel(A[l].cpu().numpy(), refs[l], 1e-3, what=f"replay {rep} layer {l}")
 
 
 @pytest.mark.parametrize("per_head", [False, True])
