@@ -22,9 +22,10 @@
 // by a 512-thread workgroup: thread t keeps vectors t, t + 512, ..., which is
 // also the vector it needs in
 // each chunk of the ordered pass, so again the row is read once (all of a
-// thread's loads in flight together).  Longer rows still are re-read by every
-// pass.  The histograms are per wave, with wave-aggregated increments where
-// lanes crowd into one bin.
+// thread's loads in flight together; its descent and output are described with
+// the kernel below).  Longer rows still are re-read by every pass.  The
+// histograms of the other paths are per wave, with wave-aggregated increments
+// where lanes crowd into one bin.
 #include "common.h"
 
 namespace kvc {
@@ -206,39 +207,80 @@ select_kernel(const float* __restrict__ S, int Hkv, int64_t n, I64s kk, int w, M
 // A row of up to REGV * NTR vectors of 4 scores (102400 scores) is held in
 // registers, as order-preserving keys, by a workgroup of NTR threads: thread t
 // keeps vectors t, t + NTR, ..., all loads in flight together, so the row is read
-// once.
-//   1. The row's smallest and largest keys bound the search.  Each pass cuts
-//      the current key range [lo, lo + 2^sp) into at most 256 bins of width
-//      2^(sp-8), so scores spread over a few binades fill many bins (digits of
-//      the raw key would put a whole binade into one or two).  The bin holding
-//      the need-th largest key becomes the next range; keys outside the range
-//      were counted by earlier passes and are not counted again.
-//   2. After the first pass the keys of the chosen bin (when at most CAND) are
-//      copied to an LDS list, and the remaining passes read the list only.
+// once.  Every step over the held keys is unrolled, so its body per key is kept
+// to a few instructions: the unrolled code is streamed through the instruction
+// cache on every step.
+//   0. Keys outside [0, n - w) (the window, and the repeated last vector) are
+//      replaced by key 0, the lowest key; the row's smallest and largest keys
+//      are taken over the row alone.  Extra copies of the lowest key never move
+//      the need-th largest key (need < n - w) and are never counted above it.
+//   1. Each pass cuts the current key range [lo, lo + 2^sp) into nbin <= 256
+//      bins of width 2^(sp-8), so scores spread over a few binades fill many
+//      bins.  A key outside the range lands in bin nbin, which is not read.  The
+//      bin holding the need-th largest key becomes the next range.
+//   2. After the first pass every thread copies its keys of the chosen bin to
+//      its own LDS slots (slot j of thread t at j * NTR + t; the key is written
+//      at every step and the slot advances on a hit, so no branches).  The
+//      remaining passes run in one wave over these lists, without block
+//      barriers.  If a thread has more than LSLOT hits, the passes run over the
+//      registers instead.
 //   3. Ordered output: chunk r of the row is vector r * NTR + t of thread t.
-//      Per chunk and element, each wave's counts and lane prefixes come from
-//      ballots (popcounts and mbcnts); the chunk and wave offsets come from one
-//      table in LDS, so the whole output takes two barriers.
+//      When every copy of T is kept (the usual case), a key is kept iff
+//      key >= T, and each wave's counts and lane positions come from one ballot
+//      per key (popcounts and mbcnts).  With a tie at the cut, "> T" and "== T"
+//      are tracked apart and the first copies of T in index order are kept.  The
+//      chunk and wave offsets come from one table in LDS (two barriers).
+// A global int32 pointer the whole wave shares, moved to scalar registers.
+using GlobalI32 = __attribute__((address_space(1))) int32_t;
+__device__ __forceinline__ GlobalI32* uniform_global(int32_t* p) {
+  const uint64_t u = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+  return (GlobalI32*)(((uint64_t)hi << 32) | lo);
+}
 constexpr int NWR = NTR / 64;   // waves of the register path
-constexpr int CAND = 8192;      // candidate keys copied to LDS after the first pass
+constexpr int LSLOT = 24;       // candidate slots per thread after the first pass
+constexpr int CAND = LSLOT * NTR;
+
+constexpr int HCOPY = 4;        // histogram copies per wave (by lane % HCOPY): fewer lanes per address
+struct RegDescent {             // LDS of the descent
+  union {
+    struct {
+      int hist[NWR][HCOPY][257];                   // passes over the registers; bin 256: outside
+    } h;
+    struct {
+      uint32_t cand[(LSLOT + 1) * NTR];            // slot LSLOT: the sink of a full list
+    };
+  };
+};
+struct RegOutput {              // LDS of the ordered output
+  int wtot[REGV][NWR];                             // per chunk and wave: above T | copies of T << 16
+  int wpre[REGV][NWR];                             // kept in the chunk's earlier waves
+  int cbase[REGV];                                 // kept in earlier chunks
+  uint8_t eqm[REGV][NTR];                          // with a tie: each thread's copies of T per chunk
+};
+union RegShared {
+  RegDescent d;
+  RegOutput o;
+};
 
 __global__ void __launch_bounds__(NTR)
 select_reg_kernel(const float* __restrict__ S, int Hkv, int64_t n, I64s kk, int w, MutPtrs idx) {
-  __shared__ int hist[NWR][256];                   // one histogram per wave
-  __shared__ uint32_t cand[CAND];
+  __shared__ RegShared sh;
+  __shared__ int wh[257];                          // histogram of the passes over the lists
+  __shared__ uint32_t fin[64];                     // the last bin's keys
+  __shared__ int fcnt[1];
+  __shared__ int cut[4];                           // tie at the cut: chunk, wave, rank there; index
   __shared__ uint32_t red[2][NWR];
-  __shared__ int wtot[REGV][NWR];                  // per chunk and wave: gt | eq << 16
-  __shared__ int wpre[REGV][NWR];                  // exclusive prefix over waves, packed
-  __shared__ int cbase[REGV][2];                   // exclusive prefix over chunks (gt, eq)
   __shared__ int scan[NWR];
   __shared__ int pick[3];
-  __shared__ int wcnt[NWR];                        // candidates of each wave's list segment
-  __shared__ int flag[2];                          // crowded bins seen; a list segment overflowed
   const int tid = threadIdx.x, lane = tid & 63, wv = tid / 64;
   const int l = blockIdx.x / Hkv, g = blockIdx.x % Hkv;
   const int64_t k = kk.v[l];
   const float* row = S + ((int64_t)l * Hkv + g) * n;
-  int32_t* out = (int32_t*)idx.p[l] + (int64_t)g * k;
+  // the output row's address is uniform: held in scalar registers, with 32-bit
+  // unsigned offsets from it
+  GlobalI32* const out = uniform_global((int32_t*)idx.p[l] + (int64_t)g * k);
   if (k <= w) {                                   // the window alone overflows the budget
     for (int64_t j = tid; j < k; j += NTR) out[j] = (int32_t)(n - k + j);
     return;
@@ -250,41 +292,35 @@ select_reg_kernel(const float* __restrict__ S, int Hkv, int64_t n, I64s kk, int 
     return;
   }
   // the thread's vectors t + r NTR, loaded once (vectors past the row repeat its
-  // last one and are never counted); element 4 (r NTR + t) + e is in the row iff
-  // 4 r NTR + e < lim
+  // last one); element 4 (r NTR + t) + e is in the row iff 4 r NTR + e < lim
   uint4 rk[REGV];
   const int lim = nb - 4 * tid;
-  uint32_t kmin = ~0u, kmax = 0u;                 // the row's key range, formed as the keys arrive
+  uint32_t kmin = ~0u, kmax = 0u;                 // over the row's keys
   {
     const int nv = (nb + 3) / 4;
     const float4* row4 = reinterpret_cast<const float4*>(row);
     float4 t[REGV];
 #pragma unroll
     for (int r = 0; r < REGV; ++r) t[r] = row4[min(r * NTR + tid, nv - 1)];
-#pragma unroll
-    for (int r = 0; r < REGV; ++r) {
-      rk[r] = make_uint4(f32_key(t[r].x), f32_key(t[r].y), f32_key(t[r].z), f32_key(t[r].w));
-      const uint32_t k4[4] = {rk[r].x, rk[r].y, rk[r].z, rk[r].w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (4 * r * NTR + e < lim) { kmin = min(kmin, k4[e]); kmax = max(kmax, k4[e]); }
-    }
-  }
-  // f(key, in the row) for every held key.  The limit is made opaque per call
-  // so that the 136 row-membership masks are formed where they are used, not
-  // hoisted out of the pass loop and held in scalar registers across it.
-  auto each = [&](auto&& f) __attribute__((always_inline)) {
-    int lm = lim;
+    int lm = lim;                                 // opaque: the membership masks die here
     asm volatile("" : "+v"(lm));
 #pragma unroll
     for (int r = 0; r < REGV; ++r) {
-      f(rk[r].x, 4 * r * NTR + 0 < lm);
-      f(rk[r].y, 4 * r * NTR + 1 < lm);
-      f(rk[r].z, 4 * r * NTR + 2 < lm);
-      f(rk[r].w, 4 * r * NTR + 3 < lm);
+      uint32_t k4[4] = {f32_key(t[r].x), f32_key(t[r].y), f32_key(t[r].z), f32_key(t[r].w)};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bool in = 4 * r * NTR + e < lm;
+        kmin = min(kmin, in ? k4[e] : ~0u);
+        k4[e] = in ? k4[e] : 0u;
+        kmax = max(kmax, k4[e]);
+      }
+      rk[r] = make_uint4(k4[0], k4[1], k4[2], k4[3]);
     }
+  }
+  auto each = [&](auto&& f) __attribute__((always_inline)) {
+#pragma unroll
+    for (int r = 0; r < REGV; ++r) { f(rk[r].x); f(rk[r].y); f(rk[r].z); f(rk[r].w); }
   };
-  // ---- 1. the row's key range
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) {
     kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o, 64));
@@ -294,182 +330,272 @@ select_reg_kernel(const float* __restrict__ S, int Hkv, int64_t n, I64s kk, int 
   __syncthreads();
 #pragma unroll
   for (int x = 0; x < NWR; ++x) { kmin = min(kmin, red[0][x]); kmax = max(kmax, red[1][x]); }
-  // ---- 2. descent over the range: T = the need-th largest key, above = keys > T
+  // ---- descent: T = the need-th largest key, above = keys > T, eqc = keys == T
+  // (eqc may include pad keys when T is the lowest key; then it exceeds the
+  // copies of T that are kept, and the output takes the tie path)
   uint32_t lo = kmin;
-  int above = 0, rem = need;
+  int above = 0, rem = need, eqc = nb;
   if (kmax != kmin) {
     int sp = 32 - __builtin_clz(kmax - kmin);   // the range is [lo, lo + 2^sp)
     bool list = false;
+    int cnt = 0;                                  // the thread's list length
 #pragma unroll 1
-    for (;;) {
-      const int s = sp > 8 ? sp - 8 : 0;          // bin width 2^s: at most 256 bins
+    for (int pass = 0;; ++pass) {
+      const int s = sp > 8 ? sp - 8 : 0;          // bin width 2^s
       const uint32_t dmax = sp >= 32 ? ~0u : (1u << sp) - 1u;
-      for (int i = tid; i < NWR * 256; i += NTR) (&hist[0][0])[i] = 0;
-      if (tid == 0) flag[0] = 0;
+      const uint32_t nbin = (dmax >> s) + 1u;     // <= 256; key - lo > dmax <=> bin >= nbin
+      for (int i = tid; i < NWR * HCOPY * 257; i += NTR) (&sh.d.h.hist[0][0][0])[i] = 0;
       __syncthreads();
-      // keys in [lo, lo + 2^sp): key - lo <= dmax (a key below lo wraps past
-      // dmax, except in the first pass, where every key is >= lo); bin
-      // (key - lo) >> s, below 256 for every valid key
-      auto bin_of = [&](uint32_t key, bool in, bool& valid) __attribute__((always_inline)) {
-        const uint32_t d = key - lo;
-        valid = in && d <= dmax;
-        return (int)(d >> s);
-      };
-      auto count_agg = [&](uint32_t key, bool in) __attribute__((always_inline)) {
-        bool v;
-        const int b = bin_of(key, in, v);
-        hist_add(hist[wv], v, b);
-      };
-      if (list) {
-        for (int i = tid; i < CAND; i += NTR) count_agg(cand[i], (i & (CAND / NWR - 1)) < wcnt[i / (CAND / NWR)]);
-      } else {
-        // A sample (two chunks of the row) tells whether many lanes share bins;
-        // if not, every lane adds its own 1 (no ballots), else the wave
-        // aggregates per bin.
-        bool crowd = false;
-        int lm = lim;
-        asm volatile("" : "+v"(lm));
-#pragma unroll
-        for (int r = 0; r < REGV; r += REGV / 2) {
-          const uint32_t k4[4] = {rk[r].x, rk[r].y, rk[r].z, rk[r].w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            bool v;
-            const int b = bin_of(k4[e], 4 * r * NTR + e < lm, v);
-            const uint64_t act = __ballot(v);
-            if (act) {
-              const int b0 = __builtin_amdgcn_readlane(b, __builtin_ctzll(act));
-              crowd |= __builtin_popcountll(__ballot(v && b == b0)) >= 16;
-            }
-          }
-        }
-        if (crowd && lane == 0) flag[0] = 1;
-        __syncthreads();
-        if (flag[0]) {
-          each(count_agg);
-        } else {
-          each([&](uint32_t key, bool in) {
-            bool v;
-            const int b = bin_of(key, in, v);
-            if (v) atomicAdd(&hist[wv][b], 1);
-          });
-        }
+      {
+        int* hh = sh.d.h.hist[wv][lane % HCOPY];
+        each([&](uint32_t key) { atomicAdd(&hh[min((key - lo) >> s, nbin)], 1); });
       }
       __syncthreads();
       int c = 0;
-      if (tid < 256) {
+      if (tid < 256 && 255 - tid < (int)nbin) {
 #pragma unroll
-        for (int x = 0; x < NWR; ++x) c += hist[x][255 - tid];
+        for (int x = 0; x < NWR * HCOPY; ++x) c += (&sh.d.h.hist[0][0][0])[x * 257 + 255 - tid];
       }
       int tot;
       const int incl = block_exclusive_scan<NTR>(c, scan, &tot) + c;
       if (tid < 256 && incl >= rem && incl - c < rem) { pick[0] = 255 - tid; pick[1] = incl - c; pick[2] = c; }
       __syncthreads();
-      const int b = pick[0], bin_count = pick[2];
+      const int b = pick[0];
+      eqc = pick[2];
       above += pick[1];
       rem -= pick[1];
       lo += (uint32_t)b << s;
       sp = s;
       if (s == 0) break;
-      if (!list && bin_count <= CAND) {         // the chosen bin's keys to LDS
-        // each wave appends to its own segment of CAND / NWR slots (a running
-        // count, no atomics); a segment that would overflow drops the list
-        constexpr int SEG = CAND / NWR;
+      if (pass == 0 && eqc <= CAND) {             // the chosen bin's keys to per-thread lists
         const uint32_t width = 1u << s;
-        int wn = 0;                               // wave-uniform
-        if (tid == 0) flag[1] = 0;
-        each([&](uint32_t key, bool in) {
-          const bool hit = in && key >= lo && key - lo < width;
-          const uint64_t m = __ballot(hit);
-          if (m) {
-            const int at = wn + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
-                                                               __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-            if (hit && at < SEG) cand[wv * SEG + at] = key;
-            wn += __builtin_popcountll(m);
-          }
+        each([&](uint32_t key) {
+          sh.d.cand[min(cnt, LSLOT) * NTR + tid] = key;
+          cnt += key - lo < width ? 1 : 0;
         });
-        __syncthreads();                          // flag[1] cleared before any wave sets it
-        if (lane == 0) {
-          wcnt[wv] = wn;
-          if (wn > SEG) flag[1] = 1;
+        list = !__syncthreads_or(cnt > LSLOT);
+        if (list) break;
+      }
+    }
+    if (list) {
+      // The remaining passes read each thread's own list (one 256-bin histogram
+      // for the block).  Once the chosen bin holds at most 64 keys they are
+      // gathered and wave 0 ranks them directly.
+      auto list_keys = [&](auto&& f) __attribute__((always_inline)) {
+#pragma unroll 1
+        for (int j = 0; j < cnt; j += 4) {        // four reads in flight
+          uint32_t x[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) x[q] = sh.d.cand[min(j + q, LSLOT) * NTR + tid];
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            if (j + q < cnt) f(x[q]);
+        }
+      };
+#pragma unroll 1
+      for (;;) {
+        const int s = sp > 8 ? sp - 8 : 0;
+        const uint32_t nbin = (((1u << sp) - 1u) >> s) + 1u;   // sp < 32 here
+        if (tid < 257) wh[tid] = 0;
+        if (tid == 0) fcnt[0] = 0;
+        __syncthreads();
+        list_keys([&](uint32_t key) { atomicAdd(&wh[min((key - lo) >> s, nbin)], 1); });
+        __syncthreads();
+        if (wv == 0) {                            // lane i walks bins 255 - 4i - q downwards
+          int c4[4], sum = 0;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int bn = 255 - 4 * lane - q;
+            c4[q] = bn < (int)nbin ? wh[bn] : 0;
+            sum += c4[q];
+          }
+          int run = wave_inclusive_scan(sum) - sum;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            if (run < rem && run + c4[q] >= rem) { pick[0] = 255 - 4 * lane - q; pick[1] = run; pick[2] = c4[q]; }
+            run += c4[q];
+          }
         }
         __syncthreads();
-        list = flag[1] == 0;
+        eqc = pick[2];
+        above += pick[1];
+        rem -= pick[1];
+        lo += (uint32_t)pick[0] << s;
+        sp = s;
+        if (s == 0) break;
+        if (eqc <= 64) {                          // gather the bin's keys, then rank them in wave 0
+          const uint32_t width = 1u << s;
+          list_keys([&](uint32_t key) {
+            if (key - lo < width) {
+              const int at = atomicAdd(&fcnt[0], 1);
+              if (at < 64) fin[at] = key;
+            }
+          });
+          __syncthreads();
+          if (wv == 0) {
+            const bool valid = lane < eqc;
+            const uint32_t x = valid ? fin[lane] : 0u;
+            int gt = 0, ge = 0;
+#pragma unroll 1
+            for (int j = 0; j < eqc; ++j) {
+              const uint32_t y = __builtin_amdgcn_readlane(x, j);
+              gt += y > x ? 1 : 0;
+              ge += y >= x ? 1 : 0;
+            }
+            const uint64_t hm = __ballot(valid && gt < rem && ge >= rem);
+            if (hm != 0 && lane == (int)__builtin_ctzll(hm)) { pick[0] = (int)x; pick[1] = gt; pick[2] = ge - gt; }
+          }
+          __syncthreads();
+          lo = (uint32_t)pick[0];
+          above += pick[1];
+          eqc = pick[2];
+          break;
+        }
       }
     }
   }
-  const uint32_t T = lo;
+  const uint32_t T = __builtin_amdgcn_readfirstlane(lo);
   const int teq = need - above;                   // >= 1 copies of T are kept
-  // ---- 3. ordered output.  Per chunk and element e, the lanes keeping their
-  // element as "> T" or "== T" are compare masks, so the wave totals are
-  // popcounts and a lane's prefix is a sum of mbcnts.
   const int nchunk = (nb + 4 * NTR - 1) / (4 * NTR);
-  auto masks = [&](int r, bool (&g)[4], bool (&q)[4]) __attribute__((always_inline)) {
-    const uint32_t k4[4] = {rk[r].x, rk[r].y, rk[r].z, rk[r].w};
-    int lm = lim;
-    asm volatile("" : "+v"(lm));
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const bool in = 4 * r * NTR + e < lm;
-      g[e] = in && k4[e] > T;
-      q[e] = in && k4[e] == T;
-    }
+  const bool untied = eqc == teq;                 // every copy of T kept (T > 0 then)
+  __syncthreads();                                // the descent's LDS is reused below
+  // ---- ordered output.  Chunk r is vector r * NTR + t of every thread t, so a
+  // lane's place is the chunk's offset, its wave's offset in the chunk, and the
+  // kept elements of the lanes below it (mbcnts of one ballot per element).
+  // Without a tie at the cut, a key is kept iff key >= T.  With one, the kept
+  // copies of T are the first teq in index order; with c the index of the last
+  // of them, a key is kept iff key > T, or key == T and its index <= c.  Pad
+  // keys need no test: they are never above T, and their places (past n - w)
+  // come after every copy of T in the row, of which there are at least teq.
+  //   1. per chunk and wave: keys above T and copies of T (popcounts);
+  //   2. wave 0, one lane per chunk: offsets that count the copies of T only
+  //      up to copy teq, and the chunk, wave and rank there of copy teq;
+  //   3. with a tie, that wave finds the copy's lane and element, hence c;
+  //   4. one masked store per kept element.
+  // Chunk loops end at the row's last chunk; the bound is made opaque per loop
+  // so that no per-chunk flags are kept across loops.
+  auto below = [&](uint64_t m, int base) __attribute__((always_inline)) {   // base + set lanes below this one
+    return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, (uint32_t)base));
   };
-  auto below = [&](uint64_t m) __attribute__((always_inline)) {   // set lanes below this one
-    return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+  auto bound = [&]() __attribute__((always_inline)) {
+    int c = nchunk;
+    asm volatile("" : "+s"(c));
+    return c;
   };
+  const int last = need - 1;                      // places are < need; the clamp keeps any slip in the row
+  if (untied) {
+    const int nc = bound();
 #pragma unroll
-  for (int r = 0; r < REGV; ++r) {
-    if (r < nchunk) {                             // uniform
-      bool g[4], q[4];
-      masks(r, g, q);
-      int tg = 0, te = 0;
+    for (int r = 0; r < REGV; ++r) {
+      if (r < nc) {                              // uniform
+        const uint32_t k4[4] = {rk[r].x, rk[r].y, rk[r].z, rk[r].w};
+        int tg = 0;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) { tg += __builtin_popcountll(__ballot(g[e])); te += __builtin_popcountll(__ballot(q[e])); }
-      if (lane == 0) wtot[r][wv] = tg | (te << 16);
-    }
-  }
-  __syncthreads();
-  if (tid < 64) {                                 // wave 0: offsets of chunks and waves
-    int cg = 0, ce = 0;
-    if (tid < nchunk) {
-      int run = 0;
-#pragma unroll
-      for (int x = 0; x < NWR; ++x) { wpre[tid][x] = run; run += wtot[tid][x]; }
-      cg = run & 0xffff;
-      ce = run >> 16;
-    }
-    const int ig = wave_inclusive_scan(cg), ie = wave_inclusive_scan(ce);
-    if (tid < nchunk) { cbase[tid][0] = ig - cg; cbase[tid][1] = ie - ce; }
-  }
-  __syncthreads();
-#pragma unroll
-  for (int r = 0; r < REGV; ++r) {
-    if (r < nchunk) {                             // uniform
-      bool g[4], q[4];
-      masks(r, g, q);
-      const int wp = wpre[r][wv];
-      int gtb = cbase[r][0] + (wp & 0xffff), eqb = cbase[r][1] + (wp >> 16);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) gtb += below(__ballot(g[e]));
-      const bool anyq = __ballot(q[0] || q[1] || q[2] || q[3]) != 0;   // rare: copies of T
-      if (anyq) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) eqb += below(__ballot(q[e]));
+        for (int e = 0; e < 4; ++e) tg += __builtin_popcountll(__ballot(k4[e] >= T));
+        if (lane == 0) sh.o.wtot[r][wv] = tg;
       }
-      const int i0 = 4 * (r * NTR + tid);
+    }
+  } else {
+    const int nc = bound();
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {              // positions without branches, one masked store
-        const int pos = gtb + min(eqb, teq);      // for "== T" kept: eqb < teq, so pos = gtb + eqb
-        const bool keep = g[e] || (q[e] && eqb < teq);
-        if (keep) out[pos] = i0 + e;
-        gtb += g[e] ? 1 : 0;
-        eqb += q[e] ? 1 : 0;
+    for (int r = 0; r < REGV; ++r) {
+      if (r < nc) {                              // uniform
+        const uint32_t k4[4] = {rk[r].x, rk[r].y, rk[r].z, rk[r].w};
+        int tg = 0, te = 0;
+        uint32_t q = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          tg += __builtin_popcountll(__ballot(k4[e] > T));
+          te += __builtin_popcountll(__ballot(k4[e] == T));
+          q |= (k4[e] == T ? 1u : 0u) << e;
+        }
+        sh.o.eqm[r][tid] = (uint8_t)q;
+        if (lane == 0) sh.o.wtot[r][wv] = tg | (te << 16);
+      }
+    }
+  }
+  if (tid == 0) { cut[0] = -1; cut[1] = -1; cut[2] = 0; cut[3] = -1; }
+  __syncthreads();
+  if (tid < 64) {
+    int ce = 0;
+    if (tid < nchunk) {
+#pragma unroll
+      for (int x = 0; x < NWR; ++x) ce += sh.o.wtot[tid][x] >> 16;
+    }
+    int eb = wave_inclusive_scan(ce) - ce;        // copies of T before chunk tid
+    int run = 0;
+    if (tid < nchunk) {
+#pragma unroll
+      for (int x = 0; x < NWR; ++x) {
+        const int wt = sh.o.wtot[tid][x], tg = wt & 0xffff, te = wt >> 16;
+        if (eb < teq && teq <= eb + te) { cut[0] = tid; cut[1] = x; cut[2] = teq - eb; }
+        sh.o.wpre[tid][x] = run;
+        run += tg + min(max(teq - eb, 0), te);    // kept: the copies of T up to copy teq
+        eb += te;
+      }
+    }
+    const int inc = wave_inclusive_scan(run);
+    if (tid < nchunk) sh.o.cbase[tid] = inc - run;
+  }
+  __syncthreads();
+  if (untied) {
+    const int nc = bound();
+#pragma unroll
+    for (int r = 0; r < REGV; ++r) {
+      if (r < nc) {                              // uniform
+        const uint32_t k4[4] = {rk[r].x, rk[r].y, rk[r].z, rk[r].w};
+        int pos = __builtin_amdgcn_readfirstlane(sh.o.cbase[r] + sh.o.wpre[r][wv]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pos = below(__ballot(k4[e] >= T), pos);
+        const int i0 = 4 * (r * NTR + tid);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const bool kp = k4[e] >= T;
+          if (kp) out[(uint32_t)min(pos, last)] = i0 + e;
+          pos += kp ? 1 : 0;
+        }
+      }
+    }
+    return;
+  }
+  const int cr = cut[0], cx = cut[1], ck = cut[2];
+  if (cr >= 0 && wv == cx) {                      // the wave holding copy teq: its lane and element
+    const uint32_t q = sh.o.eqm[cr][tid];
+    const int own = __builtin_popcount(q);
+    const int bl = wave_inclusive_scan(own) - own;   // copies in the lanes below
+    if (bl < ck && ck <= bl + own) {
+      int left = ck - bl, e = 0;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const bool one = (q >> b) & 1u;
+        if (one && left == 1) e = b;
+        left -= one ? 1 : 0;
+      }
+      cut[3] = 4 * (cr * NTR + tid) + e;
+    }
+  }
+  __syncthreads();
+  const int cidx = cut[3];
+  const int nc = bound();
+#pragma unroll
+  for (int r = 0; r < REGV; ++r) {
+    if (r < nc) {                              // uniform
+      const uint32_t k4[4] = {rk[r].x, rk[r].y, rk[r].z, rk[r].w};
+      const int i0 = 4 * (r * NTR + tid);
+      bool kp[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) kp[e] = (k4[e] > T) | ((k4[e] == T) & (i0 + e <= cidx));   // no branches
+      int pos = __builtin_amdgcn_readfirstlane(sh.o.cbase[r] + sh.o.wpre[r][wv]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) pos = below(__ballot(kp[e]), pos);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (kp[e]) out[(uint32_t)min(pos, last)] = i0 + e;
+        pos += kp[e] ? 1 : 0;
       }
     }
   }
 }
-
 }  // namespace
 }  // namespace kvc
 

@@ -385,6 +385,10 @@ SELECT_CASES = [
     (1, 2, 36844, 9000, 0, 2),       # the longest row LDS holds beside the histograms
     (1, 2, 36848, 9000, 0, 2),       # one vector longer: re-read from memory
     (2, 1, 50, 1, 0, 1),             # one token, all tied
+    (1, 2, 102400, 25600, 31, 0),    # rows in registers; n - w not a multiple of 4
+    (1, 2, 40000, 10000, 32, 0),     # rows in registers, fewer chunks than registers hold
+    (1, 3, 65536, 100, 32, 3),       # rows in registers, small budget, ties
+    (1, 2, 102400, 102000, 32, 0),   # rows in registers, nearly everything kept
     (34, 2, 300, 64, 16, 0),         # more layers than one launch holds
 ]
 
@@ -451,6 +455,58 @@ def test_select_unaligned_scores(dev):
     for l in range(L):
         np.testing.assert_array_equal(b[l].cpu().numpy(), a[l].cpu().numpy())
         np.testing.assert_array_equal(a[l].cpu().numpy(), infokv.select_topk(Sn[l], k, w))
+
+
+@pytest.mark.parametrize("distinct", [True, False], ids=["distinct", "tied"])
+def test_select_register_rows_crowded_thread(dev, distinct):
+    """Rows of 102400 scores are held in registers, thread t of the workgroup
+    holding the scores whose index i has (i // 4) % 512 == t.  Here the 200
+    scores of one thread sit in the first pass's chosen bin (distinct values
+    one float step apart, or all equal to the cut), so that thread's candidate
+    list overflows and the remaining passes run over the registers.  The kept
+    sets must still equal the oracle's."""
+    L, Hkv, n, k, w = 1, 2, 102400, 25600, 32
+    announce("select crowded thread", distinct)
+    S = synth.random_scores((L, Hkv, n), dev, seed=21).cpu().numpy()
+    nb, need = n - w, k - w
+    sel = np.nonzero((np.arange(nb) // 4) % 512 == 7)[0]
+    for h in range(Hkv):
+        row = S[0, h]
+        v = np.sort(row[:nb])[::-1][need - 1]
+        if distinct:
+            bits = np.float32(v).view(np.uint32) + np.arange(len(sel), dtype=np.uint32) - np.uint32(len(sel) // 2)
+            row[sel] = bits.view(np.float32)
+        else:
+            row[sel] = v
+    St = torch.from_numpy(S).to(dev)
+    idx = [torch.full((Hkv, k), -1, dtype=torch.int32, device=dev)]
+    B().kvc_select_topk(St, [k], w, idx)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(idx[0].cpu().numpy(), infokv.select_topk(S[0], k, w))
+
+
+@pytest.mark.parametrize("copies", [2, 7, 300])
+def test_select_register_rows_few_ties_at_cut(dev, copies):
+    """Rows held in registers with a few copies of the cut value spread over the
+    row (other scores distinct): only the first copies in index order are kept,
+    found from the chunk and wave holding the last kept copy."""
+    L, Hkv, n, k, w = 2, 4, 102400, 25600, 32
+    announce("select few ties", copies)
+    S = synth.random_scores((L, Hkv, n), dev, seed=31 + copies).cpu().numpy()
+    nb, need = n - w, k - w
+    rng = np.random.default_rng(copies)
+    for l in range(L):
+        for h in range(Hkv):
+            row = S[l, h]
+            v = np.sort(row[:nb])[::-1][need - 1 - h]     # the cut lands on copy h + 1 or beyond
+            at = rng.choice(nb, size=copies, replace=False)
+            row[at] = v
+    St = torch.from_numpy(S).to(dev)
+    idx = [torch.full((Hkv, k), -1, dtype=torch.int32, device=dev) for _ in range(L)]
+    B().kvc_select_topk(St, [k] * L, w, idx)
+    torch.cuda.synchronize()
+    for l in range(L):
+        np.testing.assert_array_equal(idx[l].cpu().numpy(), infokv.select_topk(S[l], k, w))
 
 
 def test_select_deterministic(dev):
