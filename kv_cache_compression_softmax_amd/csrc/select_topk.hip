@@ -264,6 +264,7 @@ union RegShared {
   RegOutput o;
 };
 
+template <int RV>
 __global__ void __launch_bounds__(NTR)
 select_reg_kernel(const float* __restrict__ S, int Hkv, int64_t n, I64s kk, int w, MutPtrs idx) {
   __shared__ RegShared sh;
@@ -293,19 +294,19 @@ select_reg_kernel(const float* __restrict__ S, int Hkv, int64_t n, I64s kk, int 
   }
   // the thread's vectors t + r NTR, loaded once (vectors past the row repeat its
   // last one); element 4 (r NTR + t) + e is in the row iff 4 r NTR + e < lim
-  uint4 rk[REGV];
+  uint4 rk[RV];
   const int lim = nb - 4 * tid;
   uint32_t kmin = ~0u, kmax = 0u;                 // over the row's keys
   {
     const int nv = (nb + 3) / 4;
     const float4* row4 = reinterpret_cast<const float4*>(row);
-    float4 t[REGV];
+    float4 t[RV];
 #pragma unroll
-    for (int r = 0; r < REGV; ++r) t[r] = row4[min(r * NTR + tid, nv - 1)];
+    for (int r = 0; r < RV; ++r) t[r] = row4[min(r * NTR + tid, nv - 1)];
     int lm = lim;                                 // opaque: the membership masks die here
     asm volatile("" : "+v"(lm));
 #pragma unroll
-    for (int r = 0; r < REGV; ++r) {
+    for (int r = 0; r < RV; ++r) {
       uint32_t k4[4] = {f32_key(t[r].x), f32_key(t[r].y), f32_key(t[r].z), f32_key(t[r].w)};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -319,7 +320,7 @@ select_reg_kernel(const float* __restrict__ S, int Hkv, int64_t n, I64s kk, int 
   }
   auto each = [&](auto&& f) __attribute__((always_inline)) {
 #pragma unroll
-    for (int r = 0; r < REGV; ++r) { f(rk[r].x); f(rk[r].y); f(rk[r].z); f(rk[r].w); }
+    for (int r = 0; r < RV; ++r) { f(rk[r].x); f(rk[r].y); f(rk[r].z); f(rk[r].w); }
   };
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) {
@@ -486,7 +487,7 @@ select_reg_kernel(const float* __restrict__ S, int Hkv, int64_t n, I64s kk, int 
   if (untied) {
     const int nc = bound();
 #pragma unroll
-    for (int r = 0; r < REGV; ++r) {
+    for (int r = 0; r < RV; ++r) {
       if (r < nc) {                              // uniform
         const uint32_t k4[4] = {rk[r].x, rk[r].y, rk[r].z, rk[r].w};
         int tg = 0;
@@ -498,7 +499,7 @@ select_reg_kernel(const float* __restrict__ S, int Hkv, int64_t n, I64s kk, int 
   } else {
     const int nc = bound();
 #pragma unroll
-    for (int r = 0; r < REGV; ++r) {
+    for (int r = 0; r < RV; ++r) {
       if (r < nc) {                              // uniform
         const uint32_t k4[4] = {rk[r].x, rk[r].y, rk[r].z, rk[r].w};
         int tg = 0, te = 0;
@@ -541,7 +542,7 @@ select_reg_kernel(const float* __restrict__ S, int Hkv, int64_t n, I64s kk, int 
   if (untied) {
     const int nc = bound();
 #pragma unroll
-    for (int r = 0; r < REGV; ++r) {
+    for (int r = 0; r < RV; ++r) {
       if (r < nc) {                              // uniform
         const uint32_t k4[4] = {rk[r].x, rk[r].y, rk[r].z, rk[r].w};
         int pos = __builtin_amdgcn_readfirstlane(sh.o.cbase[r] + sh.o.wpre[r][wv]);
@@ -578,7 +579,7 @@ select_reg_kernel(const float* __restrict__ S, int Hkv, int64_t n, I64s kk, int 
   const int cidx = cut[3];
   const int nc = bound();
 #pragma unroll
-  for (int r = 0; r < REGV; ++r) {
+  for (int r = 0; r < RV; ++r) {
     if (r < nc) {                              // uniform
       const uint32_t k4[4] = {rk[r].x, rk[r].y, rk[r].z, rk[r].w};
       const int i0 = 4 * (r * NTR + tid);
@@ -629,8 +630,14 @@ extern "C" int kvc_select_topk(const float* S, int L, int Hkv, int64_t n, const 
                 hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)cache) == hipSuccess;
     if (!use_cache) (void)hipGetLastError();      // a refused query only selects the other path
   }
-  // a row too long for LDS but within REGV vectors per thread stays in registers
-  const bool use_reg = vec && !use_cache && n > w && (n - w + 3) / 4 <= (int64_t)REGV * NTR;
+  // A row of more than 8192 scores, up to REGV vectors per thread, is held in
+  // registers (16 vectors per thread when that holds it): 50 -> 22 us for 256
+  // rows of 32768 scores against the LDS copy.  Shorter rows, where the LDS
+  // path was a little faster (a decode period's 7577-slot rows), keep it; a row
+  // too long for either is re-read by every pass.
+  const int64_t nvr = (n - w + 3) / 4;
+  const bool use_reg = vec && n > w && nvr <= (int64_t)REGV * NTR && (nvr > 4 * NTR || !use_cache);
+  const bool rv16 = nvr <= 16 * NTR;
   for (int l0 = 0; l0 < L; l0 += kLayersPerLaunch) {
     const int lc = min(kLayersPerLaunch, L - l0);
     I64s kk{};
@@ -638,8 +645,9 @@ extern "C" int kvc_select_topk(const float* S, int L, int Hkv, int64_t n, const 
     for (int i = 0; i < lc; ++i) { kk.v[i] = k_keep[l0 + i]; ip.p[i] = idx_out[l0 + i]; }
     const dim3 grid((unsigned)(lc * Hkv));
     const float* Sl = S + (int64_t)l0 * Hkv * n;
-    if (use_cache) hipLaunchKernelGGL((select_kernel<true, true>), grid, dim3(NT), cache, s, Sl, Hkv, n, kk, w, ip);
-    else if (use_reg) hipLaunchKernelGGL(select_reg_kernel, grid, dim3(NTR), 0, s, Sl, Hkv, n, kk, w, ip);
+    if (use_reg && rv16) hipLaunchKernelGGL(select_reg_kernel<16>, grid, dim3(NTR), 0, s, Sl, Hkv, n, kk, w, ip);
+    else if (use_reg) hipLaunchKernelGGL(select_reg_kernel<REGV>, grid, dim3(NTR), 0, s, Sl, Hkv, n, kk, w, ip);
+    else if (use_cache) hipLaunchKernelGGL((select_kernel<true, true>), grid, dim3(NT), cache, s, Sl, Hkv, n, kk, w, ip);
     else if (vec) hipLaunchKernelGGL((select_kernel<true, false>), grid, dim3(NT), 0, s, Sl, Hkv, n, kk, w, ip);
     else hipLaunchKernelGGL((select_kernel<false, false>), grid, dim3(NT), 0, s, Sl, Hkv, n, kk, w, ip);
   }

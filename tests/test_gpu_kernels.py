@@ -378,12 +378,15 @@ SELECT_CASES = [
     (1, 4, 4000, 32, 32, 0),         # window only
     (1, 4, 4000, 10, 32, 0),         # budget smaller than the window
     (1, 4, 999, 300, 0, 3),          # no window
-    (1, 2, 102400, 25600, 32, 0),    # SelKV length
-    (1, 2, 102400, 25600, 32, 4),    # SelKV length with ties: 16-byte loads, row re-read
+    (1, 2, 102400, 25600, 32, 0),    # SelKV length (row held in registers, 50 vectors per thread)
+    (1, 2, 102400, 25600, 32, 4),    # SelKV length with ties
     (2, 8, 4096, 834, 31, 5),        # ties; n - w not a multiple of 4 (row held in LDS)
-    (1, 4, 32768, 6553, 32, 0),      # InfoKV length (row held in LDS)
-    (1, 2, 36844, 9000, 0, 2),       # the longest row LDS holds beside the histograms
-    (1, 2, 36848, 9000, 0, 2),       # one vector longer: re-read from memory
+    (1, 2, 8192, 2000, 0, 0),        # the longest row that stays in LDS
+    (1, 2, 8196, 2000, 0, 3),        # one vector longer: registers, 16 vectors per thread
+    (1, 4, 32768, 6553, 32, 0),      # InfoKV length (registers, 16 vectors per thread)
+    (1, 2, 36844, 9000, 0, 2),       # registers, 50 vectors per thread from here on
+    (1, 2, 110000, 20000, 32, 0),    # longer than registers hold: re-read from memory
+    (1, 2, 110000, 20000, 32, 3),    # the same with ties
     (2, 1, 50, 1, 0, 1),             # one token, all tied
     (1, 2, 102400, 25600, 31, 0),    # rows in registers; n - w not a multiple of 4
     (1, 2, 40000, 10000, 32, 0),     # rows in registers, fewer chunks than registers hold
