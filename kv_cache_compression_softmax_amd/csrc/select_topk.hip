@@ -207,9 +207,9 @@ select_kernel(const float* __restrict__ S, int Hkv, int64_t n, I64s kk, int w, M
 // A row of up to REGV * NTR vectors of 4 scores (102400 scores) is held in
 // registers, as order-preserving keys, by a workgroup of NTR threads: thread t
 // keeps vectors t, t + NTR, ..., all loads in flight together, so the row is read
-// once.  Every step over the held keys is unrolled, so its body per key is kept
-// to a few instructions: the unrolled code is streamed through the instruction
-// cache on every step.
+// once.  Every step over the held keys is unrolled over all of them, so a step
+// costs its body's instruction count per key: each body is kept to a few
+// instructions, with no per-key membership tests and no exec-mask branches.
 //   0. Keys outside [0, n - w) (the window, and the repeated last vector) are
 //      replaced by key 0, the lowest key; the row's smallest and largest keys
 //      are taken over the row alone.  Extra copies of the lowest key never move
