@@ -392,6 +392,11 @@ SELECT_CASES = [
     (1, 2, 40000, 10000, 32, 0),     # rows in registers, fewer chunks than registers hold
     (1, 3, 65536, 100, 32, 3),       # rows in registers, small budget, ties
     (1, 2, 102400, 102000, 32, 0),   # rows in registers, nearly everything kept
+    (1, 2, 40000, 40000, 32, 0),     # rows in registers: keep everything
+    (1, 2, 40000, 32, 32, 0),        # rows in registers: window only
+    (1, 2, 40000, 20, 32, 0),        # rows in registers: budget smaller than the window
+    (1, 2, 40000, 33, 32, 2),        # rows in registers: one token besides the window, ties
+    (1, 2, 40000, 39999, 32, 2),     # rows in registers: all but one, ties
     (34, 2, 300, 64, 16, 0),         # more layers than one launch holds
 ]
 
