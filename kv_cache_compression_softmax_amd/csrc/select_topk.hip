@@ -204,10 +204,10 @@ select_kernel(const float* __restrict__ S, int Hkv, int64_t n, I64s kk, int w, M
 }
 
 // ---------------------------------------------------------------- register path
-// A row of up to REGV * NTR vectors of 4 scores (102400 scores) is held in
-// registers, as order-preserving keys, by a workgroup of NTR threads: thread t
-// keeps vectors t, t + NTR, ..., all loads in flight together, so the row is read
-// once.  Every step over the held keys is unrolled over all of them, so a step
+// A row of up to RV * NTR vectors of 4 scores (RV = 16 or REGV: 32768 or 102400
+// scores) is held in registers, as order-preserving keys, by a workgroup of NTR
+// threads: thread t keeps vectors t, t + NTR, ..., all loads in flight together,
+// so the row is read once.  Every step over the held keys is unrolled over all of them, so a step
 // costs its body's instruction count per key: each body is kept to a few
 // instructions, with no per-key membership tests and no exec-mask branches.
 //   0. Keys outside [0, n - w) (the window, and the repeated last vector) are
@@ -220,16 +220,18 @@ select_kernel(const float* __restrict__ S, int Hkv, int64_t n, I64s kk, int w, M
 //      bin holding the need-th largest key becomes the next range.
 //   2. After the first pass every thread copies its keys of the chosen bin to
 //      its own LDS slots (slot j of thread t at j * NTR + t; the key is written
-//      at every step and the slot advances on a hit, so no branches).  The
-//      remaining passes run in one wave over these lists, without block
-//      barriers.  If a thread has more than LSLOT hits, the passes run over the
-//      registers instead.
+//      at every step and the slot advances on a hit, so no branches).  The next
+//      passes read each thread's own list into one histogram for the block;
+//      once the chosen bin holds at most 64 keys they are gathered and one wave
+//      ranks them.  If a thread has more than LSLOT hits, the passes run over
+//      the registers instead.
 //   3. Ordered output: chunk r of the row is vector r * NTR + t of thread t.
 //      When every copy of T is kept (the usual case), a key is kept iff
 //      key >= T, and each wave's counts and lane positions come from one ballot
-//      per key (popcounts and mbcnts).  With a tie at the cut, "> T" and "== T"
-//      are tracked apart and the first copies of T in index order are kept.  The
-//      chunk and wave offsets come from one table in LDS (two barriers).
+//      per key (popcounts and mbcnts).  With a tie at the cut, the index c of
+//      the last kept copy of T is found first, and a key is kept iff key > T or
+//      (key == T and index <= c), again one ballot per key.  The chunk and
+//      wave offsets come from one table in LDS.
 // A global int32 pointer the whole wave shares, moved to scalar registers.
 using GlobalI32 = __attribute__((address_space(1))) int32_t;
 __device__ __forceinline__ GlobalI32* uniform_global(int32_t* p) {
