@@ -216,8 +216,11 @@ select_kernel(const float* __restrict__ S, int Hkv, int64_t n, I64s kk, int w, M
 //      the need-th largest key (need < n - w) and are never counted above it.
 //   1. Each pass cuts the current key range [lo, lo + 2^sp) into nbin <= 256
 //      bins of width 2^(sp-8), so scores spread over a few binades fill many
-//      bins.  A key outside the range lands in bin nbin, which is not read.  The
-//      bin holding the need-th largest key becomes the next range.
+//      bins.  A key outside the range lands in bin nbin, which is not read; keys
+//      below lo are tested as such, since key - lo wraps into the range when the
+//      range spans 2^31 or more (scores of both signs) or lies near the top of
+//      the key space.  The bin holding the need-th largest key becomes the next
+//      range.
 //   2. After the first pass every thread copies its keys of the chosen bin to
 //      its own LDS slots (slot j of thread t at j * NTR + t; the key is written
 //      at every step and the slot advances on a hit, so no branches).  The next
@@ -351,7 +354,7 @@ select_reg_kernel(const float* __restrict__ S, int Hkv, int64_t n, I64s kk, int 
       __syncthreads();
       {
         int* hh = sh.d.h.hist[wv][lane % HCOPY];
-        each([&](uint32_t key) { atomicAdd(&hh[min((key - lo) >> s, nbin)], 1); });
+        each([&](uint32_t key) { atomicAdd(&hh[key >= lo ? min((key - lo) >> s, nbin) : nbin], 1); });
       }
       __syncthreads();
       int c = 0;
@@ -374,7 +377,7 @@ select_reg_kernel(const float* __restrict__ S, int Hkv, int64_t n, I64s kk, int 
         const uint32_t width = 1u << s;
         each([&](uint32_t key) {
           sh.d.cand[min(cnt, LSLOT) * NTR + tid] = key;
-          cnt += key - lo < width ? 1 : 0;
+          cnt += (key >= lo) & (key - lo < width) ? 1 : 0;
         });
         list = !__syncthreads_or(cnt > LSLOT);
         if (list) break;
@@ -402,7 +405,7 @@ select_reg_kernel(const float* __restrict__ S, int Hkv, int64_t n, I64s kk, int 
         if (tid < 257) wh[tid] = 0;
         if (tid == 0) fcnt[0] = 0;
         __syncthreads();
-        list_keys([&](uint32_t key) { atomicAdd(&wh[min((key - lo) >> s, nbin)], 1); });
+        list_keys([&](uint32_t key) { atomicAdd(&wh[key >= lo ? min((key - lo) >> s, nbin) : nbin], 1); });
         __syncthreads();
         if (wv == 0) {                            // lane i walks bins 255 - 4i - q downwards
           int c4[4], sum = 0;
@@ -429,7 +432,7 @@ select_reg_kernel(const float* __restrict__ S, int Hkv, int64_t n, I64s kk, int 
         if (eqc <= 64) {                          // gather the bin's keys, then rank them in wave 0
           const uint32_t width = 1u << s;
           list_keys([&](uint32_t key) {
-            if (key - lo < width) {
+            if (key >= lo && key - lo < width) {
               const int at = atomicAdd(&fcnt[0], 1);
               if (at < 64) fin[at] = key;
             }

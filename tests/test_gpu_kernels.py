@@ -517,6 +517,50 @@ def test_select_register_rows_few_ties_at_cut(dev, copies):
         np.testing.assert_array_equal(idx[l].cpu().numpy(), infokv.select_topk(S[l], k, w))
 
 
+def test_select_register_random_sweep(dev):
+    """Seeded random shapes, budgets and score distributions for rows held in
+    registers (more than 8192 scores, 16 or 50 vectors per thread): uniform,
+    log-uniform over ten binades, signed normal, a few levels (ties), and rows
+    with -0, +0, +-inf and exact copies of the cut value mixed in.  Every kept
+    set must equal the oracle's."""
+    rng = np.random.default_rng(2024)
+    for case in range(24):
+        n = 4 * int(rng.integers(2049, 25601))
+        w = int(rng.choice([0, 1, 16, 31, 32, 64]))
+        Hkv = int(rng.integers(1, 4))
+        kind = case % 6
+        r = rng.random()
+        k = (int(rng.integers(1, w + 1)) if r < 0.1 and w > 0 else
+             w + 1 if r < 0.2 else
+             int(rng.integers(n - 64, n + 1)) if r < 0.3 else
+             int(rng.integers(w + 1, n + 1)))
+        k = max(1, min(n, k))
+        if kind == 0:
+            S = rng.random((1, Hkv, n))
+        elif kind == 1:
+            S = 2.0 ** rng.uniform(-10, 0, (1, Hkv, n))
+        elif kind == 2:
+            S = rng.normal(0, 3, (1, Hkv, n))
+        elif kind == 3:
+            S = rng.integers(0, int(rng.integers(2, 50)), (1, Hkv, n)) / 7.0
+        else:
+            S = rng.normal(0, 1, (1, Hkv, n))
+            at = rng.integers(0, n, (1, Hkv, 64))
+            np.put_along_axis(S, at, rng.choice([0.0, -0.0, np.inf, -np.inf], (1, Hkv, 64)), axis=2)
+            if kind == 5 and k > w:                 # copies of the cut value across the row
+                for g in range(Hkv):
+                    srt = np.sort(S[0, g, :n - w].astype(np.float32))[::-1]
+                    v = srt[min(k - w, n - w) - 1]
+                    S[0, g, rng.integers(0, n - w, 12)] = v
+        S = S.astype(np.float32)
+        announce("select register sweep", case, n, w, k, Hkv, kind)
+        idx = [torch.full((Hkv, k), -1, dtype=torch.int32, device=dev)]
+        B().kvc_select_topk(torch.from_numpy(S).to(dev), [k], w, idx)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(idx[0].cpu().numpy(), infokv.select_topk(S[0], k, w),
+                                      err_msg=f"case {case}: n={n} w={w} k={k} Hkv={Hkv} kind={kind}")
+
+
 def test_select_deterministic(dev):
     S = synth.random_scores((4, 8, 5000), dev, seed=9, tie_levels=4)
     a = [torch.empty(8, 1000, dtype=torch.int32, device=dev) for _ in range(4)]
