@@ -561,6 +561,51 @@ def test_select_register_random_sweep(dev):
                                       err_msg=f"case {case}: n={n} w={w} k={k} Hkv={Hkv} kind={kind}")
 
 
+def test_select_random_sweep_other_paths(dev):
+    """The same distributions on the other select paths: rows cached in LDS (up
+    to 8192 scores), rows not a multiple of 4 or not 16-byte aligned (4-byte
+    loads, re-read), and rows longer than registers hold (re-read)."""
+    rng = np.random.default_rng(77)
+    for case in range(18):
+        path = case % 3
+        n = (4 * int(rng.integers(16, 2049)) if path == 0 else
+             int(rng.integers(64, 9000)) | 1 if path == 1 else
+             4 * int(rng.integers(25601, 28001)))
+        w = int(rng.choice([0, 1, 16, 32]))
+        Hkv = int(rng.integers(1, 3))
+        kind = (case // 3) % 6
+        k = max(1, min(n, int(rng.integers(w + 1, n + 1)) if rng.random() < 0.8 else int(rng.integers(1, n + 1))))
+        if kind == 0:
+            S = rng.random((1, Hkv, n))
+        elif kind == 1:
+            S = 2.0 ** rng.uniform(-10, 0, (1, Hkv, n))
+        elif kind == 2:
+            S = rng.normal(0, 3, (1, Hkv, n))
+        elif kind == 3:
+            S = rng.integers(0, int(rng.integers(2, 50)), (1, Hkv, n)) / 7.0
+        else:
+            S = rng.normal(0, 1, (1, Hkv, n))
+            at = rng.integers(0, n, (1, Hkv, min(64, n)))
+            np.put_along_axis(S, at, rng.choice([0.0, -0.0, np.inf, -np.inf], at.shape), axis=2)
+            if kind == 5 and k > w:
+                for g in range(Hkv):
+                    srt = np.sort(S[0, g, :n - w].astype(np.float32))[::-1]
+                    S[0, g, rng.integers(0, n - w, 12)] = srt[k - w - 1]
+        S = S.astype(np.float32)
+        announce("select sweep other paths", case, path, n, w, k, Hkv, kind)
+        St = torch.from_numpy(S).to(dev)
+        if path == 1 and case % 2:                  # 4 bytes past a 16-byte boundary
+            buf = torch.empty(S.size + 4, device=dev)
+            St2 = buf[1:1 + S.size].view(S.shape)
+            St2.copy_(St)
+            St = St2
+        idx = [torch.full((Hkv, k), -1, dtype=torch.int32, device=dev)]
+        B().kvc_select_topk(St, [k], w, idx)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(idx[0].cpu().numpy(), infokv.select_topk(S[0], k, w),
+                                      err_msg=f"case {case}: path {path} n={n} w={w} k={k} Hkv={Hkv} kind={kind}")
+
+
 def test_select_deterministic(dev):
     S = synth.random_scores((4, 8, 5000), dev, seed=9, tie_levels=4)
     a = [torch.empty(8, 1000, dtype=torch.int32, device=dev) for _ in range(4)]
