@@ -215,7 +215,9 @@ int kvc_adaptive_budget(const float* Ebar, int L, int64_t B, int w, int64_t n,
  * section 2, pipeline step 2 when S is the VATP union):
  * keep the last w tokens plus the k_l - w tokens of [0, n - w) with the largest
  * S (float32 compare, ties to the lower index); if k_l <= w keep the last k_l.
- * Indices are written in ascending order.  Exact and deterministic.
+ * Indices are written in ascending order.  Exact and deterministic.  Scores
+ * are compared as float32 values (-0 equals +0, +-inf allowed); NaN scores are
+ * not supported (their rank is that of their bit pattern and not specified).
  *   S          device float32 [L, Hkv, n].
  *   k_keep     host int64 [L], each in [1, n].
  *   idx_out    host array of L device pointers, each int32 [Hkv, k_keep[l]].
