@@ -255,6 +255,11 @@ WIN_CASES = [
     (1, 6, 2, 150, 20, 32, torch.float32),          # float32 path, G = 3
     (34, 4, 2, 300, 16, 64, torch.bfloat16),        # more layers than one launch holds
     (1, 4, 1, 100003, 32, 128, torch.bfloat16),     # long rows (1024 keys per wave), ragged
+    # keys read once (teams of workgroups), each tile count and head dim
+    (1, 4, 4, 4097, 32, 128, torch.bfloat16),       # one tile, d = 128
+    (1, 12, 4, 5000, 32, 64, torch.bfloat16),       # three tiles, d = 64
+    (1, 16, 4, 3000, 32, 64, torch.bfloat16),       # four tiles, d = 64
+    (1, 4, 4, 65536, 32, 64, torch.bfloat16),       # the longest rows held at d = 64
 ]
 
 
