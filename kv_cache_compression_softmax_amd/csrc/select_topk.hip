@@ -32,7 +32,6 @@ namespace kvc {
 namespace {
 
 constexpr int NT = 1024;
-constexpr int NW = NT / 64;     // waves
 constexpr int EPT = 4;          // consecutive elements per thread in the output pass
 constexpr int HU = 8;           // elements per thread loaded together in a histogram pass
 constexpr int NTR = 512;        // threads of the register path (2 waves per SIMD)
@@ -377,7 +376,7 @@ select_reg_kernel(const float* __restrict__ S, int Hkv, int64_t n, I64s kk, int 
         const uint32_t width = 1u << s;
         each([&](uint32_t key) {
           sh.d.cand[min(cnt, LSLOT) * NTR + tid] = key;
-          cnt += (key >= lo) & (key - lo < width) ? 1 : 0;
+          cnt += ((key >= lo) & (key - lo < width)) ? 1 : 0;
         });
         list = !__syncthreads_or(cnt > LSLOT);
         if (list) break;
